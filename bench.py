@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the ZGCM-1 hybrid attention core on one MI355X.
+
+Step = one pass of the prefill hot path over the B=4 x T=16384 batch (the pages' pre-training
+length): five gated sliding-window layers (W=128) and one full-causal global layer, the repeating
+5:1 block of the model (ZGCM-1 zh-TW translation page, section 2.1). Every layer runs the whole
+fused path: QK-RMSNorm + partial RoPE (rot 42, base 1e6), banded/causal GQA attention with online
+softmax on bf16 MFMA, sigmoid gate. value = B*T / (time of one block) in tokens/s.
+
+Also measured in the same run (reported beside the headline):
+  * the B=64 decode step over a 128-slot ring (local layer) and a linear cache with context lengths
+    uniform on [8192, 65536] (global layer), cold caches, as GB/s of KV read against HBM peak;
+  * the oracle (fp64 NumPy on the host cores) on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # FLOP/s, MI355X dense bf16
+B, T, HQ, HKV, D, W = 4, 16384, 32, 8, 128, 128
+ROPE_BASE = 1e6
+SEED = 1001
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def n_pairs(T, W):
+    """(query, key) pairs per head and sequence of a window-W (0: causal) layer."""
+    if 0 < W < T:
+        return W * (W + 1) // 2 + (T - W) * W
+    return T * (T + 1) // 2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the attention core shards by (batch x KV head) with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import global_causal_attention_amd as zg
+    import synth_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; building inputs B={B} T={T}")
+
+    gen = si.generator(SEED, device="cuda")
+    swa = si.prefill_layer(gen, B, T, HQ, HKV, D, gated=True, device="cuda")
+    glo = si.prefill_layer(gen, B, T, HQ, HKV, D, gated=False, device="cuda")
+    cfg_swa = zg.AttnConfig(window=W, gated=True, rope_base=ROPE_BASE)
+    cfg_glo = zg.AttnConfig(window=0, gated=False, rope_base=ROPE_BASE)
+    out_swa = torch.empty_like(swa["q"])
+    out_glo = torch.empty_like(glo["q"])
+    ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg_swa, B, T), dtype=torch.uint8,
+                     device=dev)
+
+    def run_swa():
+        zg.zg_attn_prefill(cfg_swa, swa["q"], swa["k"], swa["v"], swa["gate"], out=out_swa,
+                           workspace=ws)
+
+    def run_glo():
+        zg.zg_attn_prefill(cfg_glo, glo["q"], glo["k"], glo["v"], out=out_glo, workspace=ws)
+
+    # calibration copy for HBM counters (a plain 1 GiB device copy, outside the timed region)
+    calib_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
+    for _ in range(args.warmup):
+        for _ in range(5):
+            run_swa()
+        run_glo()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(K):
+        ev[s][0].record(stream)
+        for i in range(5):
+            run_swa()
+            ev[s][i + 1].record(stream)
+        run_glo()
+        ev[s][6].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / K
+    swa_ms = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K) for i in range(5)) / (5 * K)
+    glo_ms = sum(ev[s][5].elapsed_time(ev[s][6]) for s in range(K)) / K
+    tokens = B * T
+    value = tokens / (ms_step * 1e-3)
+
+    flop_pair = 4 * D
+    glo_flop = B * HQ * n_pairs(T, 0) * flop_pair
+    swa_flop = B * HQ * n_pairs(T, W) * flop_pair
+    swa_bytes = B * T * (HQ * D * 2 * 3 + HKV * D * 2 * 2)   # q, gate, out + k, v (bf16)
+    glo_achieved = glo_flop / (glo_ms * 1e-3)
+    result = {
+        "metric": "gated-SWA/global attn prefill tokens/s + %MFMA peak; decode HBM GB/s %peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hybrid 5:1 prefill block (5 gated-SWA W=128 + 1 global causal "
+                               "layer), B=4 T=16384 Hq=32 Hkv=8 D=128, rot 42 base 1e6",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(glo_achieved / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": round(glo_achieved / MFMA_BF16_PEAK, 4), "traffic": None,
+                     "kernel": "global causal prefill (kprep + prefill_kernel<4,false>) per launch",
+                     "flop_per_launch": glo_flop},
+        "layers": {
+            "swa_ms": round(swa_ms, 4), "global_ms": round(glo_ms, 4),
+            "weighted_5to1_ms": round(5 * swa_ms + glo_ms, 4),
+            "swa_hbm_GBps": round(swa_bytes / (swa_ms * 1e-3) / 1e9, 1),
+            "swa_hbm_frac": round(swa_bytes / (swa_ms * 1e-3) / HBM_PEAK, 4),
+            "swa_min_bytes": swa_bytes,
+            "swa_mfma_TFLOPs_useful": round(swa_flop / (swa_ms * 1e-3) / 1e12, 2),
+            "global_TFLOPs": round(glo_achieved / 1e12, 2),
+            "global_tokens_per_s": round(tokens / (glo_ms * 1e-3), 1),
+            "swa_tokens_per_s": round(tokens / (swa_ms * 1e-3), 1),
+        },
+    }
+    log(f"[bench] step {ms_step:.3f} ms; swa {swa_ms:.3f} ms; global {glo_ms:.3f} ms")
+    del swa, glo, out_swa, out_glo, ws
+
+    if not args.no_decode:
+        result["decode"] = bench_decode(torch, zg, si, dev, stream, args.decode_reps)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(torch, si)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(torch, zg, si, dev, stream, reps):
+    """B=64 decode step: ring (local) and linear (global) layers; MALL/L2 flushed before each rep."""
+    Bd, lo, hi = 64, 8192, 65536
+    gen = si.generator(1002, device="cuda")
+    log("[bench] building decode caches (2 x 8 GiB linear, 2 x 16 MiB ring)")
+    x = si.decode_step(gen, B=Bd, len_lo=lo, len_hi=hi, device="cuda")
+    seqlens = x["seqlens"]
+    sum_len = int(seqlens.sum().item())
+    cfg_r = zg.AttnConfig(window=W, gated=True, rope_base=1e7)
+    cfg_l = zg.AttnConfig(window=0, gated=False, rope_base=1e7)
+    ws_r = torch.empty(zg.zg_attn_decode_workspace_bytes(cfg_r, Bd, hi), dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(zg.zg_attn_decode_workspace_bytes(cfg_l, Bd, hi), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x["q_new"])
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def ring():
+        zg.zg_attn_decode(cfg_r, x["q_new"], x["k_new"], x["v_new"], x["gate"], x["ring_k"],
+                          x["ring_v"], seqlens, max_seqlen=hi, out=out, workspace=ws_r)
+
+    def lin():
+        zg.zg_attn_decode(cfg_l, x["q_new"], x["k_new"], x["v_new"], None, x["lin_k"],
+                          x["lin_v"], seqlens, max_seqlen=hi, out=out, workspace=ws_l)
+
+    res = {}
+    for name, fn, kv_bytes in (("ring", ring, Bd * W * HKV * D * 2 * 2),
+                               ("linear", lin, sum_len * HKV * D * 2 * 2)):
+        for _ in range(3):
+            fn()
+        times = []
+        for _ in range(reps):
+            flush.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        med = times[len(times) // 2]
+        bw = kv_bytes / (med * 1e-3)
+        res[name] = {"ms_median": round(med, 4), "kv_bytes": kv_bytes, "GBps": round(bw / 1e9, 1),
+                     "hbm_frac": round(bw / HBM_PEAK, 4), "tokens_per_s": round(Bd / (med * 1e-3), 1)}
+        log(f"[bench] decode {name}: {med:.4f} ms, {bw / 1e9:.1f} GB/s")
+    res["workload"] = "B=64, Hq=32 Hkv=8 D=128, ring W=128 gated; linear L~U[8192,65536] ungated; base 1e7; cold MALL"
+    res["roofline"] = {"bound": "hbm", "achieved": res["linear"]["GBps"], "peak": HBM_PEAK / 1e9,
+                       "unit": "GB/s", "frac": res["linear"]["hbm_frac"], "traffic": None,
+                       "kernel": "global decode (prep + split-KV attention + combine)"}
+    del x, flush
+    return res
+
+
+def cpu_baseline(torch, si, budget_s=12.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the same 5:1 block: query rows of
+    sequence 0 (all 32 heads) of a gated local layer and of the global layer, drawn at uniform
+    positions and processed in batches until about budget_s seconds of CPU work are spent (40%
+    local, 60% global). Rate = tokens/s of a 5:1 block = 1 / (5 * t_row_local + t_row_global),
+    with the global row time scaled to the mean position of a full sequence."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    gen = si.generator(SEED)
+    Ts = 16384
+    x = si.prefill_layer(gen, 1, Ts, HQ, HKV, D, gated=True)
+    f = lambda t: t.float().numpy().astype(np.float64)
+    q, k, v, g = f(x["q"]), f(x["k"]), f(x["v"]), f(x["gate"])
+    rng = np.random.default_rng(0)
+    order_l = rng.permutation(np.arange(W, Ts))
+    order_g = rng.permutation(np.arange(Ts))
+
+    def timed(order, batch, budget, **kw):
+        n, t0 = 0, time.perf_counter()
+        while n < len(order) and time.perf_counter() - t0 < budget:
+            rows = np.sort(order[n:n + batch])
+            oracle.prefill_rows(q, k, v, g if kw["gated"] else None, rows, rope_base=ROPE_BASE, **kw)
+            n += len(rows)
+        return n, time.perf_counter() - t0, order[:n]
+
+    n_l, t_l, _ = timed(order_l, 64, 0.4 * budget_s, window=W, gated=True)
+    n_g, t_g, rows_g = timed(order_g, 16, 0.6 * budget_s, window=0, gated=False)
+    t_row_l = t_l / n_l
+    t_row_g = t_g / n_g * ((Ts + 1) / 2) / float(np.mean(rows_g + 1))
+    rate = 1.0 / (5 * t_row_l + t_row_g)
+    log(f"[bench] oracle: {t_row_l * 1e3:.2f} ms/local row ({n_l} rows), "
+        f"{t_row_g * 1e3:.2f} ms/global row ({n_g} rows)")
+    return {"value": round(rate, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_l} local-layer rows + {n_g} global-layer rows of sequence 0 (all 32 "
+                      f"heads), T={Ts}, uniform positions; global row time scaled to the mean "
+                      f"position; {t_l + t_g:.1f} s of CPU work"}
+
+
+if __name__ == "__main__":
+    main()

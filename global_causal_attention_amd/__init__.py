@@ -1,0 +1,224 @@
+"""MI355X (gfx950) hybrid attention core of ZGCM-1: Python binding of the C ABI in include/zg_attn.h.
+
+The binding only marshals arguments: it checks dtypes/devices/shapes, takes raw device pointers and
+the current HIP stream from torch, and calls libzgattn.so through ctypes. Every step of the path runs
+in the library's kernels; there is no fallback. If the library is missing the call raises.
+
+Build the library with ``python -m global_causal_attention_amd.build`` (hipcc, --offload-arch=gfx950).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+from ._abi import (LIB_PATH, ZgAttnCfg, ZgTokenStrides, load_library, ZG_OK, ZG_ERR_NULL,
+                   ZG_ERR_SHAPE, ZG_ERR_UNSUPPORTED, ZG_ERR_WORKSPACE, ZG_ERR_HIP, EXPORTS)
+
+__all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_decode", "zg_kv_bytes",
+           "zg_attn_prefill_workspace_bytes", "zg_attn_decode_workspace_bytes", "zg_rmsnorm",
+           "zg_gemm_bf16", "zg_attn_layer", "zg_attn_layer_workspace_bytes", "zg_last_error",
+           "load_library", "LIB_PATH", "EXPORTS"]
+
+
+class ZGError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"zg status {status}: {msg}")
+        self.status = status
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    """One attention layer. Defaults are ZGCM-1's local layer (zh-TW translation page, section 2.1):
+    32 query / 8 KV heads of dim 128, window 128, gated, partial RoPE on floor(0.33*128) = 42 dims."""
+    n_q_heads: int = 32
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    window: int = 128
+    gated: bool = True
+    rot_dim: int = 42
+    rope_base: float = 1e4
+    rms_eps: float = 1e-6
+    softmax_scale: float = 0.0
+
+    def c(self) -> ZgAttnCfg:
+        return ZgAttnCfg(self.n_q_heads, self.n_kv_heads, self.head_dim, self.window,
+                         1 if self.gated else 0, self.rot_dim, float(self.rope_base),
+                         float(self.rms_eps), float(self.softmax_scale))
+
+
+def _check(status: int):
+    if status != ZG_OK:
+        raise ZGError(status, zg_last_error())
+
+
+def zg_last_error() -> str:
+    return load_library().zg_last_error().decode()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, device_required=True):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device_required and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _token_stride(t, name, row):
+    """Element stride between tokens of a [B, T, H, D] (or [B*T, row]) view whose rows are dense."""
+    if t.dim() == 4:
+        if t.stride(3) != 1 or t.stride(2) != t.shape[3]:
+            raise ValueError(f"{name}: heads and dims must be dense")
+        st = t.stride(1)
+        if t.shape[0] > 1 and t.stride(0) != st * t.shape[1]:
+            raise ValueError(f"{name}: batch stride must equal T * token stride")
+        return st
+    raise ValueError(f"{name} must be 4-D [B, T, H, D]")
+
+
+def zg_attn_prefill_workspace_bytes(cfg: AttnConfig, B: int, T: int) -> int:
+    c = cfg.c()
+    return load_library().zg_attn_prefill_workspace_bytes(ctypes.byref(c), B, T)
+
+
+def zg_attn_prefill(cfg: AttnConfig, q, k, v, gate=None, *, q_norm_w=None, k_norm_w=None,
+                    pos0: int = 0, out=None, workspace=None, stream=None):
+    """Prefill attention (see include/zg_attn.h). q, gate: [B, T, Hq, 128] bf16; k, v:
+    [B, T, Hkv, 128] bf16 (token-strided views allowed). Returns out [B, T, Hq, 128] bf16."""
+    import torch
+    bf = torch.bfloat16
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, bf)
+    if cfg.gated:
+        _need(gate, "gate", bf)
+    B, T, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=bf, device=q.device)
+    _need(out, "out", bf)
+    for w, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _need(w, n, torch.float32)
+    strides = ZgTokenStrides(_token_stride(q, "q", Hq * D), _token_stride(k, "k", 0),
+                             _token_stride(v, "v", 0),
+                             _token_stride(gate, "gate", 0) if cfg.gated else Hq * D,
+                             _token_stride(out, "out", 0))
+    if k.shape[:2] != (B, T) or v.shape[:2] != (B, T) or out.shape != (B, T, Hq, D):
+        raise ValueError("q/k/v/out shapes disagree")
+    need = zg_attn_prefill_workspace_bytes(cfg, B, T)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    c = cfg.c()
+    _check(load_library().zg_attn_prefill(
+        ctypes.byref(c), B, T, pos0, _ptr(q), _ptr(k), _ptr(v), _ptr(gate if cfg.gated else None),
+        _ptr(q_norm_w), _ptr(k_norm_w), ctypes.byref(strides), _ptr(out), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def zg_attn_decode_workspace_bytes(cfg: AttnConfig, B: int, max_seqlen: int) -> int:
+    c = cfg.c()
+    return load_library().zg_attn_decode_workspace_bytes(ctypes.byref(c), B, max_seqlen)
+
+
+def zg_attn_decode(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_cache, seqlens, *,
+                   max_seqlen: int, q_norm_w=None, k_norm_w=None, out=None, workspace=None,
+                   stream=None):
+    """One decode step (see include/zg_attn.h). Updates k_cache / v_cache in place and returns
+    out [B, Hq, 128] bf16."""
+    import torch
+    bf = torch.bfloat16
+    for t, n in ((q_new, "q_new"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _need(t, n, bf)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    _need(seqlens, "seqlens", torch.int32)
+    if cfg.gated:
+        _need(gate, "gate", bf)
+    B = q_new.shape[0]
+    if out is None:
+        out = torch.empty_like(q_new)
+    need = zg_attn_decode_workspace_bytes(cfg, B, max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_new.device)
+    stride = k_cache.shape[1]
+    c = cfg.c()
+    _check(load_library().zg_attn_decode(
+        ctypes.byref(c), B, stride, max_seqlen, _ptr(q_new), _ptr(k_new), _ptr(v_new),
+        _ptr(gate if cfg.gated else None), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(k_cache),
+        _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def zg_kv_bytes(n_layers, global_every, n_kv_heads, head_dim, window, elem_bytes, batch,
+                seqlen) -> int:
+    """KV-cache bytes of a layer stack (pure host arithmetic in the library)."""
+    lib = load_library()
+    r = lib.zg_kv_bytes(n_layers, global_every, n_kv_heads, head_dim, window, elem_bytes, batch,
+                        seqlen)
+    if r == 0 and min(n_layers, global_every, n_kv_heads, head_dim, window, elem_bytes, batch,
+                      seqlen) < 0:
+        raise ZGError(ZG_ERR_SHAPE, zg_last_error())
+    return r
+
+
+def zg_rmsnorm(x, eps=1e-6, w=None, out=None, stream=None):
+    import torch
+    _need(x, "x", torch.float32)
+    rows = x.numel() // x.shape[-1]
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _check(load_library().zg_rmsnorm(rows, x.shape[-1], _ptr(x), _ptr(w), float(eps), _ptr(out),
+                                     _stream(stream)))
+    return out
+
+
+def zg_gemm_bf16(x, w, residual=None, y=None, want_y=True, stream=None):
+    """Y = X W^T (fp32 accumulate); residual (fp32) += Y if given; y = bf16(Y) if want_y."""
+    import torch
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16)
+    M, K = x.shape
+    N = w.shape[0]
+    if want_y and y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().zg_gemm_bf16(M, N, K, _ptr(x), _ptr(w), _ptr(residual),
+                                       _ptr(y if want_y else None), N, _stream(stream)))
+    return y if want_y else residual
+
+
+def zg_attn_layer_workspace_bytes(cfg: AttnConfig, B: int, T: int) -> int:
+    c = cfg.c()
+    return load_library().zg_attn_layer_workspace_bytes(ctypes.byref(c), B, T)
+
+
+def zg_attn_layer(cfg: AttnConfig, x, w_qkvg, w_o, *, q_norm_w=None, k_norm_w=None,
+                  workspace=None, stream=None):
+    """x (fp32 [B, T, hidden]) <- x + o_proj(attn(RMSNorm(x))), in place."""
+    import torch
+    _need(x, "x", torch.float32)
+    B, T, _ = x.shape
+    need = zg_attn_layer_workspace_bytes(cfg, B, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    c = cfg.c()
+    _check(load_library().zg_attn_layer(
+        ctypes.byref(c), B, T, _ptr(x), _ptr(w_qkvg), _ptr(w_o), _ptr(q_norm_w), _ptr(k_norm_w),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return x

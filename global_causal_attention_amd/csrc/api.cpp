@@ -1,0 +1,335 @@
+// C ABI of the hybrid attention core: host-side validation, workspace planning and dispatch to the
+// gfx950 kernels. Every argument is checked before anything is enqueued; failures return a
+// zg_status and leave a thread-local message. No exception crosses the ABI.
+#include "../../include/zg_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+
+#include "zg_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+zg_status fail(zg_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+zg_status fail(zg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+zg_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ZG_OK;
+  return fail(ZG_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kD = 128;
+constexpr int64_t kDecodeChunk = 1024;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+zg_status check_cfg(const zg_attn_cfg* c) {
+  if (!c) return fail(ZG_ERR_NULL, "cfg is NULL");
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1)
+    return fail(ZG_ERR_SHAPE, "n_q_heads=%d n_kv_heads=%d must be >= 1", c->n_q_heads, c->n_kv_heads);
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(ZG_ERR_SHAPE, "n_q_heads=%d is not a multiple of n_kv_heads=%d", c->n_q_heads,
+                c->n_kv_heads);
+  const int g = c->n_q_heads / c->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(ZG_ERR_UNSUPPORTED, "query heads per KV head = %d; supported: 1, 2, 4, 8", g);
+  if (c->head_dim != kD) return fail(ZG_ERR_UNSUPPORTED, "head_dim=%d; supported: 128", c->head_dim);
+  if (c->window < 0) return fail(ZG_ERR_SHAPE, "window=%d must be >= 0", c->window);
+  if (c->gated != 0 && c->gated != 1) return fail(ZG_ERR_SHAPE, "gated=%d must be 0 or 1", c->gated);
+  if (c->rot_dim < 0 || c->rot_dim > 64 || (c->rot_dim & 1))
+    return fail(ZG_ERR_UNSUPPORTED, "rot_dim=%d; supported: even values in [0, 64]", c->rot_dim);
+  if (!(c->rope_base > 1.0) || !std::isfinite(c->rope_base))
+    return fail(ZG_ERR_SHAPE, "rope_base=%g must be finite and > 1", c->rope_base);
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
+    return fail(ZG_ERR_SHAPE, "rms_eps=%g must be finite and >= 0", (double)c->rms_eps);
+  if (!std::isfinite(c->softmax_scale))
+    return fail(ZG_ERR_SHAPE, "softmax_scale must be finite");
+  return ZG_OK;
+}
+
+zg::RopeTableH rope_table(const zg_attn_cfg* c) {
+  zg::RopeTableH t{};
+  t.half = c->rot_dim / 2;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < t.half; ++i)
+    t.rev[i] = std::pow(c->rope_base, -2.0 * i / (double)c->rot_dim) / two_pi;
+  return t;
+}
+
+float scale_log2(const zg_attn_cfg* c) {
+  const double s = c->softmax_scale > 0.f ? (double)c->softmax_scale : 1.0 / std::sqrt((double)kD);
+  return (float)(s * 1.4426950408889634073599246810019);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* zg_last_error(void) { return g_err.c_str(); }
+
+uint64_t zg_kv_bytes(int32_t n_layers, int32_t global_every, int32_t n_kv_heads, int32_t head_dim,
+                     int32_t window, int32_t elem_bytes, int64_t batch, int64_t seqlen) {
+  if (n_layers < 0 || global_every < 0 || n_kv_heads < 0 || head_dim < 0 || window < 0 ||
+      elem_bytes < 0 || batch < 0 || seqlen < 0) {
+    fail(ZG_ERR_SHAPE, "zg_kv_bytes: arguments must be >= 0");
+    return 0;
+  }
+  unsigned __int128 rows = 0;
+  for (int32_t l = 1; l <= n_layers; ++l) {
+    const bool global = window == 0 || (global_every > 0 && l % global_every == 0);
+    rows += (unsigned __int128)(global ? seqlen : (seqlen < window ? seqlen : window));
+  }
+  const unsigned __int128 total = rows * 2u * (unsigned)n_kv_heads * (unsigned)head_dim *
+                                  (unsigned)elem_bytes * (unsigned __int128)batch;
+  if (total > std::numeric_limits<uint64_t>::max()) {
+    fail(ZG_ERR_SHAPE, "zg_kv_bytes: result overflows uint64");
+    return 0;
+  }
+  return (uint64_t)total;
+}
+
+size_t zg_attn_prefill_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
+  if (!cfg || B < 1 || T < 1 || cfg->n_kv_heads < 1) return 0;
+  return align256((size_t)B * T * cfg->n_kv_heads * kD * 2);
+}
+
+zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t pos0,
+                          const void* q, const void* k, const void* v, const void* gate,
+                          const float* q_norm_w, const float* k_norm_w,
+                          const zg_token_strides* strides, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  try {
+    zg_status st = check_cfg(cfg);
+    if (st != ZG_OK) return st;
+    if (!q || !k || !v || !out) return fail(ZG_ERR_NULL, "q, k, v and out must be non-NULL");
+    if (cfg->gated && !gate) return fail(ZG_ERR_NULL, "gate must be non-NULL when gated=1");
+    if (B < 1 || T < 1) return fail(ZG_ERR_SHAPE, "B=%d T=%d must be >= 1", B, T);
+    if (pos0 < 0) return fail(ZG_ERR_SHAPE, "pos0=%lld must be >= 0", (long long)pos0);
+    const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+    if ((int64_t)B * T * Hq * kD >= (int64_t(1) << 40))
+      return fail(ZG_ERR_SHAPE, "B*T*Hq*D too large");
+    zg_token_strides s{Hq * kD, Hkv * kD, Hkv * kD, Hq * kD, Hq * kD};
+    if (strides) s = *strides;
+    if (s.q < Hq * kD || s.k < Hkv * kD || s.v < Hkv * kD || s.out < Hq * kD ||
+        (cfg->gated && s.gate < Hq * kD) || (s.q | s.k | s.v | s.out) % 8 != 0 ||
+        (cfg->gated && s.gate % 8 != 0))
+      return fail(ZG_ERR_SHAPE, "token strides must be >= the packed row and multiples of 8");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (cfg->gated && !aligned16(gate)) || (q_norm_w && !aligned16(q_norm_w)) ||
+        (k_norm_w && !aligned16(k_norm_w)))
+      return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    const size_t need = zg_attn_prefill_workspace_bytes(cfg, B, T);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned16(workspace)) return fail(ZG_ERR_SHAPE, "workspace must be 16-byte aligned");
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const zg::RopeTableH rt = rope_table(cfg);
+    zg::KPrepParams kp{};
+    kp.k = static_cast<const uint16_t*>(k);
+    kp.khat = static_cast<uint16_t*>(workspace);
+    kp.k_norm_w = k_norm_w;
+    kp.sk = s.k;
+    kp.B = B;
+    kp.T = T;
+    kp.Hkv = (int32_t)Hkv;
+    kp.pos0 = pos0;
+    kp.eps = cfg->rms_eps;
+    kp.rope = rt;
+    st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
+    if (st != ZG_OK) return st;
+
+    const int G = (int)(Hq / Hkv);
+    const int mq = 256 / G;
+    zg::PrefillParams pp{};
+    pp.q = static_cast<const uint16_t*>(q);
+    pp.khat = static_cast<const uint16_t*>(workspace);
+    pp.v = static_cast<const uint16_t*>(v);
+    pp.gate = static_cast<const uint16_t*>(gate);
+    pp.out = static_cast<uint16_t*>(out);
+    pp.q_norm_w = q_norm_w;
+    pp.sq = s.q;
+    pp.sv = s.v;
+    pp.sg = s.gate;
+    pp.so = s.out;
+    pp.B = B;
+    pp.T = T;
+    pp.Hq = (int32_t)Hq;
+    pp.Hkv = (int32_t)Hkv;
+    pp.pos0 = pos0;
+    pp.window = cfg->window >= T ? 0 : cfg->window;  // a window covering the sequence is causal
+    pp.n_qtiles = (T + mq - 1) / mq;
+    pp.eps = cfg->rms_eps;
+    pp.scale_log2 = scale_log2(cfg);
+    pp.rope = rt;
+    if ((int64_t)pp.n_qtiles * B * Hkv >= (int64_t(1) << 31))
+      return fail(ZG_ERR_SHAPE, "grid too large");
+    return hip_status(zg::launch_prefill(pp, G, cfg->gated != 0, hs), "prefill launch");
+  } catch (...) {
+    return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_prefill");
+  }
+}
+
+size_t zg_attn_decode_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int64_t max_seqlen) {
+  if (!cfg || B < 1 || max_seqlen < 1 || cfg->n_q_heads < 1) return 0;
+  const int64_t keys = cfg->window > 0 ? std::min<int64_t>(cfg->window, max_seqlen) : max_seqlen;
+  const int64_t n_chunks = (keys + kDecodeChunk - 1) / kDecodeChunk;
+  size_t bytes = align256((size_t)B * cfg->n_q_heads * kD * 4);
+  if (n_chunks > 1) bytes += align256((size_t)B * cfg->n_q_heads * n_chunks * 132 * 4);
+  return bytes;
+}
+
+zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                         int64_t max_seqlen, const void* q_new, const void* k_new,
+                         const void* v_new, const void* gate, const float* q_norm_w,
+                         const float* k_norm_w, void* k_cache, void* v_cache,
+                         const int32_t* seqlens, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  try {
+    zg_status st = check_cfg(cfg);
+    if (st != ZG_OK) return st;
+    if (!q_new || !k_new || !v_new || !k_cache || !v_cache || !seqlens || !out)
+      return fail(ZG_ERR_NULL, "q_new, k_new, v_new, caches, seqlens and out must be non-NULL");
+    if (cfg->gated && !gate) return fail(ZG_ERR_NULL, "gate must be non-NULL when gated=1");
+    if (B < 1) return fail(ZG_ERR_SHAPE, "B=%d must be >= 1", B);
+    if (max_seqlen < 1 || max_seqlen >= (int64_t(1) << 31))
+      return fail(ZG_ERR_SHAPE, "max_seqlen=%lld out of range", (long long)max_seqlen);
+    if (cfg->window == 0 && cache_stride < max_seqlen)
+      return fail(ZG_ERR_SHAPE, "linear cache: cache_stride=%lld < max_seqlen=%lld",
+                  (long long)cache_stride, (long long)max_seqlen);
+    if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || (q_norm_w && !aligned16(q_norm_w)) ||
+        (k_norm_w && !aligned16(k_norm_w)))
+      return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    const size_t need = zg_attn_decode_workspace_bytes(cfg, B, max_seqlen);
+    if (!workspace || workspace_bytes < need)
+      return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned16(workspace)) return fail(ZG_ERR_SHAPE, "workspace must be 16-byte aligned");
+
+    const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+    const int64_t keys = cfg->window > 0 ? std::min<int64_t>(cfg->window, max_seqlen) : max_seqlen;
+    zg::DecodeParams p{};
+    p.q_new = static_cast<const uint16_t*>(q_new);
+    p.k_new = static_cast<const uint16_t*>(k_new);
+    p.v_new = static_cast<const uint16_t*>(v_new);
+    p.gate = static_cast<const uint16_t*>(gate);
+    p.q_norm_w = q_norm_w;
+    p.k_norm_w = k_norm_w;
+    p.k_cache = static_cast<uint16_t*>(k_cache);
+    p.v_cache = static_cast<uint16_t*>(v_cache);
+    p.seqlens = seqlens;
+    p.out = static_cast<uint16_t*>(out);
+    p.qhat = static_cast<float*>(workspace);
+    p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         align256((size_t)B * Hq * kD * 4));
+    p.B = B;
+    p.Hq = (int32_t)Hq;
+    p.Hkv = (int32_t)Hkv;
+    p.window = cfg->window;
+    p.rows = cfg->window > 0 ? cfg->window : cache_stride;
+    p.chunk = (int32_t)kDecodeChunk;
+    p.n_chunks = (int32_t)((keys + kDecodeChunk - 1) / kDecodeChunk);
+    p.gated = cfg->gated;
+    p.eps = cfg->rms_eps;
+    p.scale_log2 = scale_log2(cfg);
+    p.rope = rope_table(cfg);
+    return hip_status(zg::launch_decode(p, reinterpret_cast<hipStream_t>(stream)), "decode launch");
+  } catch (...) {
+    return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_decode");
+  }
+}
+
+zg_status zg_rmsnorm(int64_t rows, int32_t dim, const float* x, const float* w, float eps,
+                     void* y_bf16, void* stream) {
+  if (!x || !y_bf16) return fail(ZG_ERR_NULL, "x and y must be non-NULL");
+  if (rows < 1 || rows >= (int64_t(1) << 31) || dim < 8 || dim > 8192 || dim % 8 != 0)
+    return fail(ZG_ERR_SHAPE, "rows=%lld dim=%d: need rows >= 1, dim %% 8 == 0, 8 <= dim <= 8192",
+                (long long)rows, dim);
+  if (!(eps >= 0.f)) return fail(ZG_ERR_SHAPE, "eps must be >= 0");
+  if (!aligned16(x) || !aligned16(y_bf16)) return fail(ZG_ERR_SHAPE, "pointers must be 16-byte aligned");
+  zg::RmsNormParams p{x, w, static_cast<uint16_t*>(y_bf16), rows, dim, eps};
+  return hip_status(zg::launch_rmsnorm(p, reinterpret_cast<hipStream_t>(stream)), "rmsnorm launch");
+}
+
+zg_status zg_gemm_bf16(int64_t M, int32_t N, int32_t K, const void* x_bf16, const void* w_bf16,
+                       float* residual, void* y_bf16, int64_t ldy, void* stream) {
+  if (!x_bf16 || !w_bf16) return fail(ZG_ERR_NULL, "x and w must be non-NULL");
+  if (!residual && !y_bf16) return fail(ZG_ERR_NULL, "one of residual / y must be non-NULL");
+  if (M < 1 || N < 8 || K < 64 || K % 64 != 0 || N % 8 != 0)
+    return fail(ZG_ERR_SHAPE, "M=%lld N=%d K=%d: need M >= 1, N %% 8 == 0, K %% 64 == 0",
+                (long long)M, N, K);
+  if (y_bf16 && ldy < N) return fail(ZG_ERR_SHAPE, "ldy=%lld < N=%d", (long long)ldy, N);
+  if (((M + 127) / 128) * ((N + 127) / 128) >= (int64_t(1) << 31))
+    return fail(ZG_ERR_SHAPE, "problem too large");
+  if (!aligned16(x_bf16) || !aligned16(w_bf16)) return fail(ZG_ERR_SHAPE, "x and w must be 16-byte aligned");
+  zg::GemmParams p{static_cast<const uint16_t*>(x_bf16), static_cast<const uint16_t*>(w_bf16),
+                   residual, static_cast<uint16_t*>(y_bf16), ldy, M, N, K};
+  return hip_status(zg::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)), "gemm launch");
+}
+
+size_t zg_attn_layer_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
+  if (!cfg || B < 1 || T < 1 || cfg->n_q_heads < 1 || cfg->n_kv_heads < 1) return 0;
+  const size_t bt = (size_t)B * T;
+  const size_t hidden = (size_t)cfg->n_q_heads * kD;
+  const size_t nqkvg = (size_t)(cfg->n_q_heads + 2 * cfg->n_kv_heads + (cfg->gated ? cfg->n_q_heads : 0)) * kD;
+  return align256(bt * hidden * 2) + align256(bt * nqkvg * 2) +
+         zg_attn_prefill_workspace_bytes(cfg, B, T);
+}
+
+zg_status zg_attn_layer(const zg_attn_cfg* cfg, int32_t B, int32_t T, float* x,
+                        const void* w_qkvg, const void* w_o, const float* q_norm_w,
+                        const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  zg_status st = check_cfg(cfg);
+  if (st != ZG_OK) return st;
+  if (!x || !w_qkvg || !w_o) return fail(ZG_ERR_NULL, "x, w_qkvg and w_o must be non-NULL");
+  if (B < 1 || T < 1) return fail(ZG_ERR_SHAPE, "B=%d T=%d must be >= 1", B, T);
+  const size_t need = zg_attn_layer_workspace_bytes(cfg, B, T);
+  if (!workspace || workspace_bytes < need)
+    return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, need);
+  const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+  const int64_t hidden = Hq * kD;
+  const int64_t nqkvg = (Hq + 2 * Hkv + (cfg->gated ? Hq : 0)) * kD;
+  const int64_t bt = (int64_t)B * T;
+  char* ws = static_cast<char*>(workspace);
+  void* h = ws;                                                  // bf16 [bt, hidden], reused for attn out
+  void* qkvg = ws + align256(bt * hidden * 2);                   // bf16 [bt, nqkvg]
+  void* kws = ws + align256(bt * hidden * 2) + align256(bt * nqkvg * 2);
+  const size_t kws_bytes = zg_attn_prefill_workspace_bytes(cfg, B, T);
+
+  st = zg_rmsnorm(bt, (int32_t)hidden, x, nullptr, cfg->rms_eps, h, stream);
+  if (st != ZG_OK) return st;
+  st = zg_gemm_bf16(bt, (int32_t)nqkvg, (int32_t)hidden, h, w_qkvg, nullptr, qkvg, nqkvg, stream);
+  if (st != ZG_OK) return st;
+  const uint16_t* base = static_cast<const uint16_t*>(qkvg);
+  zg_token_strides s{nqkvg, nqkvg, nqkvg, nqkvg, hidden};
+  st = zg_attn_prefill(cfg, B, T, 0, base, base + Hq * kD, base + (Hq + Hkv) * kD,
+                       cfg->gated ? base + (Hq + 2 * Hkv) * kD : nullptr, q_norm_w, k_norm_w, &s, h,
+                       kws, kws_bytes, stream);
+  if (st != ZG_OK) return st;
+  return zg_gemm_bf16(bt, (int32_t)hidden, (int32_t)hidden, h, w_o, x, nullptr, 0, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Device helpers shared by the gfx950 kernels: bf16 packing, vector types, wave shuffles, and the
+// fused QK-RMSNorm + partial-RoPE row prologue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zg_kernels.hpp"
+
+namespace zg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxRotHalf = 32;  // rot_dim <= 64
+
+// Rotary frequencies in revolutions per position (theta_i / (2 pi), fp64, computed on the host).
+typedef RopeTableH RopeTable;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to nearest-even bf16 and pack (lo in bits 0..15): v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 w, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16lo(w[i]);
+    x[2 * i + 1] = bf16hi(w[i]);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+  return w;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// cos/sin of 2*pi*(pos * rev), with the product reduced modulo one revolution in fp64 so the angle
+// keeps full precision at positions up to 2^18 and beyond.
+__device__ __forceinline__ void rope_cs(int64_t pos, double rev, float& c, float& s) {
+  double r = (double)pos * rev;
+  r = r - __builtin_rint(r);
+  float a = (float)(r * 6.283185307179586476925286766559);
+  sincosf(a, &s, &c);
+}
+
+// Fused QK-RMSNorm + partial RoPE of one 128-wide head row, split over two adjacent lanes:
+// lane parity `half` holds dims [64*half, 64*half + 64) in x[0..63] (fp32, already loaded).
+// RMSNorm: x * w / sqrt(mean(x^2) + eps) over all 128 dims (partner lane = lane ^ 1).
+// RoPE: pairs (i, i + rot/2), i < rot/2 <= 32, all inside half 0, rotated by pos * theta_i.
+// `stage` is this lane pair's 64-float LDS scratch row (only half 0 touches it).
+__device__ __forceinline__ void norm_rope_row(float* x, int half, const float* __restrict__ w,
+                                              float eps, int64_t pos, const RopeTable& rt,
+                                              float* stage) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
+  ss += shfl_xor_f(ss, 1);
+  const float inv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
+  if (w) {
+    const f32x4* w4 = reinterpret_cast<const f32x4*>(w + 64 * half);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      f32x4 ww = w4[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[4 * i + j] *= inv * ww[j];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] *= inv;
+  }
+  const int h = rt.half;
+  if (half == 0 && h > 0) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) stage[i] = x[i];
+#pragma unroll
+    for (int i = 0; i < kMaxRotHalf; ++i) {
+      if (i < h) {
+        float c, s;
+        rope_cs(pos, rt.rev[i], c, s);
+        const float a = stage[i];
+        const float b = stage[i + h];
+        stage[i] = a * c - b * s;
+        stage[i + h] = b * c + a * s;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = stage[i];
+  }
+}
+
+}  // namespace zg

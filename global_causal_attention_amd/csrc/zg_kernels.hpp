@@ -1,0 +1,95 @@
+// Internal launch interface between the C ABI (api.cpp) and the gfx950 kernels (*.hip).
+// Host-visible parameter blocks; all pointers are device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zg {
+
+constexpr int kMaxRotHalfHost = 32;
+
+struct RopeTableH {
+  double rev[kMaxRotHalfHost];  // theta_i / (2 pi) for i < half
+  int32_t half;
+};
+
+// Normalise + rotate keys into a packed [B, T, Hkv, 128] bf16 buffer.
+struct KPrepParams {
+  const uint16_t* k;
+  uint16_t* khat;
+  const float* k_norm_w;
+  int64_t sk;  // token stride of k (elements)
+  int32_t B, T, Hkv;
+  int64_t pos0;
+  float eps;
+  RopeTableH rope;
+};
+
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* khat;  // packed [B, T, Hkv, 128]
+  const uint16_t* v;
+  const uint16_t* gate;
+  uint16_t* out;
+  const float* q_norm_w;
+  int64_t sq, sv, sg, so;  // token strides (elements)
+  int32_t B, T, Hq, Hkv;
+  int64_t pos0;
+  int32_t window;
+  int32_t n_qtiles;
+  float eps;
+  float scale_log2;  // softmax scale * log2(e)
+  RopeTableH rope;
+};
+
+struct DecodeParams {
+  const uint16_t* q_new;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const uint16_t* gate;
+  const float* q_norm_w;
+  const float* k_norm_w;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int32_t* seqlens;
+  uint16_t* out;
+  float* qhat;      // workspace: [B, Hq, 128] fp32 (bf16-rounded values)
+  float* partial;   // workspace: [B, Hq, n_chunks, 130] fp32 (m, l, o[128])
+  int32_t B, Hq, Hkv;
+  int32_t window;   // ring slots (0: linear)
+  int64_t rows;     // rows per sequence in the cache (window or cache_stride)
+  int32_t chunk;    // keys per split
+  int32_t n_chunks; // max splits per sequence
+  int32_t gated;
+  float eps;
+  float scale_log2;
+  RopeTableH rope;
+};
+
+struct RmsNormParams {
+  const float* x;
+  const float* w;
+  uint16_t* y;
+  int64_t rows;
+  int32_t dim;
+  float eps;
+};
+
+struct GemmParams {
+  const uint16_t* x;  // [M, K]
+  const uint16_t* w;  // [N, K]
+  float* residual;    // [M, N] or null
+  uint16_t* y;        // [M, ldy] or null
+  int64_t ldy;
+  int64_t M;
+  int32_t N, K;
+};
+
+hipError_t launch_kprep(const KPrepParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+}  // namespace zg

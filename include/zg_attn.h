@@ -1,0 +1,163 @@
+/*
+ * zg_attn.h -- C ABI of the MI355X (gfx950) hybrid attention core of ZGCM-1.
+ *
+ * The method (all pages describe "ZGCM-1: A Fully Open and Extremely Efficient Foundation Model for
+ * Math and Agentic Search"; the zh-TW translation page, section 2.1 "Model overview" and Figure 3):
+ * most layers are gated sliding-window attention with a 128-token window, every sixth layer is full
+ * causal attention; GQA with 32 query heads and 8 key/value heads of dim 128; q and k get RMSNorm and
+ * partial RoPE (rotary fraction 0.33); a local layer's output is multiplied elementwise by
+ * sigmoid(g_proj(h)) before o_proj, a global layer's is not. Section 2.3 "KV cache analysis": local
+ * layers cache a fixed 128-token window, global layers the whole sequence.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers owned by the caller; the library never allocates, frees or
+ *    synchronises. Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = null stream).
+ *  - bf16 tensors hold IEEE bfloat16 bit patterns (uint16). Layouts are row-major, last dim fastest.
+ *  - Every argument is validated on the host before any launch. A bad argument returns a non-zero
+ *    zg_status, leaves all buffers untouched and sets a thread-local message (zg_last_error). No
+ *    entry point aborts or lets a C++ exception escape.
+ *  - ZG_ERR_HIP: a HIP call or kernel launch reported an error. Faults inside a kernel surface at the
+ *    caller's next synchronisation, as with any asynchronous launch.
+ *  - NaN/Inf in inputs propagate; the hot path does no value checks.
+ *  - No mutable global state: calls from several host threads are safe; calls that share output
+ *    buffers or a workspace must be ordered by the caller.
+ */
+#ifndef ZG_ATTN_H
+#define ZG_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZG_OK = 0,
+  ZG_ERR_NULL = 1,        /* a required pointer is NULL */
+  ZG_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or inconsistent */
+  ZG_ERR_UNSUPPORTED = 3, /* a valid configuration this build has no kernel for */
+  ZG_ERR_WORKSPACE = 4,   /* workspace pointer NULL or smaller than the *_workspace_bytes query */
+  ZG_ERR_HIP = 5          /* HIP runtime / launch error */
+} zg_status;
+
+/* One attention layer's configuration.
+ * Readings where the pages are silent: RMSNorm is per head over head_dim (one weight vector for q,
+ * one for k); RMSNorm precedes RoPE; rotate-half pairs (i, i + rot_dim/2) with
+ * theta_i = rope_base^(-2i/rot_dim); positions are 0-based; softmax scale 1/sqrt(head_dim). */
+typedef struct {
+  int32_t n_q_heads;     /* Hq, e.g. 32 */
+  int32_t n_kv_heads;    /* Hkv, e.g. 8; Hq/Hkv must be 1, 2, 4 or 8 (else UNSUPPORTED) */
+  int32_t head_dim;      /* D; 128 only (else UNSUPPORTED) */
+  int32_t window;        /* W > 0: query i sees keys j with i-W < j <= i; W == 0: full causal */
+  int32_t gated;         /* 1: out *= sigmoid(gate) elementwise; 0: gate ignored (may be NULL) */
+  int32_t rot_dim;       /* rotated dims, even, 0 <= rot_dim <= 64 (ZGCM-1: floor(0.33*128) = 42) */
+  double rope_base;      /* e.g. 1e4, 1e6, 1e7; > 1 */
+  float rms_eps;         /* RMSNorm epsilon, e.g. 1e-6; >= 0 */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
+} zg_attn_cfg;
+
+/* Elements between consecutive tokens of q, k, v, gate and out (token t of sequence b starts at
+ * base + (b*T + t) * stride). Passing NULL means packed: Hq*D for q/gate/out, Hkv*D for k/v. A
+ * stride must be >= the packed one and a multiple of 8 (16-byte aligned rows). */
+typedef struct {
+  int64_t q, k, v, gate, out;
+} zg_token_strides;
+
+/* ---------------------------------------------------------------------------------------------
+ * Prefill: out[b,t,h,:] = gate?(sigmoid(gate[b,t,h,:])) * sum_j softmax_j(q_hat.k_hat_j*scale) v[b,j,h/G,:]
+ * over the key set of query t (window or full causal), with q_hat/k_hat = RoPE(RMSNorm(.)) at
+ * position pos0 + t. (zh-TW translation, section 2.1 and Fig. 3: the gated SWA formula.)
+ *   q, gate, out: [B, T, Hq, D] bf16;  k, v: [B, T, Hkv, D] bf16  (see zg_token_strides)
+ *   q_norm_w, k_norm_w: fp32[D] device pointers, or NULL for weight 1.
+ *   workspace: device scratch of at least zg_attn_prefill_workspace_bytes(cfg, B, T) bytes (it holds
+ *   the normalised, rotated keys); may be NULL when that query returns 0.
+ * Numerics: fp32 norm/RoPE/softmax/accumulation; q_hat, k_hat and the softmax weights are rounded to
+ * bf16 at the matrix-core inputs; out is rounded to nearest-even bf16.
+ * Errors: NULL -> ZG_ERR_NULL; B < 1, T < 1, pos0 < 0, bad strides -> ZG_ERR_SHAPE; head_dim != 128,
+ * Hq/Hkv not in {1,2,4,8}, rot_dim odd or > 64 -> ZG_ERR_UNSUPPORTED; small workspace ->
+ * ZG_ERR_WORKSPACE. */
+size_t zg_attn_prefill_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T);
+
+zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t pos0,
+                          const void* q, const void* k, const void* v, const void* gate,
+                          const float* q_norm_w, const float* k_norm_w,
+                          const zg_token_strides* strides,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Decode: one new token per sequence, attending over a KV cache of normalised, rotated keys.
+ * (zh-TW translation, section 2.3: local layers keep a fixed 128-token window, global layers keep
+ * the whole sequence; decoding is memory-bandwidth bound.)
+ *   seqlens: device int32[B]; seqlens[b] >= 1 is the number of positions AFTER appending, so the new
+ *            token sits at pos = seqlens[b] - 1 and must be < max_seqlen.
+ *   window W > 0 (ring): k_cache, v_cache are [B, W, Hkv, D] bf16; position p lives in slot p % W
+ *            (cache_stride is ignored and may be 0).
+ *   window 0 (linear):  k_cache, v_cache are [B, cache_stride, Hkv, D] bf16; position p in row p;
+ *            cache_stride >= max_seqlen.
+ *   q_new, gate, out: [B, Hq, D] bf16; k_new, v_new: [B, Hkv, D] bf16.
+ * The call RMSNorms and rotates q_new and k_new at pos, writes k_hat_new and v_new into the cache
+ * row of pos, then attends over positions max(0, pos-W+1)..pos (ring) or 0..pos (linear) and
+ * applies the gate if cfg->gated. The result equals prefill row pos over the same keys.
+ *   workspace >= zg_attn_decode_workspace_bytes(cfg, B, max_seqlen) (split-KV partials).
+ * Errors as for prefill; max_seqlen < 1 or cache_stride < max_seqlen (linear) -> ZG_ERR_SHAPE.
+ * seqlens values are device data and are not validated; out-of-range values are undefined
+ * behaviour. */
+size_t zg_attn_decode_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int64_t max_seqlen);
+
+zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                         int64_t max_seqlen, const void* q_new, const void* k_new,
+                         const void* v_new, const void* gate, const float* q_norm_w,
+                         const float* k_norm_w, void* k_cache, void* v_cache,
+                         const int32_t* seqlens, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * KV-cache bytes of an n_layers stack (pure host arithmetic; zh-TW translation, section 2.3):
+ *   sum over layers l = 1..n_layers of  rows(l) * 2 * n_kv_heads * head_dim * elem_bytes * batch,
+ *   rows(l) = seqlen if layer l is global (global_every > 0 && l % global_every == 0, or window <= 0)
+ *             else min(seqlen, window).
+ * ZGCM-1: zg_kv_bytes(32, 6, 8, 128, 128, 2, 1, 262144) = 5,382,864,896 (5.0 GiB) and
+ *         zg_kv_bytes(32, 1, ...) = 34,359,738,368 (32.0 GiB).
+ * Returns 0 and sets zg_last_error on negative arguments or uint64 overflow. */
+uint64_t zg_kv_bytes(int32_t n_layers, int32_t global_every, int32_t n_kv_heads, int32_t head_dim,
+                     int32_t window, int32_t elem_bytes, int64_t batch, int64_t seqlen);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* zg_last_error(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Building blocks of one Pre-LN attention layer with projections (zh-TW translation, section 2.1
+ * and Fig. 3: a normalised hidden state h feeds parallel q/k/v/gate projections; o_proj follows;
+ * section 3.1 names Pre-LN).
+ *
+ * zg_rmsnorm: y[r,:] = bf16( x[r,:] / sqrt(mean(x[r,:]^2) + eps) * (w ? w : 1) ).
+ *   x: fp32 [rows, dim]; w: fp32 [dim] or NULL; y: bf16 [rows, dim]. dim % 8 == 0, dim <= 8192. */
+zg_status zg_rmsnorm(int64_t rows, int32_t dim, const float* x, const float* w, float eps,
+                     void* y_bf16, void* stream);
+
+/* zg_gemm_bf16: Y = X * W^T with fp32 accumulation.
+ *   X: bf16 [M, K] (row stride K); W: bf16 [N, K] (row stride K).
+ *   If residual != NULL: residual[m, n] += Y[m, n] (fp32 [M, N], row stride N).
+ *   If y != NULL:        y[m, n] = bf16(Y[m, n]) (bf16, row stride ldy >= N).
+ *   At least one of residual / y must be non-NULL. K % 64 == 0, N % 8 == 0, M >= 1. */
+zg_status zg_gemm_bf16(int64_t M, int32_t N, int32_t K, const void* x_bf16, const void* w_bf16,
+                       float* residual, void* y_bf16, int64_t ldy, void* stream);
+
+/* zg_attn_layer: one whole layer, x <- x + o_proj(attn(RMSNorm(x))) on B*T tokens of width
+ * hidden = Hq*D, in place on the fp32 residual x [B, T, hidden].
+ *   w_qkvg: bf16 [(Hq + 2*Hkv + (gated ? Hq : 0)) * D, hidden], rows ordered q, k, v, gate;
+ *   w_o: bf16 [hidden, Hq*D]. The input RMSNorm has weight 1 and eps cfg->rms_eps.
+ *   workspace >= zg_attn_layer_workspace_bytes(cfg, B, T). */
+size_t zg_attn_layer_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T);
+
+zg_status zg_attn_layer(const zg_attn_cfg* cfg, int32_t B, int32_t T, float* x,
+                        const void* w_qkvg, const void* w_o, const float* q_norm_w,
+                        const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZG_ATTN_H */

@@ -1,0 +1,85 @@
+"""Properties the GPU path must show exactly or within bf16 (no oracle needed)."""
+import numpy as np
+import pytest
+import torch
+
+import global_causal_attention_amd as zg
+import synth_inputs as si
+from helpers import assert_parity, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(seed, B=2, T=300):
+    gen = si.generator(seed)
+    x = si.prefill_layer(gen, B, T)
+    return {k: v.to(DEV) for k, v in x.items()}
+
+
+@pytest.mark.parametrize("W", [128, 0])
+def test_zero_gate_is_bitwise_half(W):
+    x = _inputs(1)
+    ung = zg.zg_attn_prefill(zg.AttnConfig(window=W, gated=False), x["q"], x["k"], x["v"])
+    half = zg.zg_attn_prefill(zg.AttnConfig(window=W, gated=True), x["q"], x["k"], x["v"],
+                              torch.zeros_like(x["q"]))
+    torch.cuda.synchronize()
+    assert torch.equal(half.float(), ung.float() * 0.5)
+
+
+def test_v_one_gives_one():
+    x = _inputs(2)
+    ones = torch.ones_like(x["v"])
+    for W in (128, 5, 0):
+        o = zg.zg_attn_prefill(zg.AttnConfig(window=W, gated=False), x["q"], x["k"], ones)
+        torch.cuda.synchronize()
+        assert (o.float() - 1).abs().max().item() <= 2 ** -8
+
+
+@pytest.mark.parametrize("W", [128, 0])
+def test_runs_are_bitwise_identical(W):
+    x = _inputs(3, B=2, T=1500)
+    cfg = zg.AttnConfig(window=W, gated=W > 0)
+    a = zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"])
+    b = zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_window_covering_sequence_equals_causal():
+    x = _inputs(4, B=1, T=200)
+    a = zg.zg_attn_prefill(zg.AttnConfig(window=0, gated=True), x["q"], x["k"], x["v"], x["gate"])
+    b = zg.zg_attn_prefill(zg.AttnConfig(window=200, gated=True), x["q"], x["k"], x["v"], x["gate"])
+    c = zg.zg_attn_prefill(zg.AttnConfig(window=100000, gated=True), x["q"], x["k"], x["v"], x["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("W", [128, 0])
+def test_decode_equals_prefill_row(W):
+    """Cache built from the prefill's own keys: decode at pos reproduces prefill row pos."""
+    T = 700
+    x = _inputs(5, B=2, T=T)
+    cfg = zg.AttnConfig(window=W, gated=W > 0, rope_base=1e6)
+    full = zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"])
+    # normalised/rotated keys as the prefill computes them (its workspace holds k_hat)
+    ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, 2, T), dtype=torch.uint8, device=DEV)
+    zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"], workspace=ws)
+    khat = ws[: 2 * T * 8 * 128 * 2].view(torch.bfloat16).view(2, T, 8, 128)
+    pos = torch.tensor([T - 1, 400], dtype=torch.int32)
+    rows = W if W > 0 else T
+    kc = torch.zeros((2, rows, 8, 128), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    for b in range(2):
+        p = int(pos[b])
+        for j in range(max(0, p - W + 1) if W > 0 else 0, p):
+            r = j % W if W > 0 else j
+            kc[b, r] = khat[b, j]
+            vc[b, r] = x["v"][b, j]
+    sel = lambda t: torch.stack([t[b, int(pos[b])] for b in range(2)])
+    out = zg.zg_attn_decode(cfg, sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["gate"]), kc, vc,
+                            (pos + 1).to(DEV), max_seqlen=T)
+    torch.cuda.synchronize()
+    for b in range(2):
+        assert_parity(out[b], f64(full[b, int(pos[b])]), f"decode vs prefill row W={W}",
+                      max_abs=2e-2, mean_abs=2e-3)

@@ -1,0 +1,119 @@
+"""GPU prefill vs the fp64 oracle on seeded inputs, through the C ABI.
+
+Sizes are small enough for the oracle to finish in seconds but span several query/key tiles and a
+ragged tail; the T=1024 gated local layer (seed 1000, base 1e4) is compared in full."""
+import numpy as np
+import pytest
+import torch
+
+import global_causal_attention_amd as zg
+import oracle
+import synth_inputs as si
+from helpers import assert_parity, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(B, T, Hq, Hkv, W, gated, base, seed, pos0=0, rot=42, norm_w=False, scale=0.0,
+         q_scale=1.0):
+    print(f"[case] B={B} T={T} Hq={Hq} Hkv={Hkv} W={W} gated={gated} base={base} seed={seed} "
+          f"pos0={pos0} rot={rot} norm_w={norm_w}", flush=True)
+    gen = si.generator(seed)
+    x = si.prefill_layer(gen, B, T, Hq, Hkv, 128, gated=True)
+    qw = kw = None
+    if norm_w:
+        qw = (torch.rand(128, generator=gen) * 1.5 + 0.25) * q_scale
+        kw = torch.rand(128, generator=gen) * 1.5 + 0.25
+    cfg = zg.AttnConfig(n_q_heads=Hq, n_kv_heads=Hkv, window=W, gated=gated, rot_dim=rot,
+                        rope_base=base, softmax_scale=scale)
+    dev = {k: (v.to(DEV) if v is not None else None) for k, v in x.items()}
+    out = zg.zg_attn_prefill(cfg, dev["q"], dev["k"], dev["v"], dev["gate"],
+                             q_norm_w=None if qw is None else qw.to(DEV),
+                             k_norm_w=None if kw is None else kw.to(DEV), pos0=pos0)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["gate"]), window=W,
+                         gated=gated, rot_dim=rot, rope_base=base, eps=1e-6,
+                         q_norm_w=None if qw is None else qw.double().numpy(),
+                         k_norm_w=None if kw is None else kw.double().numpy(),
+                         scale=scale if scale > 0 else None, pos0=pos0)
+    return out, ref
+
+
+def test_local_layer_T1024_full():
+    out, ref = _run(1, 1024, 32, 8, 128, True, 1e4, 1000)
+    assert_parity(out, ref, "gated SWA B=1 T=1024")
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,W,gated,base,pos0", [
+    (1, 1, 32, 8, 128, True, 1e4, 0),
+    (1, 5, 32, 8, 128, True, 1e4, 0),
+    (2, 127, 32, 8, 128, True, 1e4, 0),
+    (1, 128, 32, 8, 128, True, 1e6, 0),
+    (1, 129, 32, 8, 128, True, 1e6, 0),
+    (3, 300, 32, 8, 128, True, 1e7, 0),
+    (1, 333, 32, 8, 0, False, 1e6, 0),
+    (2, 200, 32, 8, 0, True, 1e4, 0),
+    (1, 257, 4, 1, 128, True, 1e4, 0),
+    (1, 190, 8, 2, 3, True, 1e4, 0),
+    (1, 150, 8, 8, 1, False, 1e4, 0),
+    (1, 260, 16, 2, 64, True, 1e4, 0),
+    (2, 100, 8, 1, 0, False, 1e4, 0),
+    (1, 300, 32, 8, 128, True, 1e7, 200000),
+    (1, 70, 32, 8, 0, False, 1e7, 262000),
+])
+def test_prefill_edges(B, T, Hq, Hkv, W, gated, base, pos0):
+    out, ref = _run(B, T, Hq, Hkv, W, gated, base, 7 + T + W, pos0=pos0)
+    assert_parity(out, ref, f"B={B} T={T} Hq={Hq}/{Hkv} W={W}")
+
+
+def test_prefill_norm_weights_scale_and_rot_dims():
+    for rot, scale in ((0, 0.0), (64, 0.05), (16, 0.0)):
+        out, ref = _run(1, 200, 32, 8, 128, True, 1e4, 11, rot=rot, norm_w=True, scale=scale)
+        assert_parity(out, ref, f"rot={rot} scale={scale} with norm weights")
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _rounded_operand_reference(x, W, gated, qw, kw, base=1e4):
+    """Test-side model of the kernel's rounding points built on the oracle's prologue: q_hat, k_hat
+    and the softmax weights rounded to bf16 (the matrix-core operands), everything else fp64."""
+    q, k, v = f64(x["q"])[0], f64(x["k"])[0], f64(x["v"])[0]
+    T = q.shape[0]
+    qh = _bf16(oracle.qk_prologue(q, np.arange(T), qw, rot_dim=42, rope_base=base, eps=1e-6))
+    kh = _bf16(oracle.qk_prologue(k, np.arange(T), kw, rot_dim=42, rope_base=base, eps=1e-6))
+    out = np.zeros(q.shape)
+    for t in range(T):
+        lo = max(0, t - W + 1) if W > 0 else 0
+        s = np.einsum("hd,jhd->hj", qh[t], np.repeat(kh[lo:t + 1], 4, axis=1)) / np.sqrt(128)
+        p = np.exp(s - s.max(-1, keepdims=True))
+        o = np.einsum("hj,jhd->hd", _bf16(p), np.repeat(v[lo:t + 1], 4, axis=1)) / p.sum(-1)[:, None]
+        if gated:
+            o = o / (1 + np.exp(-f64(x["gate"])[0, t]))
+        out[t] = o
+    return out[None]
+
+
+@pytest.mark.parametrize("W", [0, 128])
+def test_prefill_peaky_logits(W):
+    """q norm weight ~8 makes logits ~N(0, 64) and exercises the running-max rescale.
+
+    At logit std 8 the bf16 rounding of the matrix-core operands alone moves outputs by up to
+    ~0.14 (a test-side emulation of exactly those rounding points reproduces the GPU's error), so
+    the fp64-oracle bar is scaled with the logit std: max-abs 2e-2 * 8, mean-abs 2e-3 * 3. The
+    tighter check is against the rounding model. The model still differs from the kernel in two
+    ways that also scale with the logit std: the kernel's fp32 prologue can round an element of
+    q_hat/k_hat to the neighbouring bf16 value of the fp64 one, and the kernel rounds softmax
+    weights taken relative to the running maximum rather than the final one; hence max-abs 4e-2
+    there with the standard mean-abs bar."""
+    gated = W > 0
+    out, ref = _run(1, 400, 32, 8, W, gated, 1e4, 12 + W, norm_w=True, q_scale=8.0)
+    assert_parity(out, ref, f"peaky logits W={W} vs fp64 oracle", max_abs=0.16, mean_abs=6e-3)
+    gen = si.generator(12 + W)
+    x = si.prefill_layer(gen, 1, 400, 32, 8, 128, gated=True)
+    qw = ((torch.rand(128, generator=gen) * 1.5 + 0.25) * 8.0).double().numpy()
+    kw = (torch.rand(128, generator=gen) * 1.5 + 0.25).double().numpy()
+    model = _rounded_operand_reference(x, W, gated, qw, kw)
+    assert_parity(out, model, f"peaky logits W={W} vs bf16-operand model", max_abs=4e-2)
