@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeParams p) {
       const u32x4* s4 = reinterpret_cast<const u32x4*>(src + 64 * half);
 #pragma unroll
       for (int i = 0; i < 8; ++i) unpack8(s4[i], x + 8 * i);
-      norm_rope_row(x, half, is_q ? p.q_norm_w : p.k_norm_w, p.eps, pos, p.rope,
-                    stage + 64 * pair);
+      norm_rope_row(x, half, is_q ? p.q_norm_w : p.k_norm_w, p.eps, pos, p.rope, stage, pair,
+                    128);
       if (is_q) {
         f32x4* dst = reinterpret_cast<f32x4*>(p.qhat + ((int64_t)b * p.Hq + h) * kHeadDim + 64 * half);
 #pragma unroll

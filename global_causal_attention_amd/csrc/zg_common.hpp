@@ -50,23 +50,26 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// cos/sin of 2*pi*(pos * rev), with the product reduced modulo one revolution in fp64 so the angle
-// keeps full precision at positions up to 2^18 and beyond.
+// cos/sin of 2*pi*(pos * rev). The product is reduced modulo one revolution in fp64, so the angle
+// keeps full precision at positions up to 2^18 and beyond; v_sin_f32 / v_cos_f32 take their input
+// in revolutions (max abs error ~1.2e-7 on [-0.5, 0.5]).
 __device__ __forceinline__ void rope_cs(int64_t pos, double rev, float& c, float& s) {
   double r = (double)pos * rev;
   r = r - __builtin_rint(r);
-  float a = (float)(r * 6.283185307179586476925286766559);
-  sincosf(a, &s, &c);
+  const float a = (float)r;
+  s = __builtin_amdgcn_sinf(a);
+  c = __builtin_amdgcn_cosf(a);
 }
 
 // Fused QK-RMSNorm + partial RoPE of one 128-wide head row, split over two adjacent lanes:
 // lane parity `half` holds dims [64*half, 64*half + 64) in x[0..63] (fp32, already loaded).
 // RMSNorm: x * w / sqrt(mean(x^2) + eps) over all 128 dims (partner lane = lane ^ 1).
 // RoPE: pairs (i, i + rot/2), i < rot/2 <= 32, all inside half 0, rotated by pos * theta_i.
-// `stage` is this lane pair's 64-float LDS scratch row (only half 0 touches it).
+// `stage` is LDS scratch laid out [dim][row] with `stride` rows (this lane pair is `row`), so lanes
+// of consecutive rows hit consecutive banks; only half 0 touches it.
 __device__ __forceinline__ void norm_rope_row(float* x, int half, const float* __restrict__ w,
                                               float eps, int64_t pos, const RopeTable& rt,
-                                              float* stage) {
+                                              float* stage, int row, int stride) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
@@ -86,21 +89,24 @@ __device__ __forceinline__ void norm_rope_row(float* x, int half, const float* _
   }
   const int h = rt.half;
   if (half == 0 && h > 0) {
+    float* st = stage + row;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) stage[i] = x[i];
+    for (int i = 0; i < 64; ++i)
+      if (i < 2 * h) st[i * stride] = x[i];
 #pragma unroll
     for (int i = 0; i < kMaxRotHalf; ++i) {
       if (i < h) {
         float c, s;
         rope_cs(pos, rt.rev[i], c, s);
-        const float a = stage[i];
-        const float b = stage[i + h];
-        stage[i] = a * c - b * s;
-        stage[i + h] = b * c + a * s;
+        const float a = st[i * stride];
+        const float b = st[(i + h) * stride];
+        st[i * stride] = a * c - b * s;
+        st[(i + h) * stride] = b * c + a * s;
       }
     }
 #pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = stage[i];
+    for (int i = 0; i < 64; ++i)
+      if (i < 2 * h) x[i] = st[i * stride];
   }
 }
 
