@@ -137,6 +137,10 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
         (cfg->gated && !aligned16(gate)) || (q_norm_w && !aligned16(q_norm_w)) ||
         (k_norm_w && !aligned16(k_norm_w)))
       return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    // K/V tiles are fetched through 32-bit buffer offsets within one sequence's rows
+    const int64_t max_row_bytes = 2 * std::max<int64_t>(s.v, Hkv * kD);
+    if ((int64_t)(T + 64) * max_row_bytes >= (int64_t(1) << 32))
+      return fail(ZG_ERR_UNSUPPORTED, "T * token stride of v (bytes) must stay below 4 GiB");
     const size_t need = zg_attn_prefill_workspace_bytes(cfg, B, T);
     if (need > 0 && (!workspace || workspace_bytes < need))
       return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",

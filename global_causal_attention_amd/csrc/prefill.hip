@@ -19,6 +19,8 @@
 // {4-7, 12-15}, so V is stored transposed in LDS with bits 2 and 3 of the key index swapped, which
 // makes each lane's 8 A-operand values one contiguous 16-byte LDS read. O^T keeps one query per lane,
 // so the online-softmax rescale is a per-lane scalar.
+#include <type_traits>
+
 #include "zg_common.hpp"
 
 namespace zg {
@@ -30,16 +32,15 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kNk = 64;                     // keys per tile
 constexpr int kRow = 256;                   // LDS bytes per K or V row (unpadded, chunk-swizzled)
 constexpr int kTileBytes = kNk * kRow;      // 16384
-constexpr int kQWaveBytes = 32 * kRow;      // per-wave q staging: 32 chunk-swizzled rows
-// LDS: two K buffers, then two V buffers. q staging aliases them before the first tile.
-constexpr int kLdsK0 = 0;
+constexpr int kLdsK0 = 0;                   // two K buffers, then two V buffers
 constexpr int kLdsV0 = 2 * kTileBytes;
 constexpr int kLdsBytes = 4 * kTileBytes;
+constexpr int kQWaveBytes = 32 * kRow;      // per-wave q staging: 32 chunk-swizzled rows
 static_assert(kWaves * kQWaveBytes <= kLdsBytes, "q staging aliases the K/V buffers");
 
-// 16-byte chunk c of tile row r is stored at chunk c ^ swz(r). Sixteen consecutive rows read at one
-// logical chunk (the QK^T operand) and four aligned rows read at four adjacent chunks (the transposed
-// V operand) both land on distinct banks.
+// 16-byte chunk c of a staged row r lives at chunk c ^ swz(r). Sixteen consecutive rows read at
+// one logical chunk (the QK^T operand) and the four aligned rows x four adjacent chunks of a
+// transposing read (the PV operand) both land on distinct banks.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8 a, const bf16x8 b, const f32x16 c) {
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -109,11 +110,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int qb = wave / G;
   const int head = kvh * G + hg;
   const int qbase = r0 + 32 * qb;
+  const float c = p.scale_log2;
 
-  // ---- q prologue: wave-private staging (32 chunk-swizzled rows of 256 B, aliasing K/V buffers)
+  // ---- q prologue: q_hat * scale * log2(e) rounded to bf16, staged through this wave's
+  // chunk-swizzled rows (aliasing the K/V buffers), read back as MFMA B operands
   bf16x8 qf[8];
   {
-    unsigned char* qs = smem + wave * 32 * kRow;
+    unsigned char* qs = smem + wave * kQWaveBytes;
     const int r = lane >> 1;
     const int half = lane & 1;
     const int t = qbase + r;
@@ -132,6 +135,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     norm_rope_row(x, half, p.q_norm_w, p.eps, p.pos0 + t, p.rope, reinterpret_cast<float*>(qs), r,
                   32);
 #pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] *= c;
+#pragma unroll
     for (int i = 0; i < 8; ++i)
       *reinterpret_cast<u32x4*>(qs + r * kRow + 16 * ((8 * half + i) ^ swz(r))) = pack8(x + 8 * i);
     __syncthreads();
@@ -147,132 +152,94 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   if (W > 0) k_begin = max(0, r0 - W + 1) & ~(kNk - 1);
   const int n_tiles = (q_last + 1 - k_begin + kNk - 1) / kNk;
 
-  // ---- ping-pong schedule. Waves 0-3 (group A) and 4-7 (group B) each hold one wave per SIMD
-  // and run one phase apart, so in every phase between two barriers one wave of each SIMD issues
-  // MFMAs (QK^T of tile j and PV of tile j-1) while the other runs the softmax of its tile on the
-  // vector ALUs. During its softmax phase a group streams the next tile it owns straight from
-  // memory into LDS (group A: K tiles, group B: V tiles):
-  //   phase 2j   : A MFMA(j)                  B softmax(j-1), loads V_j     (read from 2j+2)
-  //   phase 2j+1 : A softmax(j), loads K_{j+1} (read from 2j+2)   B MFMA(j)
-  // Two K and two V buffers; a buffer is refilled only after its last reader's phase ended.
-  const bool grp_b = wave >= 4;
+  // ---- tile streaming: waves 0-3 bring K rows, waves 4-7 V rows, straight into chunk-swizzled
+  // LDS rows (buffer_load ... lds, 4 rows = 1 KB per instruction, 4 per wave per tile). The
+  // buffer's range check returns zeros for rows at or past T. Iteration j reads K_{j+1} and V_{j-1}
+  // and streams K_{j+2} and V_j into the buffers those tiles' predecessors left; the loads are
+  // inline asm (so later LDS reads do not wait for them) and are awaited before the barrier that
+  // ends the iteration.
+  const bool v_loader = wave >= 4;
   const int wg = wave & 3;
-  const int dma_row = 16 * wg + (lane >> 4);       // + 4 i, i = 0..3
-  const int dma_pch = lane & 15;                   // physical chunk this lane fills
-  const uint16_t* g_src = grp_b ? p.v + (int64_t)b * T * p.sv + (int64_t)kvh * kHeadDim
-                                : p.khat + ((int64_t)b * T * p.Hkv + kvh) * kHeadDim;
-  const int64_t g_rstride = grp_b ? p.sv : (int64_t)p.Hkv * kHeadDim;
-  const int buf0 = grp_b ? kLdsV0 : kLdsK0;
-
-  auto dma_tile = [&](int t) {  // rows past the end are clamped to row T-1 (in bounds)
-    const int kt = k_begin + t * kNk;
-    unsigned char* dst = smem + buf0 + (t & 1) * kTileBytes + 16 * wg * kRow;
+  const int row_bytes = (int)((v_loader ? p.sv : (int64_t)p.Hkv * kHeadDim) * 2);
+  const uint16_t* slab = v_loader ? p.v + (int64_t)b * T * p.sv + (int64_t)kvh * kHeadDim
+                                  : p.khat + ((int64_t)b * T * p.Hkv + kvh) * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, T * row_bytes, 0x00020000);
+  // lane -> (row (lane >> 4) of the 4-row group i, physical chunk lane & 15)
+  auto dma_voff = [&](int i) -> uint32_t {
+    const int row = 4 * i + (lane >> 4);  // row within the wave's 16 (swizzle uses row & 15)
+    return (uint32_t)((lane >> 4) * row_bytes + 16 * ((lane & 15) ^ swz(row)));
+  };
+  const uint32_t lds_k = (uint32_t)(uintptr_t)smem + kLdsK0;
+  const uint32_t lds_v = (uint32_t)(uintptr_t)smem + kLdsV0;
+  auto dma_tile = [&](int t, bool is_v) {  // tile t into buffer t & 1
+    const uint32_t base = (is_v ? lds_v : lds_k) + (t & 1) * kTileBytes + 16 * wg * kRow;
+    const uint32_t row0 = (uint32_t)(k_begin + t * kNk + 16 * wg);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = dma_row + 4 * i;
-      const int key = min(kt + row, T - 1);
-      const uint16_t* src = g_src + (int64_t)key * g_rstride + 8 * (dma_pch ^ swz(row));
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(dst + 4 * i * kRow),
-                                       16, 0, 0);
+      const uint32_t m0v = base + 4 * i * kRow;
+      const uint32_t soff = (row0 + 4 * i) * (uint32_t)row_bytes;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   ::"s"(m0v), "v"(dma_voff(i)), "s"(rsrc), "s"(soff) : "memory", "m0");
     }
   };
-  // V rows past the end must read as zero (their weights are zero, and 0 * Inf would be NaN)
-  auto zero_tail = [&](int t) {
-    const int kt = k_begin + t * kNk;
-    if (grp_b && kt + kNk > T) {
-      __builtin_amdgcn_s_waitcnt(0);
-      unsigned char* dst = smem + buf0 + (t & 1) * kTileBytes;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = dma_row + 4 * i;
-        if (kt + row >= T)
-          *reinterpret_cast<u32x4*>(dst + row * kRow + 16 * dma_pch) = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
+  auto vm_wait = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  // ---- running softmax state: one query per lane; lanes l and l^32 share the query. The maximum
-  // is only raised when a tile exceeds it by more than 2^8 in exp2 units (lazy rescale), so
-  // unnormalised weights stay <= 256.
+  // ---- MFMA operand addresses: per-lane byte offsets, everything else is an immediate
+  int k_off[8];     // QK^T operand of step st: key row l32 (+32 per key block), dims 16 st + 8 hi
+#pragma unroll
+  for (int st = 0; st < 8; ++st) k_off[st] = kLdsK0 + l32 * kRow + 16 * ((2 * st + hi) ^ swz(l32));
+  int v_off[2][4];  // PV operand, transposing read x of dim block db (+16 rows per key step)
+  {
+    const int tr_row = 4 * hi + ((lane & 15) >> 2);
+    const int tr_dch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int row = 8 * x + tr_row;
+        v_off[x][db] = kLdsV0 + row * kRow + 16 * ((4 * db + tr_dch) ^ swz(row)) + 8 * (lane & 1);
+      }
+  }
+  // 9th key-dimension step: A = (1, 0, ...) on every key row, B = (-m_ref, 0, ...) per query, so
+  // the MFMA subtracts the softmax reference and exp2 needs no extra arithmetic
+  const bf16x8 one_op = hi ? bf16x8{} : bf16x8{(__bf16)1.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
+                                               (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+  float m_ref = 0.f;          // bf16-representable softmax reference (log2 units), per query
+  bool m_valid = false;       // set once the query has seen an unmasked key
+  bf16x8 qm = bf16x8{};       // B operand of the 9th step
+
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = -1e30f;
   float l_run = 0.f;
-  const float c = p.scale_log2;
   const int my_q = qbase + l32;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  f32x16 s[2];
-  uint32_t pk[2][8];
 
-  // A operands of one MFMA phase, in issue order: 16 QK^T operands (K rows, st-major, both key
-  // blocks) then 16 PV operands (V^T via two transposing reads each, st-major, four dim blocks).
-  const int tr_row = 4 * hi + ((lane & 15) >> 2);          // + 16 st + 8 x
-  const int tr_dch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 db: logical 16-B chunk
-  const int tr_sub = 8 * (lane & 1);
-  auto operand = [&](int j, int i) -> bf16x8 {
-    if (i < 16) {
-      const int st = i >> 1, kb = i & 1;
-      const int row = 32 * kb + l32;
-      return *reinterpret_cast<const bf16x8*>(smem + kLdsK0 + (j & 1) * kTileBytes + row * kRow +
-                                              16 * ((2 * st + hi) ^ swz(row)));
-    }
-    const int st = (i - 16) >> 2, db = (i - 16) & 3;
-    const unsigned char* vb = smem + kLdsV0 + ((j - 1) & 1) * kTileBytes;
-    const int r_a = 16 * st + tr_row;
-    const int r_b = r_a + 8;
-    const int ch = 4 * db + tr_dch;
-    const i16x4 a = lds_read_tr(vb + r_a * kRow + 16 * (ch ^ swz(r_a)) + tr_sub);
-    const i16x4 bb = lds_read_tr(vb + r_b * kRow + 16 * (ch ^ swz(r_b)) + tr_sub);
+  auto rd_k = [&](int par, int st, int kb) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(smem + k_off[st] + par * kTileBytes + kb * 32 * kRow);
+  };
+  auto rd_v = [&](int par, int st, int db) -> bf16x8 {
+    const unsigned char* base = smem + par * kTileBytes + st * 16 * kRow;
+    const i16x4 a = lds_read_tr(base + v_off[0][db]);
+    const i16x4 bb = lds_read_tr(base + v_off[1][db]);
     const i16x4 both[2] = {a, bb};
     return __builtin_bit_cast(bf16x8, both);
   };
-  auto qk_only = [&](int j) {
+  auto qk_all = [&](int par, f32x16 (&s)[2]) {  // S = K Q^T - m_ref, all 18 MFMAs
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int st = i >> 1, kb = i & 1;
-      s[kb] = mfma32(operand(j, i), qf[st], s[kb]);
-    }
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(rd_k(par, st, kb), qf[st], s[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(one_op, qm, s[kb]);
   };
-  auto mfma_phase = [&](int j) {  // j >= 1: S = K_j Q^T, then O^T += V_{j-1}^T P^T
-    constexpr int kAhead = 8;
-    bf16x8 ring[kAhead];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) ring[i] = operand(j, i);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const bf16x8 a = ring[i % kAhead];
-      if (i < 16) {
-        const int st = i >> 1, kb = i & 1;
-        s[kb] = mfma32(a, qf[st], s[kb]);
-      } else {
-        const int st = (i - 16) >> 2, db = (i - 16) & 3;
-        const int kb = st >> 1, h8 = (st & 1) * 4;
-        u32x4 bw = {pk[kb][h8], pk[kb][h8 + 1], pk[kb][h8 + 2], pk[kb][h8 + 3]};
-        o[db] = mfma32(a, __builtin_bit_cast(bf16x8, bw), o[db]);
-      }
-      if (i + kAhead < 32) ring[i % kAhead] = operand(j, i + kAhead);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto final_pv = [&](int j) {  // O^T += V_j^T P^T
-#pragma unroll
-    for (int i = 16; i < 32; ++i) {
-      const int st = (i - 16) >> 2, db = (i - 16) & 3;
-      const int kb = st >> 1, h8 = (st & 1) * 4;
-      u32x4 bw = {pk[kb][h8], pk[kb][h8 + 1], pk[kb][h8 + 2], pk[kb][h8 + 3]};
-      o[db] = mfma32(operand(j + 1, i), __builtin_bit_cast(bf16x8, bw), o[db]);
-    }
-  };
-  auto softmax_phase = [&](int j) {  // S -> P (bf16, packed), running max / sum
+  auto mask_tile = [&](int j, f32x16 (&s)[2]) {
     const int kt = k_begin + j * kNk;
-    const bool need_mask = (kt + kNk - 1 > qbase) || ((W > 0) && (kt < qbase + 31 - W + 1));
-    if (need_mask) {
+    const bool need = (kt + kNk - 1 > qbase) || ((W > 0) && (kt < qbase + 31 - W + 1));
+    if (need) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -282,57 +249,166 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
           s[kb][r] = ok ? s[kb][r] : -INFINITY;
         }
     }
-    float mx = fmaxf(s[0][0], s[0][1]);
+  };
+  // Softmax weights of the current tile: P = exp2(S) (S already has the reference subtracted).
+  // Unless a lane's tile sum exceeds 2^64 (or the query has no reference yet) nothing needs
+  // rescaling; otherwise the slow path raises the reference to the tile maximum, rescales l and O,
+  // redoes P, and moves the already computed next-tile scores to the new reference.
+  auto slow_path = [&](f32x16 (&s)[2], f32x16 (&sn)[2], u32x4 (&pk)[4], float& rs) {
+    float mx = s[0][0];
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    {  // partner lane l ^ 32 holds the other keys of the same query (VALU lane swap, no LDS)
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1]));
-    }
-    if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.0f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      m_run = m_new;
-      l_run *= alpha;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1])) + m_ref;  // tile maximum, log2 units
+    const bool has = mx > -INFINITY;
+    float m_new = m_valid ? fmaxf(m_ref, mx) : mx;
+    m_new = has || m_valid ? bf16lo(pack_bf16(m_new, 0.f)) : m_ref;
+    const float alpha = m_valid ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
+    const float delta = m_ref - m_new;
+    l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= alpha;
-    }
-    const float mc = m_run * c;
-    float rs = 0.f;
+    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    float part = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
-        pk[kb][r >> 1] = pack_bf16(p0, p1);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kb][r >> 1]), ones, rs,
-                                             false);
+        const float p0 = __builtin_amdgcn_exp2f(s[kb][r] + delta);
+        const float p1 = __builtin_amdgcn_exp2f(s[kb][r + 1] + delta);
+        const uint32_t w = pack_bf16(p0, p1);
+        pk[2 * kb + (r >> 3)][(r >> 1) & 3] = w;
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, part, false);
       }
-    l_run += rs;
+    rs = part;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[kb][r] += delta;
+    m_ref = m_new;
+    m_valid = m_valid || has;
+    qm = hi ? bf16x8{} : bf16x8{(__bf16)(-m_new), (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
+                                (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
   };
 
-  // ---- preamble: A streams K_0, B streams V_0
-  dma_tile(0);
-  zero_tail(0);
-  __syncthreads();
-  if (grp_b) __syncthreads();  // B starts one phase behind
-  for (int j = 0; j < n_tiles; ++j) {
-    if (j == 0) qk_only(0);
-    else mfma_phase(j);
-    __syncthreads();
-    softmax_phase(j);
-    if (j + 1 < n_tiles) {
-      dma_tile(j + 1);
-      zero_tail(j + 1);
+  // One iteration j >= 1 (buffer parity PAR = j & 1): the 34 MFMAs (PV of tile j-1 with its
+  // weights, then QK^T of tile j+1) are issued one by one, each followed by one quarter-pair of this
+  // tile's softmax (two exponentials, or a pack and a row-sum step), which runs in the MFMA shadow.
+  auto iter = [&](int j, auto par_c, f32x16 (&sc)[2], f32x16 (&sn)[2], u32x4 (&pk_prev)[4],
+                  u32x4 (&pk_cur)[4]) {
+    constexpr int PAR = decltype(par_c)::value;
+    const bool more = j + 1 < n_tiles;
+    if (v_loader) dma_tile(j, true);
+    else if (j + 2 < n_tiles) dma_tile(j + 2, false);
+    mask_tile(j, sc);
+    float e[32];
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sn[kb] = f32x16{};
+    // A operand of slot i (slots 32 and 33 use the constant one_op)
+    auto opnd = [&](int i) -> bf16x8 {
+      if (i < 16) return rd_v(PAR ^ 1, i >> 2, i & 3);
+      return rd_k(PAR ^ 1, (i - 16) >> 1, (i - 16) & 1);
+    };
+    constexpr int kAhead = 2;
+    bf16x8 ring[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) ring[i] = opnd(i);
+#pragma unroll
+    for (int i = 0; i < 34; ++i) {
+      // matrix work
+      if (i < 32) {
+        const bf16x8 a = ring[i % kAhead];
+        if (i + kAhead < 32) ring[i % kAhead] = opnd(i + kAhead);
+        if (i < 16) {
+          const int st = i >> 2, db = i & 3;
+          o[db] = mfma32(a, __builtin_bit_cast(bf16x8, pk_prev[st]), o[db]);
+        } else {
+          const int st = (i - 16) >> 1, kb = (i - 16) & 1;
+          sn[kb] = mfma32(a, qf[st], sn[kb]);
+        }
+      } else {
+        const int kb = i - 32;
+        sn[kb] = mfma32(one_op, qm, sn[kb]);
+      }
+      // vector work on this tile's scores
+      if (i < 32) {
+        const int k = i >> 1;                // pair of scores
+        const int kb = k >> 3, r = 2 * (k & 7);
+        if ((i & 1) == 0) {
+          e[2 * k] = __builtin_amdgcn_exp2f(sc[kb][r]);
+          e[2 * k + 1] = __builtin_amdgcn_exp2f(sc[kb][r + 1]);
+        } else {
+          const uint32_t w = pack_bf16(e[2 * k], e[2 * k + 1]);
+          pk_cur[k >> 2][k & 3] = w;
+          part[k & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
+                                                        part[k & 3], false);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    float rs = (part[0] + part[1]) + (part[2] + part[3]);
+    if (__builtin_amdgcn_ballot_w64(!m_valid || !(rs <= 0x1p64f))) slow_path(sc, sn, pk_cur, rs);
+    l_run += rs;
+    (void)more;
+    vm_wait();
+    __syncthreads();
+  };
+
+  // ---- preamble: K_0 and K_1 in LDS, S_0 computed
+  if (!v_loader) {
+    dma_tile(0, false);
+    if (n_tiles > 1) dma_tile(1, false);
+  }
+  vm_wait();
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  u32x4 pA[4], pB[4];
+  qk_all(0, sA);
+  __syncthreads();  // K_0's buffer is refilled during iteration 0
+  // iteration 0: no PV yet; QK^T of tile 1 while this tile's weights are formed
+  {
+    if (v_loader) dma_tile(0, true);
+    else if (2 < n_tiles) dma_tile(2, false);
+    mask_tile(0, sA);
+    qk_all(1, sB);  // stale keys if n_tiles == 1: discarded
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int kb = k >> 3, r = 2 * (k & 7);
+      const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(sA[kb][r]), __builtin_amdgcn_exp2f(sA[kb][r + 1]));
+      pB[k >> 2][k & 3] = w;
+      part[k & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, part[k & 3],
+                                                    false);
+    }
+    float rs = (part[0] + part[1]) + (part[2] + part[3]);
+    if (__builtin_amdgcn_ballot_w64(!m_valid || !(rs <= 0x1p64f))) slow_path(sA, sB, pB, rs);
+    l_run += rs;
+    vm_wait();
     __syncthreads();
   }
-  final_pv(n_tiles - 1);
-  if (!grp_b) __syncthreads();  // matches B's extra barrier
+  // iterations 1.. : S and weights alternate between the A/B register sets
+  int j = 1;
+  for (; j + 1 < n_tiles; j += 2) {
+    iter(j, std::integral_constant<int, 1>{}, sB, sA, pB, pA);
+    iter(j + 1, std::integral_constant<int, 0>{}, sA, sB, pA, pB);
+  }
+  if (j < n_tiles) {
+    iter(j, std::integral_constant<int, 1>{}, sB, sA, pB, pA);
+    ++j;
+  }
+  // PV of the last tile (its weights are in the set written last)
+  {
+    u32x4 (&pl)[4] = ((n_tiles & 1) ? pB : pA);
+    const int par = (n_tiles - 1) & 1;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = mfma32(rd_v(par, st, db), __builtin_bit_cast(bf16x8, pl[st]), o[db]);
+  }
 
   // ---- epilogue: normalise, gate, round, store (one query per lane, 4 dims per store)
   if (my_q < T) {

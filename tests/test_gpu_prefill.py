@@ -78,18 +78,21 @@ def _bf16(x):
 
 
 def _rounded_operand_reference(x, W, gated, qw, kw, base=1e4):
-    """Test-side model of the kernel's rounding points built on the oracle's prologue: q_hat, k_hat
-    and the softmax weights rounded to bf16 (the matrix-core operands), everything else fp64."""
+    """Test-side model of the kernel's rounding points built on the oracle's prologue: the matrix
+    cores see bf16(q_hat * scale * log2 e) and bf16(k_hat), scores are in log2 units, the softmax
+    weights are rounded to bf16 and both the weighted sum and the normaliser use the rounded
+    weights; everything else is fp64."""
     q, k, v = f64(x["q"])[0], f64(x["k"])[0], f64(x["v"])[0]
     T = q.shape[0]
-    qh = _bf16(oracle.qk_prologue(q, np.arange(T), qw, rot_dim=42, rope_base=base, eps=1e-6))
+    c = np.log2(np.e) / np.sqrt(128)
+    qh = _bf16(c * oracle.qk_prologue(q, np.arange(T), qw, rot_dim=42, rope_base=base, eps=1e-6))
     kh = _bf16(oracle.qk_prologue(k, np.arange(T), kw, rot_dim=42, rope_base=base, eps=1e-6))
     out = np.zeros(q.shape)
     for t in range(T):
         lo = max(0, t - W + 1) if W > 0 else 0
-        s = np.einsum("hd,jhd->hj", qh[t], np.repeat(kh[lo:t + 1], 4, axis=1)) / np.sqrt(128)
-        p = np.exp(s - s.max(-1, keepdims=True))
-        o = np.einsum("hj,jhd->hd", _bf16(p), np.repeat(v[lo:t + 1], 4, axis=1)) / p.sum(-1)[:, None]
+        s2 = np.einsum("hd,jhd->hj", qh[t], np.repeat(kh[lo:t + 1], 4, axis=1))
+        p = _bf16(np.exp2(s2 - s2.max(-1, keepdims=True)))
+        o = np.einsum("hj,jhd->hd", p, np.repeat(v[lo:t + 1], 4, axis=1)) / p.sum(-1)[:, None]
         if gated:
             o = o / (1 + np.exp(-f64(x["gate"])[0, t]))
         out[t] = o
@@ -106,8 +109,8 @@ def test_prefill_peaky_logits(W):
     tighter check is against the rounding model. The model still differs from the kernel in two
     ways that also scale with the logit std: the kernel's fp32 prologue can round an element of
     q_hat/k_hat to the neighbouring bf16 value of the fp64 one, and the kernel rounds softmax
-    weights taken relative to the running maximum rather than the final one; hence max-abs 4e-2
-    there with the standard mean-abs bar."""
+    weights taken relative to a running reference rather than the final maximum; hence max-abs
+    4e-2 there with the standard mean-abs bar."""
     gated = W > 0
     out, ref = _run(1, 400, 32, 8, W, gated, 1e4, 12 + W, norm_w=True, q_scale=8.0)
     assert_parity(out, ref, f"peaky logits W={W} vs fp64 oracle", max_abs=0.16, mean_abs=6e-3)
