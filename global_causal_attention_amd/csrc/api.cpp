@@ -137,10 +137,10 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
         (cfg->gated && !aligned16(gate)) || (q_norm_w && !aligned16(q_norm_w)) ||
         (k_norm_w && !aligned16(k_norm_w)))
       return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
-    // K/V tiles are fetched through 32-bit buffer offsets within one sequence's rows
-    const int64_t max_row_bytes = 2 * std::max<int64_t>(s.v, Hkv * kD);
+    // q, K and V rows are fetched through 32-bit buffer offsets within one sequence's rows
+    const int64_t max_row_bytes = 2 * std::max<int64_t>({s.q, s.v, Hkv * kD});
     if ((int64_t)(T + 64) * max_row_bytes >= (int64_t(1) << 32))
-      return fail(ZG_ERR_UNSUPPORTED, "T * token stride of v (bytes) must stay below 4 GiB");
+      return fail(ZG_ERR_UNSUPPORTED, "T * token stride of q or v (bytes) must stay below 4 GiB");
     const size_t need = zg_attn_prefill_workspace_bytes(cfg, B, T);
     if (need > 0 && (!workspace || workspace_bytes < need))
       return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
@@ -188,6 +188,16 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     pp.rope = rt;
     if ((int64_t)pp.n_qtiles * B * Hkv >= (int64_t(1) << 31))
       return fail(ZG_ERR_SHAPE, "grid too large");
+    if (zg::prefill_uses_swa(pp.window, G)) {
+      // split each sequence into runs of 64-query steps so that the grid roughly fills the device
+      int dev = 0, cus = 256;
+      if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      const int64_t steps = (T + 63) / 64;
+      const int64_t per_bh = (int64_t)B * Hkv;
+      const int64_t n_seg = std::max<int64_t>(1, std::min<int64_t>(steps, cus / per_bh));
+      pp.seg_steps = (int32_t)((steps + n_seg - 1) / n_seg);
+    }
     return hip_status(zg::launch_prefill(pp, G, cfg->gated != 0, hs), "prefill launch");
   } catch (...) {
     return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_prefill");

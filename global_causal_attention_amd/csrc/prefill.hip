@@ -19,6 +19,7 @@
 // {4-7, 12-15}, so V is stored transposed in LDS with bits 2 and 3 of the key index swapped, which
 // makes each lane's 8 A-operand values one contiguous 16-byte LDS read. O^T keeps one query per lane,
 // so the online-softmax rescale is a per-lane scalar.
+#include <cstddef>
 #include <type_traits>
 
 #include "zg_common.hpp"
@@ -439,6 +440,297 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Streaming kernel for banded layers with window <= 128 and four query heads per KV head.
+//
+// A workgroup walks a run of 64-query steps of one (sequence b, KV head); wave w owns query head
+// w % 4 and 32 queries (block w / 4) of each step. A step needs its own 64 keys and the 128 before
+// them, i.e. three 64-key tiles, so K and V tiles sit in a three-slot LDS ring and each step brings
+// in exactly one new tile, issued at the top of the step into the slot the previous step finished
+// with; its key blocks are visited last, behind the q prologue and the blocks of the two older
+// tiles. Each wave's raw q rows for the next step stream into its own 8 KB LDS area as soon as the
+// prologue has turned this step's rows into MFMA operands; the gate rows come into registers during
+// the step. Every load goes through buffer_load ... lds or plain vector loads whose completion is
+// tracked with explicit vmcnt waits, so no wait ever covers a load issued for a later phase.
+//
+// Tile layout in LDS (K and V alike): 64 rows in 16 groups of 4 rows; group g occupies 1 KB as
+// [16-byte chunk][row of the group], with chunk c stored at position c ^ (g & 3). Each
+// buffer_load ... lds fills one group (4 whole rows, so global reads stay row-contiguous), the
+// 16-row QK^T operand reads and the 4-row transposing PV reads both hit 64 distinct banks, and every
+// operand address is a per-lane base plus an immediate.
+constexpr int kSwaTile = 16 * 1024;
+constexpr int kSwaSlot = 2 * kSwaTile;      // K tile, then V tile
+constexpr int kSwaRing = 3 * kSwaSlot;
+constexpr int kSwaQArea = 32 * 256;         // per wave: 32 q rows
+constexpr int kSwaLds = kSwaRing + kWaves * kSwaQArea;
+static_assert(kSwaLds <= 160 * 1024, "LDS budget");
+
+template <bool GATED>
+__global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int per_seg = p.B * p.Hkv;
+  const int seg = blockIdx.x / per_seg;
+  const int bh = blockIdx.x - seg * per_seg;
+  const int b = bh / p.Hkv;
+  const int kvh = bh - b * p.Hkv;
+  const int T = p.T;
+  const int W = p.window;
+  const int hg = wave & 3;
+  const int qb = wave >> 2;
+  const int head = kvh * 4 + hg;
+  const int t_seg0 = seg * p.seg_steps;   // first 64-query step (= tile index) of the run
+  const int n_steps = min(p.seg_steps, (T + 63) / 64 - t_seg0);
+
+  // ---- K/V tiles: waves 0-3 bring K row groups 4 wg .. 4 wg + 3, waves 4-7 the V ones
+  const bool v_loader = wave >= 4;
+  const int wg = wave & 3;
+  const int row_bytes = (int)((v_loader ? p.sv : (int64_t)p.Hkv * kHeadDim) * 2);
+  const uint16_t* slab = v_loader ? p.v + (int64_t)b * T * p.sv + (int64_t)kvh * kHeadDim
+                                  : p.khat + ((int64_t)b * T * p.Hkv + kvh) * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, T * row_bytes, 0x00020000);
+  const uint32_t lds_kv = (uint32_t)(uintptr_t)smem + (v_loader ? kSwaTile : 0);
+  auto dma_tile = [&](int t) {  // tile t (rows 64t .. 64t + 63) into ring slot t % 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * wg + i;  // g & 3 == i
+      const uint32_t m0v = lds_kv + (t % 3) * kSwaSlot + g * 1024;
+      const uint32_t soff = (uint32_t)(64 * t + 4 * g) * (uint32_t)row_bytes;
+      const uint32_t voff = (uint32_t)((lane & 3) * row_bytes + 16 * ((lane >> 2) ^ i));
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   ::"s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+    }
+  };
+
+  // ---- raw q rows of this wave: row r at r * 256, chunk c at position c ^ (r & 7)
+  const int q_row_bytes = (int)(p.sq * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_q = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.q + (int64_t)b * T * p.sq + (int64_t)head * kHeadDim), 0, T * q_row_bytes,
+      0x00020000);
+  unsigned char* qs = smem + kSwaRing + wave * kSwaQArea;
+  const uint32_t lds_q = (uint32_t)(uintptr_t)qs;
+  auto dma_q = [&](int step) {  // 32 rows, 4 per instruction
+    const int row0 = 64 * (t_seg0 + step) + 32 * qb;
+    // the area's previous contents (this step's operands) must have been read out first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const uint32_t m0v = lds_q + i * 1024;
+      const uint32_t soff = (uint32_t)(row0 + 4 * i) * (uint32_t)q_row_bytes;
+      const uint32_t voff = (uint32_t)((lane >> 4) * q_row_bytes + 16 * ((lane & 15) ^ (r & 7)));
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   ::"s"(m0v), "v"(voff), "s"(rsrc_q), "s"(soff) : "memory", "m0");
+    }
+  };
+
+  // ---- per-lane operand offsets
+  // QK^T A operand (key row l32 of a 32-key block, chunk 2 st + hi): even and odd st differ in
+  // how the group swizzle moves the chunk
+  const int kx = (l32 >> 2) & 3;
+  const int k_lane = (l32 >> 2) * 1024 + (l32 & 3) * 16 + 64 * (hi ^ (kx & 1));
+  const int k_even = k_lane + 128 * (kx >> 1);
+  const int k_odd = k_lane - 128 * (kx >> 1);
+  // PV A operand: transposing read x of key step st covers row group 4 st + 2 x + hi
+  int v_lane[2];
+  {
+    const int u = (lane & 15) >> 2;
+    const int dch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int gx = 2 * x + hi;
+      v_lane[x] = kSwaTile + gx * 1024 + (dch ^ gx) * 64 + u * 16 + 8 * (lane & 1);
+    }
+  }
+  const bf16x8 one_op = hi ? bf16x8{} : bf16x8{(__bf16)1.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
+                                               (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  u32x2 graw[16];  // the lane's 64 gate values in output order
+  auto load_gate = [&](int step) {
+    const int t = 64 * (t_seg0 + step) + 32 * qb + l32;
+    const uint16_t* g = p.gate + ((int64_t)b * T + min(t, T - 1)) * p.sg + (int64_t)head * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        graw[4 * db + rq] = *reinterpret_cast<const u32x2*>(g + 32 * db + 8 * rq + 4 * hi);
+  };
+
+  // ---- start of the run: the tiles before the first step and the first q rows
+  {
+    const int t_first = max(0, (64 * t_seg0 - W + 1) >> 6);
+    for (int t = t_first; t < t_seg0; ++t) dma_tile(t);
+    dma_q(0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+
+  for (int step = 0; step < n_steps; ++step) {
+    const int tc = t_seg0 + step;           // this step's tile
+    const int qbase = 64 * tc + 32 * qb;
+    const int my_q = qbase + l32;
+    const bool has_next = step + 1 < n_steps;
+    dma_tile(tc);
+
+    // -- q prologue (raw rows landed before the previous epilogue): RMSNorm + RoPE, times
+    // scale * log2(e), bf16, restaged as [chunk][row] and read back as MFMA B operands
+    bf16x8 qf[8];
+    {
+      const int r = lane >> 1;
+      const int half = lane & 1;
+      float x[64];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        unpack8(*reinterpret_cast<const u32x4*>(qs + r * 256 + 128 * half + 16 * (i ^ (r & 7))),
+                x + 8 * i);
+      // the rotary table is re-read from the kernel arguments each step rather than kept in
+      // scalar registers across the loop
+      typedef __attribute__((address_space(4))) const unsigned char* karg_ptr;
+      karg_ptr ka = (karg_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(ka));
+      const RopeTable& rt = *(const RopeTable*)(ka + offsetof(PrefillParams, rope));
+      norm_rope_row_scalar_w(x, half, (const_f32_ptr)p.q_norm_w, p.eps, p.scale_log2,
+                             p.pos0 + qbase + r, rt, reinterpret_cast<float*>(qs), r, 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(qs + (8 * half + i) * 512 + (r ^ (8 * half)) * 16) = pack8(x + 8 * i);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qf[s] = *reinterpret_cast<const bf16x8*>(qs + (2 * s + hi) * 512 + (l32 ^ (8 * (s >> 2))) * 16);
+    }
+    if (has_next) dma_q(step + 1);
+    if (GATED) load_gate(step);
+
+    // -- attention over the 32-key blocks [kb_lo, kb_hi]; blocks of tile tc come last
+    f32x16 o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+    float l_run = 0.f;
+    float m_ref = 0.f;
+    bool m_valid = false;
+    bf16x8 qm = bf16x8{};
+    auto block = [&](int kb) {
+      const int slot = ((kb >> 1) % 3) * kSwaSlot + (kb & 1) * 8192;
+      const unsigned char* kp = smem + slot;
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+        s = mfma32(*reinterpret_cast<const bf16x8*>(kp + ((st & 1) ? k_odd : k_even) + 128 * st), qf[st], s);
+      s = mfma32(one_op, qm, s);
+      const int k0 = 32 * kb;
+      if (k0 + 31 > qbase || k0 < qbase + 32 - W) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool ok = (key <= my_q) && (key > my_q - W);
+          s[r] = ok ? s[r] : -INFINITY;
+        }
+      }
+      u32x4 pk[2];
+      float part[2] = {0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(s[2 * k]), __builtin_amdgcn_exp2f(s[2 * k + 1]));
+        pk[k >> 2][k & 3] = w;
+        part[k & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, part[k & 1], false);
+      }
+      float rs = part[0] + part[1];
+      // lazy reference: rescale only when a partial sum leaves [0, 2^64] or no key was seen yet
+      if (__builtin_amdgcn_ballot_w64(!m_valid || !(rs <= 0x1p64f))) {
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1])) + m_ref;
+        const bool has = mx > -INFINITY;
+        float m_new = m_valid ? fmaxf(m_ref, mx) : mx;
+        m_new = has || m_valid ? bf16lo(pack_bf16(m_new, 0.f)) : m_ref;
+        const float alpha = m_valid ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
+        const float delta = m_ref - m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] *= alpha;
+        float pt = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(s[2 * k] + delta),
+                                       __builtin_amdgcn_exp2f(s[2 * k + 1] + delta));
+          pk[k >> 2][k & 3] = w;
+          pt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, pt, false);
+        }
+        rs = pt;
+        m_ref = m_new;
+        m_valid = m_valid || has;
+        qm = hi ? bf16x8{} : bf16x8{(__bf16)(-m_new), (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
+                                    (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+      }
+      l_run += rs;
+      const unsigned char* vp = smem + slot;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const i16x4 lo4 = lds_read_tr(vp + v_lane[0] + 4096 * st + 256 * db);
+          const i16x4 hi4 = lds_read_tr(vp + v_lane[1] + 4096 * st + 256 * db);
+          const i16x4 both[2] = {lo4, hi4};
+          o[db] = mfma32(__builtin_bit_cast(bf16x8, both), __builtin_bit_cast(bf16x8, pk[st]), o[db]);
+        }
+    };
+    const int kb_lo = max(0, (qbase - W + 1) >> 5);
+    const int kb_hi = qbase >> 5;
+    const int kb_new = 2 * tc;              // first block of tile tc
+    for (int kb = kb_lo; kb < min(kb_hi + 1, kb_new); ++kb) block(kb);
+    // tile tc has landed once every wave's share of it has; only the loads issued after it (next
+    // q rows: 8 instructions, gate: 16) may still be in flight
+    if (GATED) {
+      if (has_next) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    } else {
+      if (has_next) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    for (int kb = max(kb_lo, kb_new); kb <= kb_hi; ++kb) block(kb);
+
+    // -- epilogue: every load of this step (gate, next q rows) has landed past this wait, which is
+    // issued through the builtin so that the compiler's own wait tracking knows it too (the gate
+    // registers are then free for the next prologue without further waits)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt: no wait
+    {
+      const float l_tot = l_run + shfl_xor_f(l_run, 32);
+      const float inv = 1.0f / l_tot;
+      const bool store = my_q < T;
+      uint16_t* dst = p.out + ((int64_t)b * T + min(my_q, T - 1)) * p.so + (int64_t)head * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = 32 * db + 8 * rq + 4 * hi;
+          float y[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = o[db][4 * rq + j] * inv;
+          if (GATED) {
+            const u32x2 g = graw[4 * db + rq];
+            const float gv[4] = {bf16lo(g[0]), bf16hi(g[0]), bf16lo(g[1]), bf16hi(g[1])};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              y[j] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[j] * 1.4426950408889634f));
+          }
+          const u32x2 w = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+          if (store) *reinterpret_cast<u32x2*>(dst + d0) = w;
+        }
+    }
+    // every wave is done with the oldest tile's slot, which the next step refills
+    asm volatile("s_barrier" ::: "memory");
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 hipError_t launch_kprep(const KPrepParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.T * p.Hkv;
   const int64_t blocks = (rows + 127) / 128;
@@ -459,7 +751,23 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool GATED>
+static hipError_t launch_swa_t(const PrefillParams& p, hipStream_t s) {
+  auto kern = prefill_swa_kernel<GATED>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSwaLds);
+  if (e != hipSuccess) return e;
+  const int64_t n_seg = ((int64_t)p.T + 64 * p.seg_steps - 1) / (64 * p.seg_steps);
+  const int64_t grid = n_seg * p.B * p.Hkv;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), kSwaLds, s, p);
+  return hipGetLastError();
+}
+
+bool prefill_uses_swa(int window, int group) { return window > 0 && window <= 128 && group == 4; }
+
 hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s) {
+  if (prefill_uses_swa(p.window, group))
+    return gated ? launch_swa_t<true>(p, s) : launch_swa_t<false>(p, s);
   switch (group * 2 + (gated ? 1 : 0)) {
     case 2: return launch_prefill_t<1, false>(p, s);
     case 3: return launch_prefill_t<1, true>(p, s);

@@ -110,4 +110,51 @@ __device__ __forceinline__ void norm_rope_row(float* x, int half, const float* _
   }
 }
 
+// Variant of norm_rope_row for kernels that keep loads in flight across the prologue: the weights
+// are read through scalar loads of both halves (the lane picks its half), so the prologue issues no
+// vector-memory instruction that would wait behind those loads. `scale` multiplies the result.
+typedef __attribute__((address_space(4))) const float* const_f32_ptr;
+__device__ __forceinline__ void norm_rope_row_scalar_w(float* x, int half, const_f32_ptr w,
+                                                       float eps, float scale, int64_t pos,
+                                                       const RopeTable& rt, float* stage, int row,
+                                                       int stride) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
+  ss += shfl_xor_f(ss, 1);
+  const float inv = rsqrtf(ss * (1.0f / kHeadDim) + eps) * scale;
+  if (w) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      float wl = w[i], wh = w[64 + i];
+      asm("" : "+s"(wl), "+s"(wh));  // keep both as scalar loads; the lane selects its half
+      x[i] *= inv * (half ? wh : wl);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] *= inv;
+  }
+  const int h = rt.half;
+  if (half == 0 && h > 0) {
+    float* st = stage + row;
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if (i < 2 * h) st[i * stride] = x[i];
+#pragma unroll
+    for (int i = 0; i < kMaxRotHalf; ++i) {
+      if (i < h) {
+        float c, s;
+        rope_cs(pos, rt.rev[i], c, s);
+        const float a = st[i * stride];
+        const float b = st[(i + h) * stride];
+        st[i * stride] = a * c - b * s;
+        st[(i + h) * stride] = b * c + a * s;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if (i < 2 * h) x[i] = st[i * stride];
+  }
+}
+
 }  // namespace zg

@@ -38,6 +38,7 @@ struct PrefillParams {
   int64_t pos0;
   int32_t window;
   int32_t n_qtiles;
+  int32_t seg_steps;  // banded kernel: 64-query steps per workgroup
   float eps;
   float scale_log2;  // softmax scale * log2(e)
   RopeTableH rope;
@@ -87,6 +88,8 @@ struct GemmParams {
 };
 
 hipError_t launch_kprep(const KPrepParams& p, hipStream_t s);
+// True when launch_prefill takes the streaming kernel for short windows (which reads seg_steps).
+bool prefill_uses_swa(int window, int group);
 hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s);

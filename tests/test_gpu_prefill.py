@@ -61,10 +61,37 @@ def test_local_layer_T1024_full():
     (2, 100, 8, 1, 0, False, 1e4, 0),
     (1, 300, 32, 8, 128, True, 1e7, 200000),
     (1, 70, 32, 8, 0, False, 1e7, 262000),
+    # four heads per KV head and window <= 128: runs of several 64-query steps per workgroup,
+    # run boundaries and ragged tails
+    (16, 520, 32, 8, 128, True, 1e4, 0),
+    (1, 4100, 32, 8, 128, True, 1e6, 0),
+    (1, 1000, 32, 8, 100, False, 1e4, 0),
+    (2, 700, 32, 8, 33, True, 1e4, 0),
+    (1, 640, 32, 8, 64, True, 1e4, 5),
+    (1, 333, 32, 8, 1, True, 1e4, 0),
 ])
 def test_prefill_edges(B, T, Hq, Hkv, W, gated, base, pos0):
     out, ref = _run(B, T, Hq, Hkv, W, gated, base, 7 + T + W, pos0=pos0)
     assert_parity(out, ref, f"B={B} T={T} Hq={Hq}/{Hkv} W={W}")
+
+
+@pytest.mark.parametrize("W", [128, 0])
+def test_prefill_token_strided_views(W):
+    # q, k, v and gate as column slices of one fused [B, T, (2 Hq + 2 Hkv) * 128] projection buffer,
+    # out written into a wider buffer
+    B, T, Hq, Hkv = 2, 333, 32, 8
+    print(f"[case] strided views B={B} T={T} W={W}", flush=True)
+    x = si.prefill_layer(si.generator(31 + W), B, T, Hq, Hkv, 128, gated=True)
+    fused = torch.cat([x["q"], x["k"], x["v"], x["gate"]], dim=2).to(DEV)
+    q, k, v, g = torch.split(fused, [Hq, Hkv, Hkv, Hq], dim=2)
+    wide = torch.zeros(B, T, Hq + 3, 128, dtype=torch.bfloat16, device=DEV)
+    cfg = zg.AttnConfig(window=W, gated=W > 0, rope_base=1e4)
+    zg.zg_attn_prefill(cfg, q, k, v, g if W > 0 else None, out=wide[:, :, :Hq])
+    torch.cuda.synchronize()
+    ref = oracle.prefill(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["gate"]), window=W,
+                         gated=W > 0, rope_base=1e4)
+    assert_parity(wide[:, :, :Hq], ref, f"strided views W={W}")
+    assert torch.count_nonzero(wide[:, :, Hq:]).item() == 0, "write outside the out view"
 
 
 def test_prefill_norm_weights_scale_and_rot_dims():
