@@ -160,10 +160,15 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     kp.pos0 = pos0;
     kp.eps = cfg->rms_eps;
     kp.rope = rt;
+    const int G = (int)(Hq / Hkv);
+    const int window = cfg->window >= T ? 0 : cfg->window;  // a window covering T is causal
+    const bool swa = zg::prefill_uses_swa(window, G, rt.half);
+    kp.fold = swa ? 1 : 0;
+    kp.fold_scale = scale_log2(cfg);
+    kp.fold_w = q_norm_w;
     st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
     if (st != ZG_OK) return st;
 
-    const int G = (int)(Hq / Hkv);
     const int mq = 256 / G;
     zg::PrefillParams pp{};
     pp.q = static_cast<const uint16_t*>(q);
@@ -181,14 +186,14 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     pp.Hq = (int32_t)Hq;
     pp.Hkv = (int32_t)Hkv;
     pp.pos0 = pos0;
-    pp.window = cfg->window >= T ? 0 : cfg->window;  // a window covering the sequence is causal
+    pp.window = window;
     pp.n_qtiles = (T + mq - 1) / mq;
     pp.eps = cfg->rms_eps;
     pp.scale_log2 = scale_log2(cfg);
     pp.rope = rt;
     if ((int64_t)pp.n_qtiles * B * Hkv >= (int64_t(1) << 31))
       return fail(ZG_ERR_SHAPE, "grid too large");
-    if (zg::prefill_uses_swa(pp.window, G)) {
+    if (swa) {
       // split each sequence into runs of 64-query steps so that the grid roughly fills the device
       int dev = 0, cus = 256;
       if (hipGetDevice(&dev) == hipSuccess)

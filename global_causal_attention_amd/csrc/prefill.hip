@@ -78,6 +78,14 @@ __global__ __launch_bounds__(256) void kprep_kernel(KPrepParams p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) unpack8(s4[i], x + 8 * i);
   norm_rope_row(x, half, p.k_norm_w, p.eps, p.pos0 + t, p.rope, stage, lane_pair, 128);
+  if (p.fold) {
+    const int rot = 2 * p.rope.half;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int d = 64 * half + i;
+      x[i] *= (d >= rot && p.fold_w) ? p.fold_scale * p.fold_w[d] : p.fold_scale;
+    }
+  }
   u32x4* d4 = reinterpret_cast<u32x4*>(p.khat + row * kHeadDim + 64 * half);
 #pragma unroll
   for (int i = 0; i < 8; ++i) d4[i] = pack8(x + 8 * i);
@@ -440,7 +448,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Streaming kernel for banded layers with window <= 128 and four query heads per KV head.
+// Streaming kernel for banded layers with window <= 128, four query heads per KV head and a
+// rotary dimension of 42 (21 pairs).
 //
 // A workgroup walks a run of 64-query steps of one (sequence b, KV head); wave w owns query head
 // w % 4 and 32 queries (block w / 4) of each step. A step needs its own 64 keys and the 128 before
@@ -449,14 +458,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 // with; its key blocks are visited last, behind the q prologue and the blocks of the two older
 // tiles. Each wave's raw q rows for the next step stream into its own 8 KB LDS area as soon as the
 // prologue has turned this step's rows into MFMA operands; the gate rows come into registers during
-// the step. Every load goes through buffer_load ... lds or plain vector loads whose completion is
-// tracked with explicit vmcnt waits, so no wait ever covers a load issued for a later phase.
+// the step. Loads are tracked with explicit vmcnt waits, so no wait covers a load issued for a
+// later phase.
+//
+// Arithmetic layout. The score of query i and key j in log2 units is
+//   inv_i * (q'_i . k''_j),  inv_i = 1 / sqrt(mean(q_i^2) + eps),
+// where q'_i is the raw q row with its first 42 dims replaced by RoPE(w_q * q_i) (rounded to bf16)
+// and k''_j is the prepared key with the softmax scale * log2(e), and for dims >= 42 the q norm
+// weight, folded in (the keys are prepared with KPrepParams::fold). The RMS factor is applied to
+// the scores instead of the q rows, so 86 of the 128 q dims reach the matrix cores as loaded.
 //
 // Tile layout in LDS (K and V alike): 64 rows in 16 groups of 4 rows; group g occupies 1 KB as
 // [16-byte chunk][row of the group], with chunk c stored at position c ^ (g & 3). Each
 // buffer_load ... lds fills one group (4 whole rows, so global reads stay row-contiguous), the
 // 16-row QK^T operand reads and the 4-row transposing PV reads both hit 64 distinct banks, and every
 // operand address is a per-lane base plus an immediate.
+constexpr int kSwaRotHalf = 21;
 constexpr int kSwaTile = 16 * 1024;
 constexpr int kSwaSlot = 2 * kSwaTile;      // K tile, then V tile
 constexpr int kSwaRing = 3 * kSwaSlot;
@@ -464,8 +481,14 @@ constexpr int kSwaQArea = 32 * 256;         // per wave: 32 q rows
 constexpr int kSwaLds = kSwaRing + kWaves * kSwaQArea;
 static_assert(kSwaLds <= 160 * 1024, "LDS budget");
 
+__device__ __forceinline__ float dpp_swap_pair(float v) {  // value of lane ^ 1
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF,
+                                                             0xF, false));
+}
+
 template <bool GATED>
 __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) {
+  constexpr int HR = kSwaRotHalf;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -507,7 +530,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
     }
   };
 
-  // ---- raw q rows of this wave: row r at r * 256, chunk c at position c ^ (r & 7)
+  // ---- raw q rows of this wave: row r at r * 256, chunk c at position c ^ (r & 15)
   const int q_row_bytes = (int)(p.sq * 2);
   const __amdgpu_buffer_rsrc_t rsrc_q = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.q + (int64_t)b * T * p.sq + (int64_t)head * kHeadDim), 0, T * q_row_bytes,
@@ -523,11 +546,14 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
       const int r = 4 * i + (lane >> 4);
       const uint32_t m0v = lds_q + i * 1024;
       const uint32_t soff = (uint32_t)(row0 + 4 * i) * (uint32_t)q_row_bytes;
-      const uint32_t voff = (uint32_t)((lane >> 4) * q_row_bytes + 16 * ((lane & 15) ^ (r & 7)));
+      const uint32_t voff = (uint32_t)((lane >> 4) * q_row_bytes + 16 * ((lane & 15) ^ (r & 15)));
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                    ::"s"(m0v), "v"(voff), "s"(rsrc_q), "s"(soff) : "memory", "m0");
     }
   };
+  // B-operand read of step st: chunk 2 st + hi of row l32, i.e. q_op0 + 32 (st ^ q_opx)
+  const int q_op0 = l32 * 256 + 16 * (hi ^ (l32 & 1));
+  const int q_opx = (l32 >> 1) & 7;
 
   // ---- per-lane operand offsets
   // QK^T A operand (key row l32 of a 32-key block, chunk 2 st + hi): even and odd st differ in
@@ -550,6 +576,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
   const bf16x8 one_op = hi ? bf16x8{} : bf16x8{(__bf16)1.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
                                                (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int key_lane = 4 * hi;  // key offset of this lane's score registers within a block
 
   u32x2 graw[16];  // the lane's 64 gate values in output order
   auto load_gate = [&](int step) {
@@ -577,98 +604,183 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
     const bool has_next = step + 1 < n_steps;
     dma_tile(tc);
 
-    // -- q prologue (raw rows landed before the previous epilogue): RMSNorm + RoPE, times
-    // scale * log2(e), bf16, restaged as [chunk][row] and read back as MFMA B operands
-    bf16x8 qf[8];
+    // -- q prologue (raw rows landed before the previous epilogue). Lane pair (r, half) holds dims
+    // 64 half .. 64 half + 63 of row r: sum of squares for the RMS factor, and on half 0 the
+    // rotation of dims 0..41 (weighted), written back in place as bf16.
+    float inv_q;
     {
       const int r = lane >> 1;
       const int half = lane & 1;
-      float x[64];
+      u32x4 raw[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        unpack8(*reinterpret_cast<const u32x4*>(qs + r * 256 + 128 * half + 16 * (i ^ (r & 7))),
-                x + 8 * i);
-      // the rotary table is re-read from the kernel arguments each step rather than kept in
-      // scalar registers across the loop
+        raw[i] = *reinterpret_cast<const u32x4*>(qs + r * 256 + 16 * ((8 * half + i) ^ (r & 15)));
+      float ss0 = 0.f, ss1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          // (the words go through scalars: a bit_cast of a vector element reads element 0 with
+          // this compiler)
+          const uint32_t w0 = raw[i][j], w1 = raw[i][j + 1];
+          const bf16x2 a0 = __builtin_bit_cast(bf16x2, w0), a1 = __builtin_bit_cast(bf16x2, w1);
+          ss0 = __builtin_amdgcn_fdot2_f32_bf16(a0, a0, ss0, false);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(a1, a1, ss1, false);
+        }
+      float ss = ss0 + ss1;
+      ss += dpp_swap_pair(ss);
+      const float inv_row = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
+      // rotary angles: half 0 computes pairs 0..10, half 1 pairs 11..20; half 0 takes the second
+      // set from its partner lane
       typedef __attribute__((address_space(4))) const unsigned char* karg_ptr;
       karg_ptr ka = (karg_ptr)__builtin_amdgcn_kernarg_segment_ptr();
       asm volatile("" : "+s"(ka));
       const RopeTable& rt = *(const RopeTable*)(ka + offsetof(PrefillParams, rope));
-      norm_rope_row_scalar_w(x, half, (const_f32_ptr)p.q_norm_w, p.eps, p.scale_log2,
-                             p.pos0 + qbase + r, rt, reinterpret_cast<float*>(qs), r, 32);
+      const int64_t pos = p.pos0 + qbase + r;
+      float cs[HR], sn[HR];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(qs + (8 * half + i) * 512 + (r ^ (8 * half)) * 16) = pack8(x + 8 * i);
+      for (int j = 0; j < 11; ++j) {
+        double rev0 = rt.rev[j], rev1 = rt.rev[min(j + 11, HR - 1)];
+        asm("" : "+s"(rev0), "+s"(rev1));  // scalar loads; the lane picks its pair
+        const double rev = half ? rev1 : rev0;
+        float c_, s_;
+        rope_cs(pos, rev, c_, s_);
+        if (j < 11) { cs[j] = c_; sn[j] = s_; }
+        if (j + 11 < HR) {
+          cs[j + 11] = dpp_swap_pair(c_);
+          sn[j + 11] = dpp_swap_pair(s_);
+        }
+      }
+      if (half == 0) {
+        const_f32_ptr w = (const_f32_ptr)p.q_norm_w;
+        float x[2 * HR];
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qf[s] = *reinterpret_cast<const bf16x8*>(qs + (2 * s + hi) * 512 + (l32 ^ (8 * (s >> 2))) * 16);
+        for (int d = 0; d < 2 * HR; ++d) {
+          const uint32_t word = raw[d >> 3][(d & 7) >> 1];
+          x[d] = (d & 1) ? bf16hi(word) : bf16lo(word);
+          if (w) {
+            float wd = w[d];
+            asm("" : "+s"(wd));
+            x[d] *= wd;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < HR; ++i) {
+          const float a = x[i], bb = x[i + HR];
+          x[i] = a * cs[i] - bb * sn[i];
+          x[i + HR] = bb * cs[i] + a * sn[i];
+        }
+#pragma unroll
+        for (int d = 0; d < 2 * HR; d += 2) raw[d >> 3][(d & 7) >> 1] = pack_bf16(x[d], x[d + 1]);
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+          *reinterpret_cast<u32x4*>(qs + r * 256 + 16 * (i ^ (r & 15))) = raw[i];
+      }
+      inv_q = __shfl(inv_row, 2 * l32, 64);
     }
+    bf16x8 qf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qs + q_op0 + 32 * (s ^ q_opx));
     if (has_next) dma_q(step + 1);
     if (GATED) load_gate(step);
 
-    // -- attention over the 32-key blocks [kb_lo, kb_hi]; blocks of tile tc come last
+    // -- attention over the 32-key blocks [kb_lo, kb_hi]; the blocks of older tiles newest first,
+    // then those of tile tc. Softmax weights are exp2(inv_q * (s - mu)) with a bf16 reference mu
+    // per query (subtracted by a ninth MFMA step), raised only when a partial sum leaves
+    // [0, 2^64] or no key has been seen yet.
     f32x16 o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = f32x16{};
     float l_run = 0.f;
-    float m_ref = 0.f;
+    float mu = 0.f;
     bool m_valid = false;
     bf16x8 qm = bf16x8{};
-    auto block = [&](int kb) {
+    auto block = [&](int kb, auto first_c) {
+      constexpr bool first = decltype(first_c)::value;
       const int slot = ((kb >> 1) % 3) * kSwaSlot + (kb & 1) * 8192;
       const unsigned char* kp = smem + slot;
       f32x16 s = f32x16{};
 #pragma unroll
       for (int st = 0; st < 8; ++st)
         s = mfma32(*reinterpret_cast<const bf16x8*>(kp + ((st & 1) ? k_odd : k_even) + 128 * st), qf[st], s);
-      s = mfma32(one_op, qm, s);
+      if constexpr (!first) s = mfma32(one_op, qm, s);
+      // masks: key k0 + c_r + 4 hi is valid for query my_q when 0 <= my_q - key < W
       const int k0 = 32 * kb;
-      if (k0 + 31 > qbase || k0 < qbase + 32 - W) {
+      const bool need_causal = k0 + 31 > qbase;
+      const bool need_window = k0 < qbase + 32 - W;
+      if (need_causal || need_window) {
+        const int t = my_q - k0 - key_lane;  // valid: c_r <= t and c_r > t - W
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = (key <= my_q) && (key > my_q - W);
+          const int cr = 8 * (r >> 2) + (r & 3);
+          bool ok = true;
+          if (need_causal) ok = cr <= t;
+          if (need_window) ok = ok && (cr > t - W);
           s[r] = ok ? s[r] : -INFINITY;
         }
       }
       u32x4 pk[2];
-      float part[2] = {0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(s[2 * k]), __builtin_amdgcn_exp2f(s[2 * k + 1]));
-        pk[k >> 2][k & 3] = w;
-        part[k & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, part[k & 1], false);
-      }
-      float rs = part[0] + part[1];
-      // lazy reference: rescale only when a partial sum leaves [0, 2^64] or no key was seen yet
-      if (__builtin_amdgcn_ballot_w64(!m_valid || !(rs <= 0x1p64f))) {
+      float rs;
+      if constexpr (first) {
+        // first block of the step: the reference is this block's maximum (o and l are still 0)
         float mx = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                          false, false);
-        mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1])) + m_ref;
-        const bool has = mx > -INFINITY;
-        float m_new = m_valid ? fmaxf(m_ref, mx) : mx;
-        m_new = has || m_valid ? bf16lo(pack_bf16(m_new, 0.f)) : m_ref;
-        const float alpha = m_valid ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
-        const float delta = m_ref - m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] *= alpha;
+        mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1]));
+        m_valid = mx > -INFINITY;
+        mu = m_valid ? bf16lo(pack_bf16(mx, 0.f)) : 0.f;
         float pt = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(s[2 * k] + delta),
-                                       __builtin_amdgcn_exp2f(s[2 * k + 1] + delta));
+          const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(inv_q * (s[2 * k] - mu)),
+                                       __builtin_amdgcn_exp2f(inv_q * (s[2 * k + 1] - mu)));
           pk[k >> 2][k & 3] = w;
           pt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, pt, false);
         }
         rs = pt;
-        m_ref = m_new;
-        m_valid = m_valid || has;
-        qm = hi ? bf16x8{} : bf16x8{(__bf16)(-m_new), (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
+        qm = hi ? bf16x8{} : bf16x8{(__bf16)(-mu), (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
                                     (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+      } else {
+        float part[2] = {0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(inv_q * s[2 * k]),
+                                       __builtin_amdgcn_exp2f(inv_q * s[2 * k + 1]));
+          pk[k >> 2][k & 3] = w;
+          part[k & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, part[k & 1], false);
+        }
+        rs = part[0] + part[1];
+        if (__builtin_amdgcn_ballot_w64(!m_valid || !(rs <= 0x1p64f))) {
+          float mx = s[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+          mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1])) + mu;
+          const bool has = mx > -INFINITY;
+          float mu_new = m_valid ? fmaxf(mu, mx) : mx;
+          mu_new = has || m_valid ? bf16lo(pack_bf16(mu_new, 0.f)) : mu;
+          const float delta = mu - mu_new;
+          const float alpha = m_valid ? __builtin_amdgcn_exp2f(inv_q * delta) : 0.f;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] *= alpha;
+          float pt = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(inv_q * (s[2 * k] + delta)),
+                                         __builtin_amdgcn_exp2f(inv_q * (s[2 * k + 1] + delta)));
+            pk[k >> 2][k & 3] = w;
+            pt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, pt, false);
+          }
+          rs = pt;
+          mu = mu_new;
+          m_valid = m_valid || has;
+          qm = hi ? bf16x8{} : bf16x8{(__bf16)(-mu), (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
+                                      (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+        }
       }
       l_run += rs;
       const unsigned char* vp = smem + slot;
@@ -685,17 +797,30 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
     const int kb_lo = max(0, (qbase - W + 1) >> 5);
     const int kb_hi = qbase >> 5;
     const int kb_new = 2 * tc;              // first block of tile tc
-    for (int kb = kb_lo; kb < min(kb_hi + 1, kb_new); ++kb) block(kb);
     // tile tc has landed once every wave's share of it has; only the loads issued after it (next
     // q rows: 8 instructions, gate: 16) may still be in flight
-    if (GATED) {
-      if (has_next) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    auto wait_new_tile = [&]() {
+      if (GATED) {
+        if (has_next) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      } else {
+        if (has_next) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    };
+    using First = std::integral_constant<bool, true>;
+    using Rest = std::integral_constant<bool, false>;
+    const int kb_old = min(kb_hi, kb_new - 1);  // newest block of an older tile
+    int kb2 = max(kb_lo, kb_new);
+    if (kb_old >= kb_lo) {
+      block(kb_old, First{});
+      for (int kb = kb_old - 1; kb >= kb_lo; --kb) block(kb, Rest{});
+      wait_new_tile();
     } else {
-      if (has_next) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      wait_new_tile();
+      block(kb2++, First{});
     }
-    for (int kb = max(kb_lo, kb_new); kb <= kb_hi; ++kb) block(kb);
+    for (int kb = kb2; kb <= kb_hi; ++kb) block(kb, Rest{});
 
     // -- epilogue: every load of this step (gate, next q rows) has landed past this wait, which is
     // issued through the builtin so that the compiler's own wait tracking knows it too (the gate
@@ -703,7 +828,8 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt: no wait
     {
       const float l_tot = l_run + shfl_xor_f(l_run, 32);
-      const float inv = 1.0f / l_tot;
+      // (a gate of 0 then gives exactly half the ungated output: rcp(2 l) = rcp(l) / 2)
+      const float rcp_l = __builtin_amdgcn_rcpf(l_tot);
       const bool store = my_q < T;
       uint16_t* dst = p.out + ((int64_t)b * T + min(my_q, T - 1)) * p.so + (int64_t)head * kHeadDim;
 #pragma unroll
@@ -712,14 +838,18 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
         for (int rq = 0; rq < 4; ++rq) {
           const int d0 = 32 * db + 8 * rq + 4 * hi;
           float y[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = o[db][4 * rq + j] * inv;
           if (GATED) {
+            // o / (l * (1 + exp(-g))): one reciprocal per element covers both divisions
             const u32x2 g = graw[4 * db + rq];
             const float gv[4] = {bf16lo(g[0]), bf16hi(g[0]), bf16lo(g[1]), bf16hi(g[1])};
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              y[j] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[j] * 1.4426950408889634f));
+            for (int j = 0; j < 4; ++j) {
+              const float e = __builtin_amdgcn_exp2f(-gv[j] * 1.4426950408889634f);
+              y[j] = o[db][4 * rq + j] * __builtin_amdgcn_rcpf(__builtin_fmaf(l_tot, e, l_tot));
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = o[db][4 * rq + j] * rcp_l;
           }
           const u32x2 w = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
           if (store) *reinterpret_cast<u32x2*>(dst + d0) = w;
@@ -763,10 +893,12 @@ static hipError_t launch_swa_t(const PrefillParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-bool prefill_uses_swa(int window, int group) { return window > 0 && window <= 128 && group == 4; }
+bool prefill_uses_swa(int window, int group, int rot_half) {
+  return window > 0 && window <= 128 && group == 4 && rot_half == kSwaRotHalf;
+}
 
 hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s) {
-  if (prefill_uses_swa(p.window, group))
+  if (prefill_uses_swa(p.window, group, p.rope.half))
     return gated ? launch_swa_t<true>(p, s) : launch_swa_t<false>(p, s);
   switch (group * 2 + (gated ? 1 : 0)) {
     case 2: return launch_prefill_t<1, false>(p, s);

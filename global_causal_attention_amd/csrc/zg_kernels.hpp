@@ -24,6 +24,11 @@ struct KPrepParams {
   int64_t pos0;
   float eps;
   RopeTableH rope;
+  // Folding for the banded streaming kernel: when set, dims < rot_dim are multiplied by
+  // fold_scale and dims >= rot_dim by fold_scale * fold_w[d] (fold_w may be null: 1).
+  int32_t fold;
+  float fold_scale;
+  const float* fold_w;
 };
 
 struct PrefillParams {
@@ -88,8 +93,9 @@ struct GemmParams {
 };
 
 hipError_t launch_kprep(const KPrepParams& p, hipStream_t s);
-// True when launch_prefill takes the streaming kernel for short windows (which reads seg_steps).
-bool prefill_uses_swa(int window, int group);
+// True when launch_prefill takes the streaming kernel for short windows (which reads seg_steps and
+// expects keys prepared with KPrepParams::fold set).
+bool prefill_uses_swa(int window, int group, int rot_half);
 hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s);

@@ -62,9 +62,12 @@ def test_decode_equals_prefill_row(W):
     x = _inputs(5, B=2, T=T)
     cfg = zg.AttnConfig(window=W, gated=W > 0, rope_base=1e6)
     full = zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"])
-    # normalised/rotated keys as the prefill computes them (its workspace holds k_hat)
-    ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, 2, T), dtype=torch.uint8, device=DEV)
-    zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"], workspace=ws)
+    # normalised/rotated keys as the prefill computes them: the full causal kernel's workspace
+    # holds k_hat as is (the banded kernel's holds it with the softmax scale folded in)
+    causal = zg.AttnConfig(window=0, gated=False, rope_base=1e6)
+    ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(causal, 2, T), dtype=torch.uint8,
+                     device=DEV)
+    zg.zg_attn_prefill(causal, x["q"], x["k"], x["v"], None, workspace=ws)
     khat = ws[: 2 * T * 8 * 128 * 2].view(torch.bfloat16).view(2, T, 8, 128)
     pos = torch.tensor([T - 1, 400], dtype=torch.int32)
     rows = W if W > 0 else T

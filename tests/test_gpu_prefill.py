@@ -104,20 +104,36 @@ def _bf16(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).double().numpy()
 
 
-def _rounded_operand_reference(x, W, gated, qw, kw, base=1e4):
-    """Test-side model of the kernel's rounding points built on the oracle's prologue: the matrix
-    cores see bf16(q_hat * scale * log2 e) and bf16(k_hat), scores are in log2 units, the softmax
-    weights are rounded to bf16 and both the weighted sum and the normaliser use the rounded
-    weights; everything else is fp64."""
+def _rounded_operand_reference(x, W, gated, qw, kw, base=1e4, folded=False):
+    """Test-side model of the kernel's rounding points built on the oracle's prologue; scores are
+    in log2 units, the softmax weights are rounded to bf16 and both the weighted sum and the
+    normaliser use the rounded weights; everything else is fp64.
+
+    Unfolded (full causal kernel): the matrix cores see bf16(q_hat * scale * log2 e) and
+    bf16(k_hat). Folded (banded kernel for 42 rotary dims): they see q with its first 42 dims
+    replaced by bf16(RoPE(w_q * q)), and bf16(k_hat * scale * log2 e) with the q norm weight of
+    dims >= 42 folded in; the RMS factor of q multiplies the scores."""
     q, k, v = f64(x["q"])[0], f64(x["k"])[0], f64(x["v"])[0]
     T = q.shape[0]
     c = np.log2(np.e) / np.sqrt(128)
-    qh = _bf16(c * oracle.qk_prologue(q, np.arange(T), qw, rot_dim=42, rope_base=base, eps=1e-6))
-    kh = _bf16(oracle.qk_prologue(k, np.arange(T), kw, rot_dim=42, rope_base=base, eps=1e-6))
+    pos = np.arange(T)
+    qp = oracle.qk_prologue(q, pos, qw, rot_dim=42, rope_base=base, eps=1e-6)
+    kp = oracle.qk_prologue(k, pos, kw, rot_dim=42, rope_base=base, eps=1e-6)
+    if folded:
+        inv = 1.0 / np.sqrt(np.mean(q * q, axis=-1) + 1e-6)          # [T, Hq]
+        qh = q.copy()
+        qh[..., :42] = _bf16((qp / inv[..., None])[..., :42])
+        fold = np.full(128, c)
+        fold[42:] *= qw[42:]
+        kh = _bf16(kp * fold)
+    else:
+        inv = np.ones(q.shape[:2])
+        qh = _bf16(c * qp)
+        kh = _bf16(kp)
     out = np.zeros(q.shape)
     for t in range(T):
         lo = max(0, t - W + 1) if W > 0 else 0
-        s2 = np.einsum("hd,jhd->hj", qh[t], np.repeat(kh[lo:t + 1], 4, axis=1))
+        s2 = inv[t][:, None] * np.einsum("hd,jhd->hj", qh[t], np.repeat(kh[lo:t + 1], 4, axis=1))
         p = _bf16(np.exp2(s2 - s2.max(-1, keepdims=True)))
         o = np.einsum("hj,jhd->hd", p, np.repeat(v[lo:t + 1], 4, axis=1)) / p.sum(-1)[:, None]
         if gated:
@@ -145,5 +161,5 @@ def test_prefill_peaky_logits(W):
     x = si.prefill_layer(gen, 1, 400, 32, 8, 128, gated=True)
     qw = ((torch.rand(128, generator=gen) * 1.5 + 0.25) * 8.0).double().numpy()
     kw = (torch.rand(128, generator=gen) * 1.5 + 0.25).double().numpy()
-    model = _rounded_operand_reference(x, W, gated, qw, kw)
+    model = _rounded_operand_reference(x, W, gated, qw, kw, folded=W > 0)
     assert_parity(out, model, f"peaky logits W={W} vs bf16-operand model", max_abs=4e-2)
