@@ -454,9 +454,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 // A workgroup walks a run of 64-query steps of one (sequence b, KV head); wave w owns query head
 // w % 4 and 32 queries (block w / 4) of each step. A step needs its own 64 keys and the 128 before
 // them, i.e. three 64-key tiles, so K and V tiles sit in a three-slot LDS ring and each step brings
-// in exactly one new tile, issued at the top of the step into the slot the previous step finished
-// with; its key blocks are visited last, behind the q prologue and the blocks of the two older
-// tiles. Each wave's raw q rows for the next step stream into its own 8 KB LDS area as soon as the
+// in exactly one new tile, issued at the top of the step into the slot of a tile the previous
+// step read only before its mid-step barrier; the new tile's key blocks are visited last, behind
+// the q prologue and the blocks of the two older tiles, and one barrier per step (before those
+// blocks) is the only synchronisation. Each wave's raw q rows for the next step stream into its own 8 KB LDS area as soon as the
 // prologue has turned this step's rows into MFMA operands; the gate rows come into registers during
 // the step. Loads are tracked with explicit vmcnt waits, so no wait covers a load issued for a
 // later phase.
@@ -578,15 +579,15 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int key_lane = 4 * hi;  // key offset of this lane's score registers within a block
 
-  u32x2 graw[16];  // the lane's 64 gate values in output order
+  // Gate rows and output rows move as whole 16-byte chunks: lane (row q, hi) holds chunks
+  // 2 m + hi (m = 0..7) of row q. The MFMA output layout gives each lane 4-dim halves of every
+  // chunk instead; one v_permlane32_swap per dword converts between the two (chunk pair 2m, 2m+1).
+  u32x4 gch[8];
   auto load_gate = [&](int step) {
     const int t = 64 * (t_seg0 + step) + 32 * qb + l32;
     const uint16_t* g = p.gate + ((int64_t)b * T + min(t, T - 1)) * p.sg + (int64_t)head * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-        graw[4 * db + rq] = *reinterpret_cast<const u32x2*>(g + 32 * db + 8 * rq + 4 * hi);
+    for (int m = 0; m < 8; ++m) gch[m] = *reinterpret_cast<const u32x4*>(g + 8 * (2 * m + hi));
   };
 
   // ---- start of the run: the tiles before the first step and the first q rows
@@ -684,10 +685,10 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
     if (has_next) dma_q(step + 1);
     if (GATED) load_gate(step);
 
-    // -- attention over the 32-key blocks [kb_lo, kb_hi]; the blocks of older tiles newest first,
+    // -- attention over the 32-key blocks [kb_lo, kb_hi]: the blocks of older tiles newest first,
     // then those of tile tc. Softmax weights are exp2(inv_q * (s - mu)) with a bf16 reference mu
     // per query (subtracted by a ninth MFMA step), raised only when a partial sum leaves
-    // [0, 2^64] or no key has been seen yet.
+    // [0, 2^64] or no key has been seen yet; the first block of a step sets it from its maximum.
     f32x16 o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = f32x16{};
@@ -704,38 +705,33 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
       for (int st = 0; st < 8; ++st)
         s = mfma32(*reinterpret_cast<const bf16x8*>(kp + ((st & 1) ? k_odd : k_even) + 128 * st), qf[st], s);
       if constexpr (!first) s = mfma32(one_op, qm, s);
-      // masks: key k0 + c_r + 4 hi is valid for query my_q when 0 <= my_q - key < W
+      // masks: key k0 + c_r + 4 hi is valid for query my_q when 0 <= my_q - key < W, i.e. when
+      // (unsigned)(t - c_r) < W with t = my_q - k0 - 4 hi
       const int k0 = 32 * kb;
-      const bool need_causal = k0 + 31 > qbase;
-      const bool need_window = k0 < qbase + 32 - W;
-      if (need_causal || need_window) {
-        const int t = my_q - k0 - key_lane;  // valid: c_r <= t and c_r > t - W
+      if (k0 + 31 > qbase || k0 < qbase + 32 - W) {
+        const uint32_t t = (uint32_t)(my_q - k0 - key_lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int cr = 8 * (r >> 2) + (r & 3);
-          bool ok = true;
-          if (need_causal) ok = cr <= t;
-          if (need_window) ok = ok && (cr > t - W);
-          s[r] = ok ? s[r] : -INFINITY;
+          const uint32_t cr = 8 * (r >> 2) + (r & 3);
+          s[r] = (t - cr < (uint32_t)W) ? s[r] : -INFINITY;
         }
       }
       u32x4 pk[2];
       float rs;
       if constexpr (first) {
-        // first block of the step: the reference is this block's maximum (o and l are still 0)
         float mx = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                         false, false);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1]));
         m_valid = mx > -INFINITY;
         mu = m_valid ? bf16lo(pack_bf16(mx, 0.f)) : 0.f;
+        const float nmu = -inv_q * mu;
         float pt = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(inv_q * (s[2 * k] - mu)),
-                                       __builtin_amdgcn_exp2f(inv_q * (s[2 * k + 1] - mu)));
+          const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(inv_q, s[2 * k], nmu)),
+                                       __builtin_amdgcn_exp2f(__builtin_fmaf(inv_q, s[2 * k + 1], nmu)));
           pk[k >> 2][k & 3] = w;
           pt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, pt, false);
         }
@@ -756,8 +752,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
           float mx = s[0];
 #pragma unroll
           for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                           false, false);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
           mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1])) + mu;
           const bool has = mx > -INFINITY;
           float mu_new = m_valid ? fmaxf(mu, mx) : mx;
@@ -796,13 +791,13 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
     };
     const int kb_lo = max(0, (qbase - W + 1) >> 5);
     const int kb_hi = qbase >> 5;
-    const int kb_new = 2 * tc;              // first block of tile tc
+    const int kb_new = 2 * tc;
     // tile tc has landed once every wave's share of it has; only the loads issued after it (next
-    // q rows: 8 instructions, gate: 16) may still be in flight
+    // q rows: 8 instructions, gate: 8) may still be in flight
     auto wait_new_tile = [&]() {
       if (GATED) {
-        if (has_next) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        if (has_next) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
       } else {
         if (has_next) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -832,16 +827,28 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
       const float rcp_l = __builtin_amdgcn_rcpf(l_tot);
       const bool store = my_q < T;
       uint16_t* dst = p.out + ((int64_t)b * T + min(my_q, T - 1)) * p.so + (int64_t)head * kHeadDim;
+      if (GATED) {
+        // chunks -> output layout: dims 8c + 4 hi .. + 3 of chunk c in half (c & 1) of gch[c / 2]
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d0 = 32 * db + 8 * rq + 4 * hi;
+          for (int d = 0; d < 2; ++d) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(gch[m][d], gch[m][d + 2], false, false);
+            gch[m][d] = sw[0];
+            gch[m][d + 2] = sw[1];
+          }
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint32_t w[4];  // output layout words of chunks 2m (w[0..1]) and 2m + 1 (w[2..3])
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = 2 * m + h, db = c >> 2, rq = c & 3;
           float y[4];
           if (GATED) {
             // o / (l * (1 + exp(-g))): one reciprocal per element covers both divisions
-            const u32x2 g = graw[4 * db + rq];
-            const float gv[4] = {bf16lo(g[0]), bf16hi(g[0]), bf16lo(g[1]), bf16hi(g[1])};
+            const uint32_t g0 = gch[m][2 * h], g1 = gch[m][2 * h + 1];
+            const float gv[4] = {bf16lo(g0), bf16hi(g0), bf16lo(g1), bf16hi(g1)};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float e = __builtin_amdgcn_exp2f(-gv[j] * 1.4426950408889634f);
@@ -851,12 +858,22 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
 #pragma unroll
             for (int j = 0; j < 4; ++j) y[j] = o[db][4 * rq + j] * rcp_l;
           }
-          const u32x2 w = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
-          if (store) *reinterpret_cast<u32x2*>(dst + d0) = w;
+          w[2 * h] = pack_bf16(y[0], y[1]);
+          w[2 * h + 1] = pack_bf16(y[2], y[3]);
         }
+        // output layout -> chunk 2m + hi of this lane's row
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(w[d], w[d + 2], false, false);
+          w[d] = sw[0];
+          w[d + 2] = sw[1];
+        }
+        if (store)
+          *reinterpret_cast<u32x4*>(dst + 8 * (2 * m + hi)) = u32x4{w[0], w[1], w[2], w[3]};
+      }
     }
-    // every wave is done with the oldest tile's slot, which the next step refills
-    asm volatile("s_barrier" ::: "memory");
+    // No barrier here: the slot the next step refills held a tile that only the older-tile blocks
+    // of this step read, and every wave finished those before the barrier above.
   }
 }
 
