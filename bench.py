@@ -125,6 +125,11 @@ def main():
     swa_flop = B * HQ * n_pairs(T, W) * flop_pair
     swa_bytes = B * T * (HQ * D * 2 * 3 + HKV * D * 2 * 2)   # q, gate, out + k, v (bf16)
     glo_achieved = glo_flop / (glo_ms * 1e-3)
+    # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record (null if the kernels
+    # changed since it was taken)
+    from global_causal_attention_amd.counters import lookup_traffic
+    parts = [lookup_traffic("prefill_kernel<4, false>"), lookup_traffic("kprep_kernel")]
+    glo_traffic = None if None in parts else sum(parts)
     result = {
         "metric": "gated-SWA/global attn prefill tokens/s + %MFMA peak; decode HBM GB/s %peak",
         "value": round(value, 1),
@@ -143,8 +148,10 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(glo_achieved / 1e12, 2),
                      "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
-                     "frac": round(glo_achieved / MFMA_BF16_PEAK, 4), "traffic": None,
-                     "kernel": "global causal prefill (kprep + prefill_kernel<4,false>) per launch",
+                     "frac": round(glo_achieved / MFMA_BF16_PEAK, 4),
+                     "traffic": glo_traffic,
+                     "kernel": "global causal prefill launch (kprep_kernel + "
+                               "prefill_kernel<4, false>)",
                      "flop_per_launch": glo_flop},
         "layers": {
             "swa_ms": round(swa_ms, 4), "global_ms": round(glo_ms, 4),
@@ -215,9 +222,15 @@ def bench_decode(torch, zg, si, dev, stream, reps):
                      "hbm_frac": round(bw / HBM_PEAK, 4), "tokens_per_s": round(Bd / (med * 1e-3), 1)}
         log(f"[bench] decode {name}: {med:.4f} ms, {bw / 1e9:.1f} GB/s")
     res["workload"] = "B=64, Hq=32 Hkv=8 D=128, ring W=128 gated; linear L~U[8192,65536] ungated; base 1e7; cold MALL"
+    from global_causal_attention_amd.counters import lookup_traffic
+    parts = [lookup_traffic("decode_prep_kernel", 16384),
+             lookup_traffic("decode_attn_kernel<4>", Bd * HKV * 16 * 1024),
+             lookup_traffic("decode_combine_kernel", 262144)]
     res["roofline"] = {"bound": "hbm", "achieved": res["linear"]["GBps"], "peak": HBM_PEAK / 1e9,
-                       "unit": "GB/s", "frac": res["linear"]["hbm_frac"], "traffic": None,
-                       "kernel": "global decode (prep + split-KV attention + combine)"}
+                       "unit": "GB/s", "frac": res["linear"]["hbm_frac"],
+                       "traffic": None if None in parts else sum(parts),
+                       "kernel": "global decode launch (decode_prep_kernel + "
+                                 "decode_attn_kernel<4> + decode_combine_kernel)"}
     del x, flush
     return res
 

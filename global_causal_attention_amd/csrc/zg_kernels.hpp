@@ -96,6 +96,7 @@ hipError_t launch_kprep(const KPrepParams& p, hipStream_t s);
 // True when launch_prefill takes the streaming kernel for short windows (which reads seg_steps and
 // expects keys prepared with KPrepParams::fold set).
 bool prefill_uses_swa(int window, int group, int rot_half);
+hipError_t launch_prefill_swa(const PrefillParams& p, bool gated, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s);
