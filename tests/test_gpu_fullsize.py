@@ -1,0 +1,124 @@
+"""GPU parity at the benchmark sizes, on sampled outputs the fp64 oracle computes one by one.
+
+Workloads (seeded N(0,1) bf16, drawn on the device with a seeded generator; the oracle reads the
+same tensors copied to the host):
+  * B=4, T=16384 gated local layer (W=128) and full causal layer, RoPE base 1e6 (the timed 5:1
+    block): sampled query rows of every sequence, all 32 heads, in the launch configuration the
+    benchmark times (runs of 32 steps of 64 queries for the local layer);
+  * B=64 decode step, 128-slot rings and linear caches with context lengths uniform on
+    [8192, 65536], base 1e7: every ring sequence, sampled linear sequences;
+  * B=1, T=262144 gated local and full causal layers, base 1e7: sampled rows.
+Sampled rows cover the sequence edges, tile/step/run boundaries (+-1 around multiples of 64 and
+2048) and seeded uniform positions."""
+import numpy as np
+import pytest
+import torch
+
+import global_causal_attention_amd as zg
+import oracle
+import synth_inputs as si
+from helpers import assert_parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _host(t):
+    return t.float().cpu().numpy()
+
+
+def _rows(T, n_uniform, seed):
+    edges = {0, 1, 2, 126, 127, 128, 129, T - 2, T - 1}
+    for m in (64, 2048):
+        for c in range(m, T, max(m, T // 8)):
+            edges |= {c - 1, c, c + 1}
+    rng = np.random.default_rng(seed)
+    edges |= set(rng.integers(0, T, n_uniform).tolist())
+    return sorted(r for r in edges if 0 <= r < T)
+
+
+def _layer(B, T, seed, base):
+    gen = si.generator(seed, device=DEV)
+    return si.prefill_layer(gen, B, T, 32, 8, 128, gated=True, device=DEV)
+
+
+@pytest.mark.parametrize("W", [128, 0])
+def test_b4_t16384_sampled_rows(W):
+    B, T, base = 4, 16384, 1e6
+    print(f"[case] B={B} T={T} W={W} base={base}", flush=True)
+    x = _layer(B, T, 1001, base)
+    cfg = zg.AttnConfig(window=W, gated=W > 0, rope_base=base)
+    out = zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"] if W else None)
+    torch.cuda.synchronize()
+    rows = _rows(T, 96 if W else 24, 11 + W)
+    q, k, v, g = (_host(x[n]) for n in ("q", "k", "v", "gate"))
+    got = _host(out[:, rows])
+    if W:
+        ref = np.concatenate([oracle.prefill_rows(q, k, v, g, [r], window=W, gated=True,
+                                                  rope_base=base) for r in rows], axis=1)
+    else:
+        ref = oracle.prefill_rows(q, k, v, None, rows, window=0, gated=False, rope_base=base)
+    assert_parity(got, ref, f"B=4 T=16384 W={W}, {len(rows)} rows x 4 sequences")
+
+
+def test_b64_decode_rings_and_linear_caches():
+    Bd, lo, hi = 64, 8192, 65536
+    print(f"[case] decode B={Bd} L~U[{lo},{hi}]", flush=True)
+    x = si.decode_step(si.generator(1002, device=DEV), B=Bd, len_lo=lo, len_hi=hi, device=DEV)
+    seq = x["seqlens"]
+    seq_h = seq.cpu().numpy()
+    # local layer: 128-slot rings, gated
+    cfg = zg.AttnConfig(window=128, gated=True, rope_base=1e7)
+    kc, vc = x["ring_k"].clone(), x["ring_v"].clone()
+    out = zg.zg_attn_decode(cfg, x["q_new"], x["k_new"], x["v_new"], x["gate"], kc, vc, seq,
+                            max_seqlen=hi)
+    torch.cuda.synchronize()
+    ref, rk, rv = oracle.decode(_host(x["q_new"]), _host(x["k_new"]), _host(x["v_new"]),
+                                _host(x["gate"]), _host(x["ring_k"]), _host(x["ring_v"]), seq_h,
+                                window=128, gated=True, rope_base=1e7)
+    assert_parity(out, ref, "decode B=64 rings")
+    rel = np.abs(kc.float().cpu().numpy() - rk) / np.maximum(np.abs(rk), 1e-6)
+    assert rel.max() <= 2.0 ** -7, f"ring K after the write: rel {rel.max():.2e}"
+    assert torch.equal(vc.cpu(), torch.from_numpy(rv).to(torch.bfloat16)), "ring V write"
+    # global layer: linear caches, ungated; the oracle runs on sampled sequences
+    cfg = zg.AttnConfig(window=0, gated=False, rope_base=1e7)
+    kc, vc = x["lin_k"], x["lin_v"]
+    out = zg.zg_attn_decode(cfg, x["q_new"], x["k_new"], x["v_new"], None, kc, vc, seq,
+                            max_seqlen=hi)
+    torch.cuda.synchronize()
+    pick = sorted(set([int(np.argmax(seq_h)), int(np.argmin(seq_h))] +
+                      np.random.default_rng(5).choice(Bd, 10, replace=False).tolist()))
+    for b in pick:
+        L = int(seq_h[b])
+        r, rk, _ = oracle.decode(_host(x["q_new"][b:b + 1]), _host(x["k_new"][b:b + 1]),
+                                 _host(x["v_new"][b:b + 1]), None, _host(kc[b:b + 1, :L]),
+                                 _host(vc[b:b + 1, :L]), seq_h[b:b + 1], window=0, gated=False,
+                                 rope_base=1e7)
+        assert_parity(out[b:b + 1], r, f"decode linear sequence {b} (L={L})")
+        # the written row is one bf16 rounding of the fp32 k_hat: within a bf16 ulp of fp64
+        got_k, ref_k = kc[b, L - 1].float().cpu().numpy(), rk[0, L - 1]
+        rel = np.abs(got_k - ref_k) / np.maximum(np.abs(ref_k), 1e-6)
+        assert rel.max() <= 2.0 ** -7, f"linear K row {L - 1} of sequence {b}: rel {rel.max():.2e}"
+        assert torch.equal(vc[b, L - 1].cpu(), x["v_new"][b].cpu()), "linear V write"
+
+
+@pytest.mark.parametrize("W", [128, 0])
+def test_t262144_sampled_rows(W):
+    T, base = 262144, 1e7
+    print(f"[case] B=1 T={T} W={W} base={base}", flush=True)
+    x = _layer(1, T, 1003, base)
+    cfg = zg.AttnConfig(window=W, gated=W > 0, rope_base=base)
+    out = zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"] if W else None)
+    torch.cuda.synchronize()
+    if W:
+        rows = _rows(T, 48, 21)
+        q, k, v, g = (_host(x[n]) for n in ("q", "k", "v", "gate"))
+        ref = np.concatenate([oracle.prefill_rows(q, k, v, g, [r], window=W, gated=True,
+                                                  rope_base=base) for r in rows], axis=1)
+    else:
+        rows = [0, 1, 127, 128, 129, 4095, 65536, 131071, 262143] + \
+            np.random.default_rng(22).integers(0, T, 3).tolist()
+        rows = sorted(set(rows))
+        q, k, v = (_host(x[n]) for n in ("q", "k", "v"))
+        ref = oracle.prefill_rows(q, k, v, None, rows, window=0, gated=False, rope_base=base)
+    assert_parity(_host(out[:, rows]), ref, f"B=1 T=262144 W={W}, {len(rows)} rows")
