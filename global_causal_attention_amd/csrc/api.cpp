@@ -37,6 +37,7 @@ zg_status hip_status(hipError_t e, const char* where) {
 
 constexpr int kD = 128;
 constexpr int64_t kDecodeChunk = 1024;
+constexpr int64_t kDecodeMaxChunks = 1024;  // split-KV chunks the combine kernel merges
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -233,6 +234,10 @@ zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride
     if (B < 1) return fail(ZG_ERR_SHAPE, "B=%d must be >= 1", B);
     if (max_seqlen < 1 || max_seqlen >= (int64_t(1) << 31))
       return fail(ZG_ERR_SHAPE, "max_seqlen=%lld out of range", (long long)max_seqlen);
+    const int64_t keys = cfg->window > 0 ? std::min<int64_t>(cfg->window, max_seqlen) : max_seqlen;
+    if ((keys + kDecodeChunk - 1) / kDecodeChunk > kDecodeMaxChunks)
+      return fail(ZG_ERR_UNSUPPORTED, "max_seqlen=%lld: at most %lld keys per sequence",
+                  (long long)max_seqlen, (long long)(kDecodeChunk * kDecodeMaxChunks));
     if (cfg->window == 0 && cache_stride < max_seqlen)
       return fail(ZG_ERR_SHAPE, "linear cache: cache_stride=%lld < max_seqlen=%lld",
                   (long long)cache_stride, (long long)max_seqlen);
@@ -247,7 +252,6 @@ zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride
     if (!aligned16(workspace)) return fail(ZG_ERR_SHAPE, "workspace must be 16-byte aligned");
 
     const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
-    const int64_t keys = cfg->window > 0 ? std::min<int64_t>(cfg->window, max_seqlen) : max_seqlen;
     zg::DecodeParams p{};
     p.q_new = static_cast<const uint16_t*>(q_new);
     p.k_new = static_cast<const uint16_t*>(k_new);

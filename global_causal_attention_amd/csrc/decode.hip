@@ -19,9 +19,19 @@ namespace zg {
 namespace {
 constexpr int kDecThreads = 256;
 constexpr int kPartStride = 132;  // floats per partial record: m, l, pad, pad, o[128]
+constexpr int kMaxChunks = 1024;  // chunks per sequence the combine kernel merges
 
 __device__ __forceinline__ int64_t n_valid_rows(int pos, int window) {
   return window > 0 ? (int64_t)min(pos + 1, window) : (int64_t)pos + 1;
+}
+
+// Sum over the 16 lanes of a DPP row, left in every lane: rotations by 8, 4, 2 and 1 (VALU only).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+  return v;
 }
 }  // namespace
 
@@ -29,6 +39,8 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeParams p) {
   __shared__ float stage[128 * 64];
   const int b = blockIdx.x;
   const int pos = p.seqlens[b] - 1;
+  // a length outside [1, cache rows] is a caller error: touch nothing (the output is unspecified)
+  if (pos < 0 || (p.window == 0 && pos >= p.rows)) return;
   const int64_t row = p.window > 0 ? (int64_t)(pos % p.window) : (int64_t)pos;
   const int pair = threadIdx.x >> 1;
   const int half = threadIdx.x & 1;
@@ -83,7 +95,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int pos = p.seqlens[b] - 1;
-  const int64_t n_valid = n_valid_rows(pos, p.window);
+  if (pos < 0 || (p.window == 0 && pos >= p.rows)) return;
+  const int64_t n_valid = min(n_valid_rows(pos, p.window), (int64_t)p.n_chunks * p.chunk);
   const int64_t k0 = (int64_t)chunk_id * p.chunk;
   if (k0 >= n_valid) return;
   const int n = (int)min((int64_t)p.chunk, n_valid - k0);
@@ -132,12 +145,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
         d[h] = a;
       }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        d[h] += shfl_xor_f(d[h], 8);
-        d[h] += shfl_xor_f(d[h], 4);
-        d[h] += shfl_xor_f(d[h], 2);
-        d[h] += shfl_xor_f(d[h], 1);
-      }
+      for (int h = 0; h < G; ++h) d[h] = row16_sum(d[h]);
       const int j = j0 + 16 * u + kg;
       if (j < n && dl < G) {
         float v = d[0];
@@ -240,24 +248,48 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
   }
 }
 
+// One workgroup per (head, sequence), one thread per output dim. The chunk weights exp2(m_c - M)
+// are formed once (chunks spread over the threads) and shared through LDS; the per-dim sums then
+// issue their loads independently of each other.
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
+  __shared__ float w_s[kMaxChunks];
+  __shared__ float red[2];
   const int head = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
   const int pos = p.seqlens[b] - 1;
+  if (pos < 0 || (p.window == 0 && pos >= p.rows)) return;
   const int64_t n_valid = n_valid_rows(pos, p.window);
-  const int nc = (int)((n_valid + p.chunk - 1) / p.chunk);
+  const int nc = (int)min((n_valid + p.chunk - 1) / p.chunk, (int64_t)p.n_chunks);
   if (nc <= 1) return;
   const float* rec = p.partial + ((int64_t)b * p.Hq + head) * p.n_chunks * kPartStride;
   float mx = -INFINITY;
-  for (int c = 0; c < nc; ++c) mx = fmaxf(mx, rec[c * kPartStride]);
-  float l = 0.f, o = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float w = __builtin_amdgcn_exp2f(rec[c * kPartStride] - mx);
-    l += rec[c * kPartStride + 1] * w;
-    o += rec[c * kPartStride + 4 + d] * w;
+  for (int c = d; c < nc; c += 128) mx = fmaxf(mx, rec[(int64_t)c * kPartStride]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  float lw = 0.f;
+  for (int c = d; c < nc; c += 128) {
+    const float w = __builtin_amdgcn_exp2f(rec[(int64_t)c * kPartStride] - mx);
+    w_s[c] = w;
+    lw += rec[(int64_t)c * kPartStride + 1] * w;
   }
-  float y = o / l;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lw += shfl_xor_f(lw, o);
+  __syncthreads();  // every thread has read red[] above before it is reused
+  if ((d & 63) == 0) red[d >> 6] = lw;
+  __syncthreads();
+  const float l = red[0] + red[1];
+  float o0 = 0.f, o1 = 0.f;
+  int c = 0;
+  for (; c + 1 < nc; c += 2) {
+    o0 += rec[(int64_t)c * kPartStride + 4 + d] * w_s[c];
+    o1 += rec[(int64_t)(c + 1) * kPartStride + 4 + d] * w_s[c + 1];
+  }
+  if (c < nc) o0 += rec[(int64_t)c * kPartStride + 4 + d] * w_s[c];
+  float y = (o0 + o1) / l;
   if (p.gated) {
     const float g = bf16lo(p.gate[((int64_t)b * p.Hq + head) * kHeadDim + d]);
     y *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));

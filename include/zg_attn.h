@@ -100,9 +100,12 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
  * row of pos, then attends over positions max(0, pos-W+1)..pos (ring) or 0..pos (linear) and
  * applies the gate if cfg->gated. The result equals prefill row pos over the same keys.
  *   workspace >= zg_attn_decode_workspace_bytes(cfg, B, max_seqlen) (split-KV partials).
- * Errors as for prefill; max_seqlen < 1 or cache_stride < max_seqlen (linear) -> ZG_ERR_SHAPE.
- * seqlens values are device data and are not validated; out-of-range values are undefined
- * behaviour. */
+ * Errors as for prefill; max_seqlen < 1 or cache_stride < max_seqlen (linear) -> ZG_ERR_SHAPE;
+ * more than 2^20 keys to attend over (linear max_seqlen > 1048576) -> ZG_ERR_UNSUPPORTED.
+ * seqlens values are device data and are not validated by the host; the kernels skip a sequence
+ * whose seqlens[b] is < 1, or > cache_stride for a linear cache (no cache write, its out rows
+ * unspecified), so no access leaves the caches; values above max_seqlen are otherwise a caller
+ * error with unspecified results. */
 size_t zg_attn_decode_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int64_t max_seqlen);
 
 zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
