@@ -36,8 +36,7 @@ zg_status hip_status(hipError_t e, const char* where) {
 }
 
 constexpr int kD = 128;
-constexpr int64_t kDecodeChunk = 1024;
-constexpr int64_t kDecodeMaxChunks = 1024;  // split-KV chunks the combine kernel merges
+constexpr int64_t kDecodeChunk = zg::kDecodeChunkKeys;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -235,9 +234,9 @@ zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride
     if (max_seqlen < 1 || max_seqlen >= (int64_t(1) << 31))
       return fail(ZG_ERR_SHAPE, "max_seqlen=%lld out of range", (long long)max_seqlen);
     const int64_t keys = cfg->window > 0 ? std::min<int64_t>(cfg->window, max_seqlen) : max_seqlen;
-    if ((keys + kDecodeChunk - 1) / kDecodeChunk > kDecodeMaxChunks)
+    if ((keys + kDecodeChunk - 1) / kDecodeChunk > zg::kDecodeMaxChunks)
       return fail(ZG_ERR_UNSUPPORTED, "max_seqlen=%lld: at most %lld keys per sequence",
-                  (long long)max_seqlen, (long long)(kDecodeChunk * kDecodeMaxChunks));
+                  (long long)max_seqlen, (long long)(kDecodeChunk * zg::kDecodeMaxChunks));
     if (cfg->window == 0 && cache_stride < max_seqlen)
       return fail(ZG_ERR_SHAPE, "linear cache: cache_stride=%lld < max_seqlen=%lld",
                   (long long)cache_stride, (long long)max_seqlen);

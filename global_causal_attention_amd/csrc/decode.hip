@@ -6,11 +6,13 @@
 // Three launches on the caller's stream:
 //  1. decode_prep: RMSNorm + RoPE of q_new (kept as bf16-rounded fp32 in the workspace) and of k_new
 //     (written into its cache row with v_new). Stream order makes the new row visible to step 2.
-//  2. decode_attn: split-KV. One workgroup per (sequence, KV head, chunk of keys). Pass A streams the
-//     chunk's K rows (16 lanes x 16 bytes per row) and forms the G scores of every key; the chunk's
-//     softmax is then exact (max, exp2, sum over LDS); pass B streams the V rows and accumulates
-//     P V. A sequence with one chunk writes its output directly; otherwise the chunk writes
-//     (max, sum, unnormalised o) partials.
+//  2. decode_attn: split-KV. One workgroup per (sequence, KV head, chunk of 1024 keys). Pass A
+//     streams the chunk's K rows (8 lanes x 2 x 16 bytes per 256-byte row, non-temporal loads) and
+//     forms the G scores of every key with v_dot2_f32_bf16 on bf16 pairs; the chunk's softmax is
+//     then exact (max, exp2, sum over LDS) and leaves bf16 P in key pairs; pass B streams the V rows
+//     (16 lanes x 16 bytes per row) and accumulates P V, again with v_dot2_f32_bf16 over key pairs.
+//     A sequence with one chunk writes its output directly; otherwise the chunk writes (max, sum,
+//     unnormalised o) partials.
 //  3. decode_combine: log-sum-exp merge of the partials, gate, bf16 store.
 #include "zg_common.hpp"
 
@@ -19,7 +21,6 @@ namespace zg {
 namespace {
 constexpr int kDecThreads = 256;
 constexpr int kPartStride = 132;  // floats per partial record: m, l, pad, pad, o[128]
-constexpr int kMaxChunks = 1024;  // chunks per sequence the combine kernel merges
 
 __device__ __forceinline__ int64_t n_valid_rows(int pos, int window) {
   return window > 0 ? (int64_t)min(pos + 1, window) : (int64_t)pos + 1;
@@ -83,12 +84,49 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeParams p) {
   }
 }
 
+constexpr int kDecKL = 8;  // lanes per key row in pass A
+constexpr int kDecLA = 8;  // 16-byte K loads in flight per lane in pass A
+
+namespace {
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
+// Sum over groups of KL consecutive lanes (KL = 4, 8 or 16), left in every lane of the group.
+template <int KL>
+__device__ __forceinline__ float group_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if constexpr (KL >= 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  if constexpr (KL >= 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// Cache rows are read once per step: non-temporal loads keep them from displacing reused lines.
+__device__ __forceinline__ u32x4 stream_load(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+}  // namespace
+
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p) {
-  constexpr int kMaxChunk = 1024;
-  __shared__ float q_s[G][kHeadDim];
-  __shared__ float s_s[G][kMaxChunk];
-  __shared__ float red[4][G][kHeadDim];
+  constexpr int kMaxChunk = kDecodeChunkKeys;
+  constexpr int KL = kDecKL;
+  constexpr int CPK = 16 / KL;          // 16-byte pieces of a 256-byte key row per lane (pass A)
+  constexpr int KPR = kDecThreads / KL;  // keys per workgroup round (pass A)
+  constexpr int UA = kDecLA / CPK > 0 ? kDecLA / CPK : 1;  // rounds per pass-A step
+  constexpr int STEP_A = KPR * UA;       // keys per pass-A step
+  static_assert(KL == 4 || KL == 8 || KL == 16, "lanes per key");
+  static_assert(kMaxChunk % 64 == 0, "pass B walks the chunk in blocks of 64 keys");
+  static_assert(G * kMaxChunk >= 4 * G * kHeadDim, "the score rows also hold the final reduction");
+  // Head h's row of s_s holds its raw scores; the softmax then overwrites the row's first half
+  // with bf16 P in key pairs (dword q <- keys of pair q, read before any later write reaches
+  // them); after pass B the array holds the cross-wave reduction.
+  __shared__ float s_s[G * kMaxChunk];
   __shared__ float ml[G][2];
 
   const int chunk_id = blockIdx.x;
@@ -105,107 +143,146 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int kg = tid >> 4;   // key slot 0..15
-  const int dl = tid & 15;   // 8-dim chunk
-
-  for (int i = tid; i < G * kHeadDim; i += kDecThreads)
-    q_s[i / kHeadDim][i % kHeadDim] =
-        p.qhat[((int64_t)b * p.Hq + kvh * G) * kHeadDim + i];
-  __syncthreads();
-  float qv[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qv[h][j] = q_s[h][8 * dl + j];
-
   const int64_t row_stride = (int64_t)p.Hkv * kHeadDim;
-  const uint16_t* kbase = p.k_cache + ((int64_t)b * p.rows + k0) * row_stride + kvh * kHeadDim + 8 * dl;
-  const uint16_t* vbase = p.v_cache + ((int64_t)b * p.rows + k0) * row_stride + kvh * kHeadDim + 8 * dl;
+  const int64_t head_off = ((int64_t)b * p.rows + k0) * row_stride + kvh * kHeadDim;
 
-  // ---- pass A: scores (log2 domain)
-  constexpr int U = 4;
-  for (int j0 = 0; j0 < n; j0 += 16 * U) {
-    u32x4 kr[U];
+  // ---- pass A: raw scores q.k (bf16 pairs through v_dot2_f32_bf16, fp32 sums)
+  {
+    const int kq = tid / KL;
+    const int sub = tid % KL;
+    uint32_t qp[G][CPK][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + 16 * u + kg;
-      kr[u] = j < n ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * row_stride)
-                    : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kx[8];
-      unpack8(kr[u], kx);
-      float d[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a += qv[h][e] * kx[e];
-        d[h] = a;
+      for (int c = 0; c < CPK; ++c) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(
+            p.qhat + ((int64_t)b * p.Hq + kvh * G + h) * kHeadDim + 8 * sub + 8 * KL * c);
+        const f32x4 a = src[0], bb = src[1];
+        qp[h][c][0] = pack_bf16(a[0], a[1]);
+        qp[h][c][1] = pack_bf16(a[2], a[3]);
+        qp[h][c][2] = pack_bf16(bb[0], bb[1]);
+        qp[h][c][3] = pack_bf16(bb[2], bb[3]);
       }
+    const uint16_t* kbase = p.k_cache + head_off + 8 * sub;
+    auto load = [&](u32x4 (&kr)[UA][CPK], int j0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) d[h] = row16_sum(d[h]);
-      const int j = j0 + 16 * u + kg;
-      if (j < n && dl < G) {
-        float v = d[0];
+      for (int u = 0; u < UA; ++u) {
+        const int j = j0 + KPR * u + kq;
 #pragma unroll
-        for (int h = 1; h < G; ++h) v = (dl == h) ? d[h] : v;
-        s_s[dl][j] = v * p.scale_log2;
+        for (int c = 0; c < CPK; ++c)
+          kr[u][c] = j < n ? stream_load(kbase + (int64_t)j * row_stride + 8 * KL * c)
+                           : u32x4{0u, 0u, 0u, 0u};
       }
+    };
+    auto score = [&](const u32x4 (&kr)[UA][CPK], int j0) {
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        float d[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float a = 0.f;
+#pragma unroll
+          for (int c = 0; c < CPK; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t w = kr[u][c][i];
+              a = dot2(w, qp[h][c][i], a);
+            }
+          d[h] = group_sum<KL>(a);
+        }
+        const int j = j0 + KPR * u + kq;
+#pragma unroll
+        for (int h0 = 0; h0 < G; h0 += KL) {  // lane sub writes heads h0 + sub
+          if (j < n && h0 + sub < G) {
+            float v = d[h0];
+#pragma unroll
+            for (int h = h0 + 1; h < G && h < h0 + KL; ++h) v = (sub == h - h0) ? d[h] : v;
+            s_s[(h0 + sub) * kMaxChunk + j] = v;
+          }
+        }
+      }
+    };
+    for (int j0 = 0; j0 < n; j0 += STEP_A) {
+      u32x4 ka[UA][CPK];
+      load(ka, j0);
+      score(ka, j0);
     }
   }
   __syncthreads();
 
-  // ---- exact softmax over the chunk: one wave per head
+  // ---- exact softmax over the chunk, one wave per head; P rounded to bf16 and stored in key
+  // pairs over the head's score row, the row sum taken over the rounded values. Pass B pairs key
+  // j with key j + 16 (j % 32 < 16): dword (j / 64) * 32 + ((j / 32) % 2) * 16 + j % 16 holds both.
+  const int n_pad = (n + 63) & ~63;
   for (int h = wave; h < G; h += 4) {
+    float* sh = s_s + h * kMaxChunk;
     float mx = -INFINITY;
-    for (int j = lane; j < n; j += 64) mx = fmaxf(mx, s_s[h][j]);
+    for (int j = lane; j < n; j += 64) mx = fmaxf(mx, sh[j]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+    const float c = p.scale_log2;
+    const float nmc = -mx * c;
     float sum = 0.f;
-    for (int j = lane; j < n; j += 64) {
-      const float e = __builtin_amdgcn_exp2f(s_s[h][j] - mx);
-      s_s[h][j] = e;
-      sum += e;
+    for (int q = lane; q < n_pad / 2; q += 64) {
+      const int ja = (q >> 5) * 64 + ((q >> 4) & 1) * 32 + (q & 15);  // ja >= q
+      const int jb = ja + 16;
+      const float ea = ja < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(sh[ja], c, nmc)) : 0.f;
+      const float eb = jb < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(sh[jb], c, nmc)) : 0.f;
+      const uint32_t w = pack_bf16(ea, eb);
+      sh[q] = __uint_as_float(w);  // same element type as the score reads: no reordering across
+      sum += bf16lo(w) + bf16hi(w);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += shfl_xor_f(sum, o);
     if (lane == 0) {
-      ml[h][0] = mx;
+      ml[h][0] = mx * c;
       ml[h][1] = sum;
     }
   }
   __syncthreads();
 
-  // ---- pass B: o[h][d] = sum_j p[h][j] v[j][d]
+  // ---- pass B: o[h][d] = sum_j p[h][j] v[j][d]; keys j and j + 16 of a lane paired per dim
+  const int kg = tid >> 4;  // key slot 0..15
+  const int dl = tid & 15;  // 8-dim piece of the row
   float acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  for (int j0 = 0; j0 < n; j0 += 16 * U) {
-    u32x4 vr[U];
+  const uint16_t* vbase = p.v_cache + head_off + 8 * dl;
+  auto load_v = [&](u32x4 (&vr)[4], int j0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int j = j0 + 16 * u + kg;
-      vr[u] = j < n ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * row_stride)
-                    : u32x4{0u, 0u, 0u, 0u};
+      vr[u] = j < n ? stream_load(vbase + (int64_t)j * row_stride) : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  auto accumulate = [&](const u32x4 (&vr)[4], int j0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + 16 * u + kg;
-      if (j < n) {
-        float vx[8];
-        unpack8(vr[u], vx);
+    for (int t = 0; t < 2; ++t) {
+      uint32_t lo[4], hi[4];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pj = s_s[h][j];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = vr[2 * t][i], bb = vr[2 * t + 1][i];
+        lo[i] = __builtin_amdgcn_perm(bb, a, 0x05040100u);  // dim 2i of keys (j, j + 16)
+        hi[i] = __builtin_amdgcn_perm(bb, a, 0x07060302u);  // dim 2i + 1
+      }
+      const int q = (j0 >> 6) * 32 + t * 16 + kg;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] += pj * vx[e];
+      for (int h = 0; h < G; ++h) {
+        const uint32_t pw = __float_as_uint(s_s[h * kMaxChunk + q]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[h][2 * i] = dot2(lo[i], pw, acc[h][2 * i]);
+          acc[h][2 * i + 1] = dot2(hi[i], pw, acc[h][2 * i + 1]);
         }
       }
     }
+  };
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    u32x4 va[4];
+    load_v(va, j0);
+    accumulate(va, j0);
   }
   // reduce the 4 key slots of a wave (lanes 16 apart), then the 4 waves through LDS
 #pragma unroll
@@ -217,18 +294,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
       a += shfl_xor_f(a, 32);
       acc[h][e] = a;
     }
+  __syncthreads();  // every wave is done reading P
+  float* red = s_s;  // [4 waves][G][128]
   if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[wave][h][8 * lane + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) red[(wave * G + h) * kHeadDim + 8 * lane + e] = acc[h][e];
   }
   __syncthreads();
 
   for (int i = tid; i < G * kHeadDim; i += kDecThreads) {
     const int h = i / kHeadDim;
     const int d = i - h * kHeadDim;
-    const float o = red[0][h][d] + red[1][h][d] + red[2][h][d] + red[3][h][d];
+    const float o = red[(0 * G + h) * kHeadDim + d] + red[(1 * G + h) * kHeadDim + d] +
+                    red[(2 * G + h) * kHeadDim + d] + red[(3 * G + h) * kHeadDim + d];
     const int head = kvh * G + h;
     if (n_chunks_b == 1) {
       float y = o / ml[h][1];
@@ -252,7 +332,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
 // are formed once (chunks spread over the threads) and shared through LDS; the per-dim sums then
 // issue their loads independently of each other.
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
-  __shared__ float w_s[kMaxChunks];
+  __shared__ float w_s[kDecodeMaxChunks];
   __shared__ float red[2];
   const int head = blockIdx.x;
   const int b = blockIdx.y;

@@ -49,6 +49,10 @@ struct PrefillParams {
   RopeTableH rope;
 };
 
+// Split-KV decode: keys per chunk (one workgroup each), and the most chunks one sequence may have.
+constexpr int kDecodeChunkKeys = 1024;
+constexpr int kDecodeMaxChunks = 2048;
+
 struct DecodeParams {
   const uint16_t* q_new;
   const uint16_t* k_new;
