@@ -202,6 +202,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   float m_ref = 0.f;          // bf16-representable softmax reference (log2 units), per query
   bool m_valid = false;       // set once the query has seen an unmasked key
   bf16x8 qm = bf16x8{};       // B operand of the 9th step
+  // The reference is free as long as exp2 stays in range: it is 0 unless the first tile's maximum
+  // lies outside [-32, 32] or a later tile forces a rescale, and while it is 0 on every lane of
+  // the wave the 9th step would add zero and is skipped.
+  bool need_ref = false;      // wave-uniform
 
   f32x16 o[4];
 #pragma unroll
@@ -227,8 +231,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     for (int st = 0; st < 8; ++st)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(rd_k(par, st, kb), qf[st], s[kb]);
+    if (need_ref) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(one_op, qm, s[kb]);
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(one_op, qm, s[kb]);
+    }
   };
   auto mask_tile = [&](int j, f32x16 (&s)[2]) {
     const int kt = k_begin + j * kNk;
@@ -246,8 +252,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
   // Softmax weights of the current tile: P = exp2(S) (S already has the reference subtracted).
   // Unless a lane's tile sum exceeds 2^64 (or the query has no reference yet) nothing needs
-  // rescaling; otherwise the slow path raises the reference to the tile maximum, rescales l and O,
-  // redoes P, and moves the already computed next-tile scores to the new reference.
+  // rescaling; otherwise the slow path sets the reference (0 for a first tile whose maximum lies
+  // in [-32, 32], else the running maximum), rescales l and O, redoes P, and moves the already
+  // computed next-tile scores to the new reference.
   auto slow_path = [&](f32x16 (&s)[2], f32x16 (&sn)[2], u32x4 (&pk)[4], float& rs) {
     float mx = s[0][0];
 #pragma unroll
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
                                                      false, false);
     mx = fmaxf(mx, __uint_as_float(hi ? sw[0] : sw[1])) + m_ref;  // tile maximum, log2 units
     const bool has = mx > -INFINITY;
-    float m_new = m_valid ? fmaxf(m_ref, mx) : mx;
+    float m_new = m_valid ? fmaxf(m_ref, mx) : (fabsf(mx) <= 32.f ? 0.f : mx);
     m_new = has || m_valid ? bf16lo(pack_bf16(m_new, 0.f)) : m_ref;
     const float alpha = m_valid ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
     const float delta = m_ref - m_new;
@@ -285,11 +292,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     m_valid = m_valid || has;
     qm = hi ? bf16x8{} : bf16x8{(__bf16)(-m_new), (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f,
                                 (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+    need_ref = __builtin_amdgcn_ballot_w64(m_ref != 0.f) != 0;
   };
 
-  // One iteration j >= 1 (buffer parity PAR = j & 1): the 34 MFMAs (PV of tile j-1 with its
-  // weights, then QK^T of tile j+1) are issued one by one, each followed by one quarter-pair of this
-  // tile's softmax (two exponentials, or a pack and a row-sum step), which runs in the MFMA shadow.
+  // One iteration j >= 1 (buffer parity PAR = j & 1): the 32 (34 with the 9th step) MFMAs (PV of
+  // tile j-1 with its weights, then QK^T of tile j+1) are issued one by one, each followed by a slice of this tile's
+  // softmax (an exponential, plus a pack and a row-sum step every other slot), which runs in the
+  // MFMA shadow.
   auto iter = [&](int j, auto par_c, f32x16 (&sc)[2], f32x16 (&sn)[2], u32x4 (&pk_prev)[4],
                   u32x4 (&pk_cur)[4]) {
     constexpr int PAR = decltype(par_c)::value;
@@ -325,20 +334,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         }
       } else {
         const int kb = i - 32;
-        sn[kb] = mfma32(one_op, qm, sn[kb]);
+        if (need_ref) sn[kb] = mfma32(one_op, qm, sn[kb]);
       }
-      // vector work on this tile's scores
+      // vector work on this tile's scores: one exponential per slot, the pack and row-sum step of
+      // a pair in the slot of its second score
       if (i < 32) {
-        const int k = i >> 1;                // pair of scores
-        const int kb = k >> 3, r = 2 * (k & 7);
-        if ((i & 1) == 0) {
-          e[2 * k] = __builtin_amdgcn_exp2f(sc[kb][r]);
-          e[2 * k + 1] = __builtin_amdgcn_exp2f(sc[kb][r + 1]);
-        } else {
-          const uint32_t w = pack_bf16(e[2 * k], e[2 * k + 1]);
+        e[i] = __builtin_amdgcn_exp2f(sc[i >> 4][i & 15]);
+        if (i & 1) {
+          const int k = i >> 1;  // pair of scores
+          uint32_t w = pack_bf16(e[i - 1], e[i]);
+          float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
+                                                     part[k & 3], false);
+          // pins the pair's work to this slot: the compiler would otherwise sink it past the
+          // branch around the 9th step, out of the MFMA shadow
+          asm volatile("" : "+v"(w), "+v"(ps));
           pk_cur[k >> 2][k & 3] = w;
-          part[k & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
-                                                        part[k & 3], false);
+          part[k & 3] = ps;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
