@@ -302,8 +302,8 @@ zg_status zg_gemm_bf16(int64_t M, int32_t N, int32_t K, const void* x_bf16, cons
     return fail(ZG_ERR_SHAPE, "M=%lld N=%d K=%d: need M >= 1, N %% 8 == 0, K %% 64 == 0",
                 (long long)M, N, K);
   if (y_bf16 && ldy < N) return fail(ZG_ERR_SHAPE, "ldy=%lld < N=%d", (long long)ldy, N);
-  if (((M + 127) / 128) * ((N + 127) / 128) >= (int64_t(1) << 31))
-    return fail(ZG_ERR_SHAPE, "problem too large");
+  if (K > (1 << 20) || ((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31))
+    return fail(ZG_ERR_SHAPE, "problem too large (K <= 2^20, fewer than 2^31 tiles of 256 x 256)");
   if (!aligned16(x_bf16) || !aligned16(w_bf16)) return fail(ZG_ERR_SHAPE, "x and w must be 16-byte aligned");
   zg::GemmParams p{static_cast<const uint16_t*>(x_bf16), static_cast<const uint16_t*>(w_bf16),
                    residual, static_cast<uint16_t*>(y_bf16), ldy, M, N, K};

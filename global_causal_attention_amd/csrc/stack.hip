@@ -51,103 +51,147 @@ hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s) {
 
 // ---------------------------------------------------------------------------------------------
 // GEMM: Y[m, n] = sum_k X[m, k] W[n, k]. Both operands are K-contiguous, so each MFMA operand lane
-// reads 16 contiguous bytes of a row from LDS. 128 x 128 tile per 256-thread workgroup, each wave a
-// 64 x 64 quadrant of 2 x 2 v_mfma_f32_32x32x16_bf16 blocks; K advances 64 per stage with register
-// prefetch and two LDS buffers.
+// reads 16 contiguous bytes of a staged row. One workgroup of 4 waves (one per SIMD) computes a
+// 256 x 256 tile; each wave owns a 128 x 128 quadrant of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks, so
+// every operand read from LDS feeds four MFMAs. K advances 64 per stage: the stage's 256-row X and
+// W slabs (128 bytes per row) stream into LDS by buffer_load ... lds, double-buffered, one barrier
+// per stage. A staged row keeps its eight 16-byte chunks XOR-swizzled by (row mod 8), so the
+// 32-row operand reads are bank-conflict-free; the DMA realises the swizzle by permuting the
+// global addresses of the lanes (the LDS side of one DMA instruction is 1 KB of consecutive
+// bytes = 8 whole rows). Rows past M or N read as zeros through the buffer range check.
+// Tiles are ordered for L2 reuse: workgroup i runs on XCD i mod 8, so each XCD is given a
+// contiguous range of tiles, walked in groups of 8 m-tiles sharing one n-tile column at a time.
 namespace {
-constexpr int kGT = 128;          // tile M and N
-constexpr int kGK = 64;           // K per stage
-constexpr int kGRow = 144;        // LDS bytes per 64-element row (+16 pad, conflict-free)
-constexpr int kGTile = kGT * kGRow;
-constexpr int kGBuf = 2 * kGTile;
+constexpr int kGBM = 256;                   // tile M
+constexpr int kGBN = 256;                   // tile N
+constexpr int kGBK = 64;                    // K per stage
+constexpr int kGThreads = 256;              // 4 waves
+constexpr int kGRowB = 2 * kGBK;            // 128 bytes per staged row
+constexpr int kGTileA = kGBM * kGRowB;      // 32 KB
+constexpr int kGStage = kGTileA + kGBN * kGRowB;
+constexpr int kGLds = 2 * kGStage;          // 128 KB
+constexpr int kGGroupM = 8;
 
 __device__ __forceinline__ f32x16 mfma32g(const bf16x8 a, const bf16x8 b, const f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 }  // namespace
 
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int n_tiles_n = (p.N + kGT - 1) / kGT;
-  const int64_t tm = blockIdx.x / n_tiles_n;
-  const int tn = blockIdx.x - (int)(tm * n_tiles_n);
-  const int64_t m0 = tm * kGT;
-  const int n0 = tn * kGT;
-  const int wm = (wave >> 1) * 64;
-  const int wn = (wave & 1) * 64;
 
-  // loader: each thread moves 4 x 16 B of X and of W per stage: row = tid / 2, 64-byte half.
-  const int lrow = tid >> 1;
-  const int lhalf = tid & 1;
-  const bool xrow_ok = m0 + lrow < p.M;
-  const bool wrow_ok = n0 + lrow < p.N;
-  const uint16_t* xsrc = p.x + (xrow_ok ? (m0 + lrow) : 0) * (int64_t)p.K + 32 * lhalf;
-  const uint16_t* wsrc = p.w + (int64_t)(wrow_ok ? (n0 + lrow) : 0) * p.K + 32 * lhalf;
-  u32x4 px[4], pw[4];
-  auto load = [&](int k0) {
+  // ---- tile of this workgroup
+  const int n_tn = (p.N + kGBN - 1) / kGBN;
+  const int64_t n_tm = (p.M + kGBM - 1) / kGBM;
+  const int64_t n_tiles = n_tm * n_tn;
+  int64_t t = blockIdx.x;
+  if (n_tiles % 8 == 0) t = (t % 8) * (n_tiles / 8) + t / 8;
+  const int64_t per_group = (int64_t)kGGroupM * n_tn;
+  const int64_t grp = t / per_group;
+  const int64_t first_m = grp * kGGroupM;
+  const int gm = (int)min((int64_t)kGGroupM, n_tm - first_m);
+  const int64_t rr = t - grp * per_group;
+  const int64_t m0 = (first_m + rr % gm) * kGBM;
+  const int n0 = (int)(rr / gm) * kGBN;
+
+  // ---- stage DMA: wave w moves row groups 8w .. 8w+7 (8 rows = 1 KB each) of both slabs
+  const uint32_t rowb = (uint32_t)p.K * 2;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.x + m0 * p.K), 0, (int)(min(p.M - m0, (int64_t)kGBM) * rowb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.w + (int64_t)n0 * p.K), 0, (int)(min(p.N - n0, kGBN) * rowb), 0x00020000);
+  const uint32_t voff = (lane >> 3) * rowb + 16 * ((lane & 7) ^ (lane >> 3));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  auto dma_stage = [&](int buf, int k0) {
+    const uint32_t base = lds0 + buf * kGStage + wave * 8 * 1024;
+    const uint32_t s0 = wave * 64 * rowb + 2 * k0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      px[j] = xrow_ok ? *reinterpret_cast<const u32x4*>(xsrc + k0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-      pw[j] = wrow_ok ? *reinterpret_cast<const u32x4*>(wsrc + k0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t soff = s0 + 8 * i * rowb;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   ::"s"(base + i * 1024), "v"(voff), "s"(ra), "s"(soff) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   ::"s"(base + kGTileA + i * 1024), "v"(voff), "s"(rb), "s"(soff) : "memory", "m0");
     }
   };
-  auto store = [&](int buf) {
-    unsigned char* xs = smem + buf * kGBuf;
-    unsigned char* ws = xs + kGTile;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(xs + lrow * kGRow + 64 * lhalf + 16 * j) = px[j];
-      *reinterpret_cast<u32x4*>(ws + lrow * kGRow + 64 * lhalf + 16 * j) = pw[j];
-    }
-  };
 
-  f32x16 acc[2][2];
+  // ---- operand reads: row (quadrant + 32 i + l32), chunk (2 ks + hi) ^ (row mod 8)
+  const int wm = (wave >> 1) * 128;
+  const int wn = (wave & 1) * 128;
+  int a_off[4], b_off[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  const int n_k = p.K / kGK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int it = 0; it < n_k; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_k) load((it + 1) * kGK);
-    const unsigned char* xs = smem + buf * kGBuf;
-    const unsigned char* ws = xs + kGTile;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 a[2], bb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8*>(xs + (wm + 32 * i + l32) * kGRow + 32 * ks + 16 * hi);
-        bb[i] = *reinterpret_cast<const bf16x8*>(ws + (wn + 32 * i + l32) * kGRow + 32 * ks + 16 * hi);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32g(a[i], bb[j], acc[i][j]);
-    }
-    if (it + 1 < n_k) store(buf ^ 1);
-    __syncthreads();
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c = 16 * ((2 * ks + hi) ^ (l32 & 7));
+    a_off[ks] = (wm + l32) * kGRowB + c;
+    b_off[ks] = kGTileA + (wn + l32) * kGRowB + c;
   }
 
-  // epilogue: lane holds column n = l32 of each 32x32 block, rows 8*(r/4) + 4*hi + r%4
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int n_k = p.K / kGBK;
+  dma_stage(0, 0);
+  for (int it = 0; it < n_k; ++it) {
+    // this wave's DMA of stage it has landed; the barrier publishes every wave's and guarantees
+    // that all reads of the other buffer (stage it - 1) are done before it is refilled
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (it + 1 < n_k) dma_stage((it + 1) & 1, (it + 1) * kGBK);
+    const unsigned char* st = smem + (it & 1) * kGStage;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + 32 * kGRowB * i);
+        b[i] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + 32 * kGRowB * i);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32g(a[i], b[j], acc[i][j]);
+    }
+  }
+
+  // ---- epilogue: lane holds column n = l32 of each 32x32 block, rows 8*(r/4) + 4*hi + r%4.
+  // Full tiles issue a block's 16 residual loads before any add or store.
+  const bool full = m0 + kGBM <= p.M && n0 + kGBN <= p.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       const int n = n0 + wn + 32 * j + l32;
+      const int64_t mb = m0 + wm + 32 * i + 4 * hi;
+      if (full) {
+        if (p.residual) {
+          float* rp = p.residual + mb * p.N + n;
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = rp[(int64_t)(8 * (r >> 2) + (r & 3)) * p.N];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) rp[(int64_t)(8 * (r >> 2) + (r & 3)) * p.N] = v[r] + acc[i][j][r];
+        }
+        if (p.y) {
+          uint16_t* yp = p.y + mb * p.ldy + n;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            yp[(int64_t)(8 * (r >> 2) + (r & 3)) * p.ldy] = (uint16_t)(pack_bf16(acc[i][j][r], 0.f) & 0xffffu);
+        }
+        continue;
+      }
       if (n >= p.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int64_t m = mb + 8 * (r >> 2) + (r & 3);
         if (m >= p.M) continue;
         const float v = acc[i][j][r];
         if (p.residual) p.residual[m * p.N + n] += v;
@@ -157,12 +201,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
-  constexpr int lds = 2 * kGBuf;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
   if (e != hipSuccess) return e;
-  const int64_t tiles = ((p.M + kGT - 1) / kGT) * ((p.N + kGT - 1) / kGT);
-  hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(256), lds, s, p);
+  const int64_t tiles = ((p.M + kGBM - 1) / kGBM) * ((p.N + kGBN - 1) / kGBN);
+  hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(kGThreads), kGLds, s, p);
   return hipGetLastError();
 }
 
