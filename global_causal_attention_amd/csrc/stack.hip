@@ -55,10 +55,10 @@ hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s) {
 // 256 x 256 tile; each wave owns a 128 x 128 quadrant of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks, so
 // every operand read from LDS feeds four MFMAs. K advances 64 per stage: the stage's 256-row X and
 // W slabs (128 bytes per row) stream into LDS by buffer_load ... lds, double-buffered, one barrier
-// per stage. A staged row keeps its eight 16-byte chunks XOR-swizzled by (row mod 8), so the
-// 32-row operand reads are bank-conflict-free; the DMA realises the swizzle by permuting the
-// global addresses of the lanes (the LDS side of one DMA instruction is 1 KB of consecutive
-// bytes = 8 whole rows). Rows past M or N read as zeros through the buffer range check.
+// per stage. A staged row keeps its eight 16-byte chunks XOR-swizzled by (row / 2 mod 8): two
+// 128-byte rows share one 256-byte bank window, so the 16 rows of one read pass then cover all 64
+// banks exactly once; the DMA realises the swizzle by permuting the global addresses of the lanes
+// (the LDS side of one DMA instruction is 1 KB of consecutive bytes = 8 whole rows). Rows past M or N read as zeros through the buffer range check.
 // Tiles are ordered for L2 reuse: workgroup i runs on XCD i mod 8, so each XCD is given a
 // contiguous range of tiles, walked in groups of 8 m-tiles sharing one n-tile column at a time.
 namespace {
@@ -106,7 +106,10 @@ void gemm_kernel(GemmParams p) {
       (void*)(p.x + m0 * p.K), 0, (int)(min(p.M - m0, (int64_t)kGBM) * rowb), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.w + (int64_t)n0 * p.K), 0, (int)(min(p.N - n0, kGBN) * rowb), 0x00020000);
-  const uint32_t voff = (lane >> 3) * rowb + 16 * ((lane & 7) ^ (lane >> 3));
+  // lane -> row (lane / 8) of an 8-row group, physical chunk lane % 8; in odd groups the row's
+  // swizzle has bit 2 set
+  const uint32_t voff0 = (lane >> 3) * rowb + 16 * ((lane & 7) ^ (lane >> 4));
+  const uint32_t voff1 = (lane >> 3) * rowb + 16 * ((lane & 7) ^ (lane >> 4) ^ 4);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   auto dma_stage = [&](int buf, int k0) {
     const uint32_t base = lds0 + buf * kGStage + wave * 8 * 1024;
@@ -114,6 +117,7 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t soff = s0 + 8 * i * rowb;
+      const uint32_t voff = (i & 1) ? voff1 : voff0;  // group 8 * wave + i: parity of i
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                    ::"s"(base + i * 1024), "v"(voff), "s"(ra), "s"(soff) : "memory", "m0");
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -121,13 +125,13 @@ void gemm_kernel(GemmParams p) {
     }
   };
 
-  // ---- operand reads: row (quadrant + 32 i + l32), chunk (2 ks + hi) ^ (row mod 8)
+  // ---- operand reads: row (quadrant + 32 i + l32), chunk (2 ks + hi) ^ (row / 2 mod 8)
   const int wm = (wave >> 1) * 128;
   const int wn = (wave & 1) * 128;
   int a_off[4], b_off[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int c = 16 * ((2 * ks + hi) ^ (l32 & 7));
+    const int c = 16 * ((2 * ks + hi) ^ ((l32 >> 1) & 7));
     a_off[ks] = (wm + l32) * kGRowB + c;
     b_off[ks] = kGTileA + (wn + l32) * kGRowB + c;
   }
