@@ -55,7 +55,8 @@ hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s) {
 // 256 x 256 tile; each wave owns a 128 x 128 quadrant of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks, so
 // every operand read from LDS feeds four MFMAs. K advances 64 per stage: the stage's 256-row X and
 // W slabs (128 bytes per row) stream into LDS by buffer_load ... lds, double-buffered, one barrier
-// per stage. A staged row keeps its eight 16-byte chunks XOR-swizzled by (row / 2 mod 8): two
+// per stage; within a stage the operands of the next 16-deep step are read while the 16 MFMAs of
+// the current one run. A staged row keeps its eight 16-byte chunks XOR-swizzled by (row / 2 mod 8): two
 // 128-byte rows share one 256-byte bank window, so the 16 rows of one read pass then cover all 64
 // banks exactly once; the DMA realises the swizzle by permuting the global addresses of the lanes
 // (the LDS side of one DMA instruction is 1 KB of consecutive bytes = 8 whole rows). Rows past M or N read as zeros through the buffer range check.
@@ -64,13 +65,25 @@ hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s) {
 namespace {
 constexpr int kGBM = 256;                   // tile M
 constexpr int kGBN = 256;                   // tile N
-constexpr int kGBK = 64;                    // K per stage
+constexpr int kGBK = 64;                    // K per stage (32 or 64)
+constexpr int kGNBuf = 2;                   // stages resident in LDS
 constexpr int kGThreads = 256;              // 4 waves
-constexpr int kGRowB = 2 * kGBK;            // 128 bytes per staged row
-constexpr int kGTileA = kGBM * kGRowB;      // 32 KB
+constexpr int kGRowB = 2 * kGBK;            // bytes per staged row
+constexpr int kGChunks = kGRowB / 16;       // 16-byte chunks per staged row
+constexpr int kGRowsPerDma = 1024 / kGRowB; // rows filled by one DMA instruction (1 KB)
+constexpr int kGDmaPerSlab = kGBM / kGRowsPerDma / 4;  // DMA instructions per wave per slab
+constexpr int kGTileA = kGBM * kGRowB;
 constexpr int kGStage = kGTileA + kGBN * kGRowB;
-constexpr int kGLds = 2 * kGStage;          // 128 KB
+constexpr int kGLds = kGNBuf * kGStage;
 constexpr int kGGroupM = 8;
+static_assert(kGBK == 32 || kGBK == 64, "stage depth");
+static_assert(kGLds <= 160 * 1024, "LDS budget");
+
+// Physical chunk of logical chunk c in staged row r: the rows sharing one 256-byte bank window
+// differ in (r mod (256 / row bytes)), the XOR term enumerates the rest of a 16-row read pass.
+__device__ __forceinline__ int gswz(int r) {
+  return kGBK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
 
 __device__ __forceinline__ f32x16 mfma32g(const bf16x8 a, const bf16x8 b, const f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -100,24 +113,26 @@ void gemm_kernel(GemmParams p) {
   const int64_t m0 = (first_m + rr % gm) * kGBM;
   const int n0 = (int)(rr / gm) * kGBN;
 
-  // ---- stage DMA: wave w moves row groups 8w .. 8w+7 (8 rows = 1 KB each) of both slabs
+  // ---- stage DMA: wave w fills DMA groups [w, w + 1) * kGDmaPerSlab of each slab
   const uint32_t rowb = (uint32_t)p.K * 2;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.x + m0 * p.K), 0, (int)(min(p.M - m0, (int64_t)kGBM) * rowb), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.w + (int64_t)n0 * p.K), 0, (int)(min(p.N - n0, kGBN) * rowb), 0x00020000);
-  // lane -> row (lane / 8) of an 8-row group, physical chunk lane % 8; in odd groups the row's
-  // swizzle has bit 2 set
-  const uint32_t voff0 = (lane >> 3) * rowb + 16 * ((lane & 7) ^ (lane >> 4));
-  const uint32_t voff1 = (lane >> 3) * rowb + 16 * ((lane & 7) ^ (lane >> 4) ^ 4);
+  // lane -> row lane / kGChunks of the DMA group, physical chunk lane % kGChunks; the logical
+  // chunk depends on the group's parity only through gswz (64-deep stages, odd groups)
+  const int dr = lane / kGChunks;
+  const int dp = lane % kGChunks;
+  const uint32_t voff0 = dr * rowb + 16 * (dp ^ gswz(dr));
+  const uint32_t voff1 = dr * rowb + 16 * (dp ^ gswz(dr + kGRowsPerDma));
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   auto dma_stage = [&](int buf, int k0) {
-    const uint32_t base = lds0 + buf * kGStage + wave * 8 * 1024;
-    const uint32_t s0 = wave * 64 * rowb + 2 * k0;
+    const uint32_t base = lds0 + buf * kGStage + wave * kGDmaPerSlab * 1024;
+    const uint32_t s0 = wave * kGDmaPerSlab * kGRowsPerDma * rowb + 2 * k0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t soff = s0 + 8 * i * rowb;
-      const uint32_t voff = (i & 1) ? voff1 : voff0;  // group 8 * wave + i: parity of i
+    for (int i = 0; i < kGDmaPerSlab; ++i) {
+      const uint32_t soff = s0 + i * kGRowsPerDma * rowb;
+      const uint32_t voff = (i & 1) ? voff1 : voff0;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                    ::"s"(base + i * 1024), "v"(voff), "s"(ra), "s"(soff) : "memory", "m0");
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -125,13 +140,14 @@ void gemm_kernel(GemmParams p) {
     }
   };
 
-  // ---- operand reads: row (quadrant + 32 i + l32), chunk (2 ks + hi) ^ (row / 2 mod 8)
+  // ---- operand reads: row (quadrant + 32 i + l32), logical chunk 2 ks + hi
   const int wm = (wave >> 1) * 128;
   const int wn = (wave & 1) * 128;
-  int a_off[4], b_off[4];
+  constexpr int kSub = kGBK / 16;
+  int a_off[kSub], b_off[kSub];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int c = 16 * ((2 * ks + hi) ^ ((l32 >> 1) & 7));
+  for (int ks = 0; ks < kSub; ++ks) {
+    const int c = 16 * ((2 * ks + hi) ^ gswz(l32));
     a_off[ks] = (wm + l32) * kGRowB + c;
     b_off[ks] = kGTileA + (wn + l32) * kGRowB + c;
   }
@@ -143,26 +159,37 @@ void gemm_kernel(GemmParams p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   const int n_k = p.K / kGBK;
-  dma_stage(0, 0);
+  for (int s = 0; s < kGNBuf - 1 && s < n_k; ++s) dma_stage(s, s * kGBK);
   for (int it = 0; it < n_k; ++it) {
-    // this wave's DMA of stage it has landed; the barrier publishes every wave's and guarantees
-    // that all reads of the other buffer (stage it - 1) are done before it is refilled
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // this wave's DMA of stage it has landed (later stages may still be in flight); the barrier
+    // publishes every wave's and guarantees that all reads of the buffer refilled next (stage
+    // it - 1) are done
+    const int ahead = min(kGNBuf - 2, n_k - 1 - it);  // stages issued after stage it
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * kGDmaPerSlab) & 15) | (((4 * kGDmaPerSlab) >> 4) << 14));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * kGDmaPerSlab) & 15) | (((2 * kGDmaPerSlab) >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (it + 1 < n_k) dma_stage((it + 1) & 1, (it + 1) * kGBK);
-    const unsigned char* st = smem + (it & 1) * kGStage;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 a[4], b[4];
+    if (it + kGNBuf - 1 < n_k) dma_stage((it + kGNBuf - 1) % kGNBuf, (it + kGNBuf - 1) * kGBK);
+    const unsigned char* st = smem + (it % kGNBuf) * kGStage;
+    // operands of step ks + 1 are read while the 16 MFMAs of step ks run
+    bf16x8 a[2][4], b[2][4];
+    auto read_ops = [&](int ks) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + 32 * kGRowB * i);
-        b[i] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + 32 * kGRowB * i);
+        a[ks & 1][i] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + 32 * kGRowB * i);
+        b[ks & 1][i] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + 32 * kGRowB * i);
       }
+    };
+    read_ops(0);
+#pragma unroll
+    for (int ks = 0; ks < kSub; ++ks) {
+      if (ks + 1 < kSub) read_ops(ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32g(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32g(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
