@@ -10,9 +10,15 @@ softmax on bf16 MFMA, sigmoid gate. value = B*T / (time of one block) in tokens/
 Also measured in the same run (reported beside the headline):
   * the B=64 decode step over a 128-slot ring (local layer) and a linear cache with context lengths
     uniform on [8192, 65536] (global layer), cold caches, as GB/s of KV read against HBM peak;
+  * one gated local and one global layer at B=1, T=262144 (base 1e7), against the HBM and MFMA
+    rooflines;
+  * the 32-layer attention stack with projections at B=1, T=65536 (27 gated local + 5 global
+    layers, hidden 4096, N(0, 0.02) weights), as tokens/s and useful TFLOP/s with a per-component
+    breakdown;
   * the oracle (fp64 NumPy on the host cores) on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long]
+                       [--no-stack]
 Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
@@ -52,6 +58,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-reps", type=int, default=20)
+    ap.add_argument("--no-long", action="store_true", help="skip the B=1, T=262144 layers")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer stack")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -128,7 +136,10 @@ def main():
     # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record (null if the kernels
     # changed since it was taken)
     from global_causal_attention_amd.counters import lookup_traffic
-    parts = [lookup_traffic("prefill_kernel<4, false>"), lookup_traffic("kprep_kernel")]
+    grid_prefill = ((T + 63) // 64) * B * HKV * 512     # threads: 64-query tiles x (b, kv head)
+    grid_kprep = ((B * T * HKV + 127) // 128) * 256      # threads: 128 key rows per block
+    parts = [lookup_traffic("prefill_kernel<4, false>", grid_prefill),
+             lookup_traffic("kprep_kernel", grid_kprep)]
     glo_traffic = None if None in parts else sum(parts)
     result = {
         "metric": "gated-SWA/global attn prefill tokens/s + %MFMA peak; decode HBM GB/s %peak",
@@ -170,6 +181,10 @@ def main():
 
     if not args.no_decode:
         result["decode"] = bench_decode(torch, zg, si, dev, stream, args.decode_reps)
+    if not args.no_long:
+        result["long_context"] = bench_long(torch, zg, si, dev, stream)
+    if not args.no_stack:
+        result["stack"] = bench_stack(torch, zg, si, dev, stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, si)
@@ -233,6 +248,107 @@ def bench_decode(torch, zg, si, dev, stream, reps):
                                  "decode_attn_kernel<4> + decode_combine_kernel)"}
     del x, flush
     return res
+
+
+def _time(torch, stream, fn, reps, warm=1):
+    """Median of `reps` timed calls (HIP events on the launch stream) after `warm` untimed ones."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def bench_long(torch, zg, si, dev, stream):
+    """B=1, T=262144: one gated local layer (W=128) and one global layer, RoPE base 1e7."""
+    Tl = 262144
+    log(f"[bench] long context: building B=1 T={Tl} layer inputs")
+    x = si.prefill_layer(si.generator(1003, device="cuda"), 1, Tl, HQ, HKV, D, gated=True,
+                         device="cuda")
+    out = torch.empty_like(x["q"])
+    res = {"workload": f"B=1, T={Tl}, Hq=32 Hkv=8 D=128, rot 42, base 1e7"}
+    for name, win in (("swa", W), ("global", 0)):
+        cfg = zg.AttnConfig(window=win, gated=win > 0, rope_base=1e7)
+        ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, 1, Tl), dtype=torch.uint8, device=dev)
+        fn = lambda: zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"] if win else None,
+                                        out=out, workspace=ws)
+        ms = _time(torch, stream, fn, 5 if win else 2)
+        flop = HQ * n_pairs(Tl, win) * 4 * D
+        r = {"ms_median": round(ms, 3), "tokens_per_s": round(Tl / (ms * 1e-3), 1),
+             "TFLOPs_useful": round(flop / (ms * 1e-3) / 1e12, 2)}
+        if win:
+            nbytes = Tl * (HQ * D * 2 * 3 + HKV * D * 2 * 2)
+            r.update({"min_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)})
+        else:
+            r["mfma_frac"] = round(flop / (ms * 1e-3) / MFMA_BF16_PEAK, 4)
+        res[name] = r
+        log(f"[bench] T={Tl} {name}: {ms:.3f} ms")
+        del ws
+    del x, out
+    return res
+
+
+def bench_stack(torch, zg, si, dev, stream, n_layers=32, Ts=65536, hidden=4096):
+    """The attention-only stack with projections: x <- x + o_proj(attn(RMSNorm(x))) for 32 layers,
+    global at layers 6, 12, 18, 24, 30 (ungated, full causal), gated W=128 elsewhere; base 1e7.
+    One untimed pass, then the median of two timed passes; per-layer events give the breakdown."""
+    log(f"[bench] stack: {n_layers} layers, T={Ts}, hidden {hidden}")
+    gen = si.generator(1004, device="cuda")
+    x = si.stack_input(gen, 1, Ts, hidden, device="cuda")
+    layers = []
+    for l in range(1, n_layers + 1):
+        g = l % 6 == 0
+        w = si.stack_layer_weights(gen, hidden, HQ, HKV, D, is_global=g, device="cuda")
+        parts = [w["wq"], w["wk"], w["wv"]] + ([] if g else [w["wg"]])
+        layers.append((g, torch.cat(parts, 0).contiguous(), w["wo"]))
+        del w, parts
+    cfgs = {False: zg.AttnConfig(window=W, gated=True, rope_base=1e7),
+            True: zg.AttnConfig(window=0, gated=False, rope_base=1e7)}
+    ws = torch.empty(max(zg.zg_attn_layer_workspace_bytes(c, 1, Ts) for c in cfgs.values()),
+                     dtype=torch.uint8, device=dev)
+
+    def one_pass(evs=None):
+        for i, (g, wqkvg, wo) in enumerate(layers):
+            zg.zg_attn_layer(cfgs[g], x, wqkvg, wo, workspace=ws)
+            if evs is not None:
+                evs[i + 1].record(stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(2):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
+        evs[0].record(stream)
+        one_pass(evs)
+        torch.cuda.synchronize()
+        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n_layers)]
+        runs.append((sum(per), per))
+    runs.sort(key=lambda r: r[0])
+    total, per = runs[0]
+    n_glob = sum(1 for g, _, _ in layers if g)
+    t_glob = sum(p for p, (g, _, _) in zip(per, layers) if g)
+    t_loc = total - t_glob
+    # useful FLOP: projections (2 per weight per token) + attention (4*D per (head, key) pair)
+    proj = sum(2 * Ts * (wqkvg.numel() + wo.numel()) for _, wqkvg, wo in layers)
+    att = sum(HQ * n_pairs(Ts, 0 if g else W) * 4 * D for g, _, _ in layers)
+    del layers, ws, x
+    return {"workload": f"B=1, T={Ts}, hidden {hidden}, {n_layers} layers ({n_glob} global), "
+                        f"N(0, 0.02) bf16 weights, fp32 residual, base 1e7",
+            "ms": round(total, 2), "tokens_per_s": round(Ts / (total * 1e-3), 1),
+            "useful_flop": proj + att,
+            "TFLOPs_useful": round((proj + att) / (total * 1e-3) / 1e12, 1),
+            "mfma_frac": round((proj + att) / (total * 1e-3) / MFMA_BF16_PEAK, 4),
+            "local_layer_ms": round(t_loc / (n_layers - n_glob), 3),
+            "global_layer_ms": round(t_glob / n_glob, 3)}
 
 
 def cpu_baseline(torch, si, budget_s=12.0):
