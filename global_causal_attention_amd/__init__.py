@@ -15,7 +15,7 @@ from dataclasses import dataclass
 from ._abi import (LIB_PATH, ZgAttnCfg, ZgTokenStrides, load_library, ZG_OK, ZG_ERR_NULL,
                    ZG_ERR_SHAPE, ZG_ERR_UNSUPPORTED, ZG_ERR_WORKSPACE, ZG_ERR_HIP, EXPORTS)
 
-__all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_decode", "zg_kv_bytes",
+__all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached", "zg_attn_decode", "zg_kv_bytes",
            "zg_attn_prefill_workspace_bytes", "zg_attn_decode_workspace_bytes", "zg_rmsnorm",
            "zg_gemm_bf16", "zg_attn_layer", "zg_attn_layer_workspace_bytes", "zg_last_error",
            "load_library", "LIB_PATH", "EXPORTS"]
@@ -126,6 +126,54 @@ def zg_attn_prefill(cfg: AttnConfig, q, k, v, gate=None, *, q_norm_w=None, k_nor
     _check(load_library().zg_attn_prefill(
         ctypes.byref(c), B, T, pos0, _ptr(q), _ptr(k), _ptr(v), _ptr(gate if cfg.gated else None),
         _ptr(q_norm_w), _ptr(k_norm_w), ctypes.byref(strides), _ptr(out), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def zg_attn_prefill_cached_workspace_bytes(cfg: AttnConfig, B: int, T: int) -> int:
+    c = cfg.c()
+    return load_library().zg_attn_prefill_cached_workspace_bytes(ctypes.byref(c), B, T)
+
+
+def zg_attn_prefill_cached(cfg: AttnConfig, q, k, v, gate, k_cache, v_cache, *, pos0: int,
+                           q_norm_w=None, k_norm_w=None, out=None, workspace=None, stream=None):
+    """Chunked prefill through the decode caches (see include/zg_attn.h): the T new tokens sit at
+    positions pos0 .. pos0+T-1; k_cache/v_cache are [B, W, Hkv, 128] rings (window > 0) or
+    [B, stride, Hkv, 128] linear caches (window 0), read for earlier positions and updated with
+    the new tokens. Returns out [B, T, Hq, 128] bf16."""
+    import torch
+    bf = torch.bfloat16
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, bf)
+    if cfg.gated:
+        _need(gate, "gate", bf)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, bf)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    B, T, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=bf, device=q.device)
+    _need(out, "out", bf)
+    for w, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _need(w, n, torch.float32)
+    strides = ZgTokenStrides(_token_stride(q, "q", Hq * D), _token_stride(k, "k", 0),
+                             _token_stride(v, "v", 0),
+                             _token_stride(gate, "gate", 0) if cfg.gated else Hq * D,
+                             _token_stride(out, "out", 0))
+    if k.shape[:2] != (B, T) or v.shape[:2] != (B, T) or out.shape != (B, T, Hq, D):
+        raise ValueError("q/k/v/out shapes disagree")
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B:
+        raise ValueError("k_cache/v_cache shapes disagree")
+    need = zg_attn_prefill_cached_workspace_bytes(cfg, B, T)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    c = cfg.c()
+    _check(load_library().zg_attn_prefill_cached(
+        ctypes.byref(c), B, T, pos0, _ptr(q), _ptr(k), _ptr(v), _ptr(gate if cfg.gated else None),
+        _ptr(q_norm_w), _ptr(k_norm_w), ctypes.byref(strides), _ptr(k_cache), _ptr(v_cache),
+        k_cache.shape[1], _ptr(out), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 

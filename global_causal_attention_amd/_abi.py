@@ -31,6 +31,10 @@ EXPORTS = {
     "zg_attn_prefill_workspace_bytes": (_SZ, [_CFG, _I32, _I32]),
     "zg_attn_prefill": (ctypes.c_int, [_CFG, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P,
                                        ctypes.POINTER(ZgTokenStrides), _P, _P, _SZ, _P]),
+    "zg_attn_prefill_cached_workspace_bytes": (_SZ, [_CFG, _I32, _I32]),
+    "zg_attn_prefill_cached": (ctypes.c_int, [_CFG, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P,
+                                              ctypes.POINTER(ZgTokenStrides), _P, _P, _I64, _P,
+                                              _P, _SZ, _P]),
     "zg_attn_decode_workspace_bytes": (_SZ, [_CFG, _I32, _I64]),
     "zg_attn_decode": (ctypes.c_int, [_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _SZ, _P]),

@@ -158,6 +158,8 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     kp.T = T;
     kp.Hkv = (int32_t)Hkv;
     kp.pos0 = pos0;
+    kp.out_rows = T;
+    kp.out_row0 = 0;
     kp.eps = cfg->rms_eps;
     kp.rope = rt;
     const int G = (int)(Hq / Hkv);
@@ -188,6 +190,9 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     pp.pos0 = pos0;
     pp.window = window;
     pp.n_qtiles = (T + mq - 1) / mq;
+    pp.kv_rows = T;
+    pp.n_keys = T;
+    pp.qoff = 0;
     pp.eps = cfg->rms_eps;
     pp.scale_log2 = scale_log2(cfg);
     pp.rope = rt;
@@ -206,6 +211,163 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     return hip_status(zg::launch_prefill(pp, G, cfg->gated != 0, hs), "prefill launch");
   } catch (...) {
     return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_prefill");
+  }
+}
+
+size_t zg_attn_prefill_cached_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
+  if (!cfg || B < 1 || T < 1 || cfg->n_kv_heads < 1) return 0;
+  if (cfg->window <= 0) return 0;  // linear caches: keys are read from the cache itself
+  const size_t rows = (size_t)cfg->window - 1 + T;  // ring context + the new tokens
+  return 2 * align256((size_t)B * rows * cfg->n_kv_heads * kD * 2);
+}
+
+zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t pos0,
+                                 const void* q, const void* k, const void* v, const void* gate,
+                                 const float* q_norm_w, const float* k_norm_w,
+                                 const zg_token_strides* strides, void* k_cache, void* v_cache,
+                                 int64_t cache_stride, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  try {
+    zg_status st = check_cfg(cfg);
+    if (st != ZG_OK) return st;
+    if (!q || !k || !v || !out || !k_cache || !v_cache)
+      return fail(ZG_ERR_NULL, "q, k, v, out and the caches must be non-NULL");
+    if (cfg->gated && !gate) return fail(ZG_ERR_NULL, "gate must be non-NULL when gated=1");
+    if (B < 1 || T < 1) return fail(ZG_ERR_SHAPE, "B=%d T=%d must be >= 1", B, T);
+    if (pos0 < 0 || pos0 + T >= (int64_t(1) << 31))
+      return fail(ZG_ERR_SHAPE, "pos0=%lld out of range", (long long)pos0);
+    const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+    const int64_t W = cfg->window;
+    const bool ring = W > 0;
+    if (!ring && cache_stride < pos0 + T)
+      return fail(ZG_ERR_SHAPE, "linear cache: cache_stride=%lld < pos0 + T=%lld",
+                  (long long)cache_stride, (long long)(pos0 + T));
+    if ((int64_t)B * T * Hq * kD >= (int64_t(1) << 40))
+      return fail(ZG_ERR_SHAPE, "B*T*Hq*D too large");
+    zg_token_strides s{Hq * kD, Hkv * kD, Hkv * kD, Hq * kD, Hq * kD};
+    if (strides) s = *strides;
+    if (s.q < Hq * kD || s.k < Hkv * kD || s.v < Hkv * kD || s.out < Hq * kD ||
+        (cfg->gated && s.gate < Hq * kD) || (s.q | s.k | s.v | s.out) % 8 != 0 ||
+        (cfg->gated && s.gate % 8 != 0))
+      return fail(ZG_ERR_SHAPE, "token strides must be >= the packed row and multiples of 8");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(k_cache) || !aligned16(v_cache) || (cfg->gated && !aligned16(gate)) ||
+        (q_norm_w && !aligned16(q_norm_w)) || (k_norm_w && !aligned16(k_norm_w)))
+      return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    const int64_t row = Hkv * kD;  // elements per cache row
+    const int64_t n_ctx = ring ? std::min<int64_t>(pos0, W - 1) : pos0;
+    const int64_t n_keys = n_ctx + T;
+    if ((n_keys + 64) * 2 * std::max<int64_t>({s.q, row}) >= (int64_t(1) << 32))
+      return fail(ZG_ERR_UNSUPPORTED, "(context + T) * row bytes must stay below 4 GiB");
+    const size_t need = zg_attn_prefill_cached_workspace_bytes(cfg, B, T);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  workspace ? workspace_bytes : (size_t)0, need);
+    if (need > 0 && !aligned16(workspace)) return fail(ZG_ERR_SHAPE, "workspace must be 16-byte aligned");
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    uint16_t* kc = static_cast<uint16_t*>(k_cache);
+    uint16_t* vc = static_cast<uint16_t*>(v_cache);
+    // keys and values the attention reads: the linear cache itself, or a staging copy of the
+    // ring's context followed by the new tokens
+    uint16_t* ks = kc;
+    uint16_t* vs = vc;
+    int64_t kv_rows = cache_stride, row0 = pos0;
+    if (ring) {
+      ks = static_cast<uint16_t*>(workspace);
+      vs = ks + align256((size_t)B * (W - 1 + T) * row * 2) / 2;
+      kv_rows = n_keys;
+      row0 = n_ctx;
+      if (n_ctx > 0) {
+        for (int which = 0; which < 2; ++which) {
+          zg::RowCopyParams g{};
+          g.src = which ? vc : kc;
+          g.dst = which ? vs : ks;
+          g.src_bstride = W; g.dst_bstride = kv_rows;
+          g.src_row0 = pos0 - n_ctx; g.dst_row0 = 0;
+          g.src_stride = row; g.dst_stride = row;
+          g.src_ring = W; g.dst_ring = 0;
+          g.row_elems = (int32_t)row; g.rows = (int32_t)n_ctx; g.B = B;
+          st = hip_status(zg::launch_row_copy(g, hs), "ring gather launch");
+          if (st != ZG_OK) return st;
+        }
+      }
+    }
+    const zg::RopeTableH rt = rope_table(cfg);
+    zg::KPrepParams kp{};
+    kp.k = static_cast<const uint16_t*>(k);
+    kp.khat = ks;
+    kp.k_norm_w = k_norm_w;
+    kp.sk = s.k;
+    kp.B = B;
+    kp.T = T;
+    kp.Hkv = (int32_t)Hkv;
+    kp.pos0 = pos0;
+    kp.out_rows = kv_rows;
+    kp.out_row0 = row0;
+    kp.eps = cfg->rms_eps;
+    kp.rope = rt;
+    st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
+    if (st != ZG_OK) return st;
+    zg::RowCopyParams vcp{};
+    vcp.src = static_cast<const uint16_t*>(v);
+    vcp.dst = vs;
+    vcp.src_bstride = T; vcp.dst_bstride = kv_rows;
+    vcp.src_row0 = 0; vcp.dst_row0 = row0;
+    vcp.src_stride = s.v; vcp.dst_stride = row;
+    vcp.row_elems = (int32_t)row; vcp.rows = T; vcp.B = B;
+    st = hip_status(zg::launch_row_copy(vcp, hs), "v copy launch");
+    if (st != ZG_OK) return st;
+
+    const int G = (int)(Hq / Hkv);
+    const int mq = 256 / G;
+    zg::PrefillParams pp{};
+    pp.q = static_cast<const uint16_t*>(q);
+    pp.khat = ks;
+    pp.v = vs;
+    pp.gate = static_cast<const uint16_t*>(gate);
+    pp.out = static_cast<uint16_t*>(out);
+    pp.q_norm_w = q_norm_w;
+    pp.sq = s.q;
+    pp.sv = row;
+    pp.sg = s.gate;
+    pp.so = s.out;
+    pp.B = B;
+    pp.T = T;
+    pp.Hq = (int32_t)Hq;
+    pp.Hkv = (int32_t)Hkv;
+    pp.pos0 = pos0;
+    pp.window = (ring && W < n_keys) ? (int32_t)W : 0;  // a window covering every key is causal
+    pp.n_qtiles = (T + mq - 1) / mq;
+    pp.kv_rows = kv_rows;
+    pp.n_keys = (int32_t)n_keys;
+    pp.qoff = (int32_t)n_ctx;
+    pp.eps = cfg->rms_eps;
+    pp.scale_log2 = scale_log2(cfg);
+    pp.rope = rt;
+    if ((int64_t)pp.n_qtiles * B * Hkv >= (int64_t(1) << 31))
+      return fail(ZG_ERR_SHAPE, "grid too large");
+    st = hip_status(zg::launch_prefill_general(pp, G, cfg->gated != 0, hs), "prefill launch");
+    if (st != ZG_OK) return st;
+    if (ring) {
+      // the ring keeps the last W positions; written after the attention has read the context
+      const int64_t first = std::max<int64_t>(pos0, pos0 + T - W);
+      for (int which = 0; which < 2; ++which) {
+        zg::RowCopyParams w{};
+        w.src = which ? vs : ks;
+        w.dst = which ? vc : kc;
+        w.src_bstride = kv_rows; w.dst_bstride = W;
+        w.src_row0 = n_ctx + (first - pos0); w.dst_row0 = first;
+        w.src_stride = row; w.dst_stride = row;
+        w.src_ring = 0; w.dst_ring = W;
+        w.row_elems = (int32_t)row; w.rows = (int32_t)(pos0 + T - first); w.B = B;
+        st = hip_status(zg::launch_row_copy(w, hs), "ring write launch");
+        if (st != ZG_OK) return st;
+      }
+    }
+    return ZG_OK;
+  } catch (...) {
+    return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_prefill_cached");
   }
 }
 

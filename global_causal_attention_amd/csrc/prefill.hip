@@ -71,7 +71,8 @@ __global__ __launch_bounds__(256) void kprep_kernel(KPrepParams p) {
       x[i] *= (d >= rot && p.fold_w) ? p.fold_scale * p.fold_w[d] : p.fold_scale;
     }
   }
-  u32x4* d4 = reinterpret_cast<u32x4*>(p.khat + row * kHeadDim + 64 * half);
+  const int64_t orow = ((bt / p.T) * p.out_rows + p.out_row0 + t) * p.Hkv + h;
+  u32x4* d4 = reinterpret_cast<u32x4*>(p.khat + orow * kHeadDim + 64 * half);
 #pragma unroll
   for (int i = 0; i < 8; ++i) d4[i] = pack8(x + 8 * i);
 }
@@ -99,6 +100,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int r0 = qtile * MQ;
   const int T = p.T;
   const int W = p.window;
+  const int qoff = p.qoff;
 
   const int hg = wave % G;
   const int qb = wave / G;
@@ -140,10 +142,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     __syncthreads();
   }
 
-  // ---- key tile range of the workgroup
-  const int q_last = min(r0 + MQ, T) - 1;
+  // ---- key tile range of the workgroup (key rows; query row t is key row qoff + t)
+  const int q_last = qoff + min(r0 + MQ, T) - 1;
   int k_begin = 0;
-  if (W > 0) k_begin = max(0, r0 - W + 1) & ~(kNk - 1);
+  if (W > 0) k_begin = max(0, qoff + r0 - W + 1) & ~(kNk - 1);
   const int n_tiles = (q_last + 1 - k_begin + kNk - 1) / kNk;
 
   // ---- tile streaming: waves 0-3 bring K rows, waves 4-7 V rows, straight into chunk-swizzled
@@ -155,10 +157,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const bool v_loader = wave >= 4;
   const int wg = wave & 3;
   const int row_bytes = (int)((v_loader ? p.sv : (int64_t)p.Hkv * kHeadDim) * 2);
-  const uint16_t* slab = v_loader ? p.v + (int64_t)b * T * p.sv + (int64_t)kvh * kHeadDim
-                                  : p.khat + ((int64_t)b * T * p.Hkv + kvh) * kHeadDim;
+  const uint16_t* slab = v_loader ? p.v + (int64_t)b * p.kv_rows * p.sv + (int64_t)kvh * kHeadDim
+                                  : p.khat + ((int64_t)b * p.kv_rows * p.Hkv + kvh) * kHeadDim;
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, T * row_bytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, p.n_keys * row_bytes, 0x00020000);
   // lane -> (row (lane >> 4) of the 4-row group i, physical chunk lane & 15)
   auto dma_voff = [&](int i) -> uint32_t {
     const int row = 4 * i + (lane >> 4);  // row within the wave's 16 (swizzle uses row & 15)
@@ -211,7 +213,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float l_run = 0.f;
-  const int my_q = qbase + l32;
+  const int my_row = qbase + l32;   // query row
+  const int my_q = qoff + my_row;   // its key row
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   auto rd_k = [&](int par, int st, int kb) -> bf16x8 {
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
   auto mask_tile = [&](int j, f32x16 (&s)[2]) {
     const int kt = k_begin + j * kNk;
-    const bool need = (kt + kNk - 1 > qbase) || ((W > 0) && (kt < qbase + 31 - W + 1));
+    const bool need = (kt + kNk - 1 > qoff + qbase) || ((W > 0) && (kt < qoff + qbase + 31 - W + 1));
     if (need) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -416,10 +419,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   }
 
   // ---- epilogue: normalise, gate, round, store (one query per lane, 4 dims per store)
-  if (my_q < T) {
+  if (my_row < T) {
     const float l_tot = l_run + shfl_xor_f(l_run, 32);
     const float inv = 1.0f / l_tot;
-    const int64_t tok = (int64_t)b * T + my_q;
+    const int64_t tok = (int64_t)b * T + my_row;
     uint16_t* dst = p.out + tok * p.so + (int64_t)head * kHeadDim;
     const uint16_t* gsrc = GATED ? p.gate + tok * p.sg + (int64_t)head * kHeadDim : nullptr;
 #pragma unroll
@@ -444,6 +447,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Cache hand-off: copies of whole token rows between caches and staging buffers, 16 bytes per
+// lane (the pages' KV-cache layout: local layers a ring of the last window positions, global
+// layers one row per position; zh-TW translation page, section 2.3).
+__global__ __launch_bounds__(256) void row_copy_kernel(RowCopyParams p) {
+  const int lanes_per_row = p.row_elems / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_seq = (int64_t)p.rows * lanes_per_row;
+  if (i >= per_seq * p.B) return;
+  const int64_t b = i / per_seq;
+  const int64_t rem = i - b * per_seq;
+  const int64_t j = rem / lanes_per_row;
+  const int c = (int)(rem - j * lanes_per_row);
+  int64_t rs = p.src_row0 + j, rd = p.dst_row0 + j;
+  if (p.src_ring > 0) rs %= p.src_ring;
+  if (p.dst_ring > 0) rd %= p.dst_ring;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p.src + (b * p.src_bstride + rs) * p.src_stride + 8 * c);
+  *reinterpret_cast<u32x4*>(p.dst + (b * p.dst_bstride + rd) * p.dst_stride + 8 * c) = v;
+}
+
+hipError_t launch_row_copy(const RowCopyParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.B * p.rows * (p.row_elems / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(row_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 hipError_t launch_kprep(const KPrepParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.T * p.Hkv;
   const int64_t blocks = (rows + 127) / 128;
@@ -465,7 +495,12 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s) {
-  if (prefill_uses_swa(p.window, group, p.rope.half)) return launch_prefill_swa(p, gated, s);
+  if (p.qoff == 0 && p.kv_rows == p.T && prefill_uses_swa(p.window, group, p.rope.half))
+    return launch_prefill_swa(p, gated, s);
+  return launch_prefill_general(p, group, gated, s);
+}
+
+hipError_t launch_prefill_general(const PrefillParams& p, int group, bool gated, hipStream_t s) {
   switch (group * 2 + (gated ? 1 : 0)) {
     case 2: return launch_prefill_t<1, false>(p, s);
     case 3: return launch_prefill_t<1, true>(p, s);

@@ -452,6 +452,7 @@ static hipError_t launch_swa_t(const PrefillParams& p, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kSwaLds);
   if (e != hipSuccess) return e;
+  if (p.seg_steps < 1) return hipErrorInvalidValue;
   const int64_t n_seg = ((int64_t)p.T + 64 * p.seg_steps - 1) / (64 * p.seg_steps);
   const int64_t grid = n_seg * p.B * p.Hkv;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), kSwaLds, s, p);

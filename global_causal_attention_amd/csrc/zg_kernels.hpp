@@ -22,6 +22,9 @@ struct KPrepParams {
   int64_t sk;  // token stride of k (elements)
   int32_t B, T, Hkv;
   int64_t pos0;
+  // output rows: k_hat of (b, t) goes to row out_row0 + t of sequence b, sequences out_rows
+  // rows apart (out_rows = T, out_row0 = 0 for a packed [B, T, Hkv, 128] result)
+  int64_t out_rows, out_row0;
   float eps;
   RopeTableH rope;
   // Folding for the banded streaming kernel: when set, dims < rot_dim are multiplied by
@@ -44,6 +47,11 @@ struct PrefillParams {
   int32_t window;
   int32_t n_qtiles;
   int32_t seg_steps;  // banded kernel: 64-query steps per workgroup
+  // Keys: sequence b's k_hat and v rows start kv_rows rows apart; n_keys of them are valid, and
+  // query row t is key row qoff + t (rows before qoff are earlier positions from a cache).
+  // Plain prefill: kv_rows = n_keys = T, qoff = 0.
+  int64_t kv_rows;
+  int32_t n_keys, qoff;
   float eps;
   float scale_log2;  // softmax scale * log2(e)
   RopeTableH rope;
@@ -96,12 +104,30 @@ struct GemmParams {
   int32_t N, K;
 };
 
+// Row copies between token-major [B, rows, Hkv, 128] buffers (caches, staging): row j of
+// sequence b goes from src row src_row0 + j to dst row dst_row0 + j; a side whose ring > 0 takes
+// its row index modulo ring (a ring cache's slot).
+struct RowCopyParams {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t src_bstride, dst_bstride;  // rows per sequence
+  int64_t src_row0, dst_row0;
+  int64_t src_stride, dst_stride;    // elements per row (token stride)
+  int64_t src_ring, dst_ring;
+  int32_t row_elems;                 // elements copied per row (multiple of 8)
+  int32_t rows;                      // rows per sequence
+  int32_t B;
+};
+hipError_t launch_row_copy(const RowCopyParams& p, hipStream_t s);
+
 hipError_t launch_kprep(const KPrepParams& p, hipStream_t s);
 // True when launch_prefill takes the streaming kernel for short windows (which reads seg_steps and
 // expects keys prepared with KPrepParams::fold set).
 bool prefill_uses_swa(int window, int group, int rot_half);
 hipError_t launch_prefill_swa(const PrefillParams& p, bool gated, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s);
+// The general tiled kernel only (any window, key rows offset from query rows, unfolded keys).
+hipError_t launch_prefill_general(const PrefillParams& p, int group, bool gated, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);

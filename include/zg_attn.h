@@ -86,6 +86,33 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Chunked prefill through the decode caches: the T new tokens of every sequence sit at positions
+ * pos0 .. pos0+T-1, keys of earlier positions come from the caches, and the call leaves the new
+ * tokens' normalised, rotated keys and values in the caches, so decode (or a further chunk) can
+ * continue from pos0 + T. (zh-TW translation, section 2.3: local layers keep a fixed 128-token
+ * window, global layers the whole sequence.) Every sequence continues at the same pos0.
+ *   window W > 0 (ring): k_cache, v_cache [B, W, Hkv, D] bf16; position p in slot p % W. On entry
+ *            the slots hold positions max(0, pos0-W) .. pos0-1 (others are not read); on return
+ *            positions max(0, pos0+T-W) .. pos0+T-1. cache_stride is ignored.
+ *   window 0 (linear): k_cache, v_cache [B, cache_stride, Hkv, D] bf16; rows 0 .. pos0-1 hold the
+ *            earlier positions; rows pos0 .. pos0+T-1 are written; cache_stride >= pos0 + T.
+ *   q, k, v, gate, out, strides, norm weights: as for zg_attn_prefill (out = the T new rows).
+ * The result equals zg_attn_prefill over the whole sequence 0 .. pos0+T-1, rows pos0 .. pos0+T-1,
+ * up to rounding; pos0 = 0 with any cache contents is the plain prefill plus the cache fill.
+ *   workspace >= zg_attn_prefill_cached_workspace_bytes(cfg, B, T) (0 for linear caches: the
+ *   attention reads the cache; rings stage their W-1 context rows and the new rows).
+ * Errors as for prefill; linear cache_stride < pos0 + T -> ZG_ERR_SHAPE; (context + T) rows of
+ * more than 4 GiB per sequence -> ZG_ERR_UNSUPPORTED. */
+size_t zg_attn_prefill_cached_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T);
+
+zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t pos0,
+                                 const void* q, const void* k, const void* v, const void* gate,
+                                 const float* q_norm_w, const float* k_norm_w,
+                                 const zg_token_strides* strides, void* k_cache, void* v_cache,
+                                 int64_t cache_stride, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Decode: one new token per sequence, attending over a KV cache of normalised, rotated keys.
  * (zh-TW translation, section 2.3: local layers keep a fixed 128-token window, global layers keep
  * the whole sequence; decoding is memory-bandwidth bound.)

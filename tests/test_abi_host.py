@@ -101,3 +101,24 @@ def test_gemm_and_rmsnorm_reject_bad_arguments():
     assert lib.zg_gemm_bf16(16, 64, 128, 16, 16, None, 16, 32, None) == zg.ZG_ERR_SHAPE
     assert lib.zg_rmsnorm(4, 12, 16, None, 1e-6, 16, None) == zg.ZG_ERR_SHAPE
     assert lib.zg_rmsnorm(4, 128, None, None, 1e-6, 16, None) == zg.ZG_ERR_NULL
+
+
+def test_prefill_cached_rejects_bad_arguments():
+    lib = zg.load_library()
+    c = zg.AttnConfig(window=0, gated=False).c()
+    ws = 256
+    # linear cache shorter than pos0 + T
+    st = lib.zg_attn_prefill_cached(ctypes.byref(c), 1, 8, 100, 16, 16, 16, None, None, None, None,
+                                    16, 16, 100, 16, ws, 1 << 20, None)
+    assert st == zg.ZG_ERR_SHAPE
+    # missing cache
+    st = lib.zg_attn_prefill_cached(ctypes.byref(c), 1, 8, 0, 16, 16, 16, None, None, None, None,
+                                    None, 16, 100, 16, ws, 1 << 20, None)
+    assert st == zg.ZG_ERR_NULL
+    # ring caches need the staging workspace
+    cr = zg.AttnConfig(window=128, gated=False).c()
+    assert zg.zg_attn_prefill_cached_workspace_bytes(zg.AttnConfig(window=128, gated=False), 1, 8) > 0
+    assert zg.zg_attn_prefill_cached_workspace_bytes(zg.AttnConfig(window=0, gated=False), 1, 8) == 0
+    st = lib.zg_attn_prefill_cached(ctypes.byref(cr), 1, 8, 0, 16, 16, 16, None, None, None, None,
+                                    16, 16, 0, 16, None, 0, None)
+    assert st == zg.ZG_ERR_WORKSPACE
