@@ -15,10 +15,15 @@ Also measured in the same run (reported beside the headline):
   * the 32-layer attention stack with projections at B=1, T=65536 (27 gated local + 5 global
     layers, hidden 4096, N(0, 0.02) weights), as tokens/s and useful TFLOP/s with a per-component
     breakdown;
+  * chunked prefill through the decode caches: B=4 sequences continue with 2048 new tokens after
+    16384 cached positions, on a global layer (linear caches) and a gated local layer (rings);
+  * a context sweep at 262,144 tokens per step (T = 4K .. 256K, B = 256K / T): one local and one
+    global layer timed per T, and the 32-layer attention time of the all-global, 1:1, 3:1 and
+    ZGCM-1's 5:1 schedules (global at every 1st, 2nd, 4th, 6th layer);
   * the oracle (fp64 NumPy on the host cores) on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long]
-                       [--no-stack]
+                       [--no-stack] [--no-chunked] [--no-sweep] [--no-block]
 Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
@@ -60,6 +65,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=20)
     ap.add_argument("--no-long", action="store_true", help="skip the B=1, T=262144 layers")
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer stack")
+    ap.add_argument("--no-chunked", action="store_true", help="skip the chunked prefill")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the context sweep")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the timed 5:1 block (profiling the other workloads alone; value null)")
     args = ap.parse_args()
@@ -95,6 +102,10 @@ def main():
         result["long_context"] = bench_long(torch, zg, si, dev, stream)
     if not args.no_stack:
         result["stack"] = bench_stack(torch, zg, si, dev, stream)
+    if not args.no_chunked:
+        result["chunked_prefill"] = bench_chunked(torch, zg, si, dev, stream)
+    if not args.no_sweep:
+        result["context_sweep"] = bench_sweep(torch, zg, si, dev, stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, si)
@@ -353,6 +364,78 @@ def bench_stack(torch, zg, si, dev, stream, n_layers=32, Ts=65536, hidden=4096):
             "mfma_frac": round((proj + att) / (total * 1e-3) / MFMA_BF16_PEAK, 4),
             "local_layer_ms": round(t_loc / (n_layers - n_glob), 3),
             "global_layer_ms": round(t_glob / n_glob, 3)}
+
+
+def bench_chunked(torch, zg, si, dev, stream, Bc=4, ctx=16384, Tc=2048):
+    """Chunked prefill through the caches: each of Bc sequences has ctx positions in its caches and
+    continues with Tc new tokens (base 1e6). Cache contents are N(0,1) bf16 standing for
+    normalised, rotated keys and values; every timed call rewrites the same cache rows."""
+    log(f"[bench] chunked prefill: B={Bc}, {ctx} cached positions + {Tc} new")
+    gen = si.generator(1005, device="cuda")
+    x = si.prefill_layer(gen, Bc, Tc, HQ, HKV, D, gated=True, device="cuda")
+    out = torch.empty_like(x["q"])
+    res = {"workload": f"B={Bc}, {ctx} cached positions + {Tc} new tokens, Hq=32 Hkv=8 D=128, "
+                       f"base 1e6; global layer on linear caches, gated W=128 layer on rings"}
+    for name, win in (("global", 0), ("swa", W)):
+        rows = win if win else ctx + Tc
+        kc = si.randn_bf16(gen, (Bc, rows, HKV, D), device="cuda")
+        vc = si.randn_bf16(gen, (Bc, rows, HKV, D), device="cuda")
+        cfg = zg.AttnConfig(window=win, gated=win > 0, rope_base=ROPE_BASE)
+        need = zg.zg_attn_prefill_cached_workspace_bytes(cfg, Bc, Tc)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        fn = lambda: zg.zg_attn_prefill_cached(cfg, x["q"], x["k"], x["v"],
+                                               x["gate"] if win else None, kc, vc, pos0=ctx,
+                                               out=out, workspace=ws)
+        ms = _time(torch, stream, fn, 10)
+        if win:
+            pairs = Tc * win   # every new query sees a full window
+            nbytes = Bc * Tc * (HQ * D * 2 * 3 + HKV * D * 2 * 2) + Bc * min(Tc, win) * HKV * D * 2 * 2
+            r = {"ms_median": round(ms, 4), "hbm_frac": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4),
+                 "min_bytes": nbytes}
+        else:
+            pairs = Tc * ctx + Tc * (Tc + 1) // 2
+            flop = Bc * HQ * pairs * 4 * D
+            r = {"ms_median": round(ms, 4), "TFLOPs_useful": round(flop / (ms * 1e-3) / 1e12, 1),
+                 "mfma_frac": round(flop / (ms * 1e-3) / MFMA_BF16_PEAK, 4)}
+        r["tokens_per_s"] = round(Bc * Tc / (ms * 1e-3), 1)
+        res[name] = r
+        log(f"[bench] chunked {name}: {ms:.3f} ms")
+        del kc, vc, ws
+    del x, out
+    return res
+
+
+def bench_sweep(torch, zg, si, dev, stream, tokens=262144, n_layers=32):
+    """Attention-only context sweep at a fixed number of tokens per step: per T, one gated local
+    layer (W=128) and one global layer are timed (base 1e7); a schedule's 32-layer attention time
+    is n_local * t_local + n_global * t_global, with layer l global iff l % every == 0."""
+    res = {"workload": f"{tokens} tokens per step, B = {tokens} / T, Hq=32 Hkv=8 D=128, base 1e7",
+           "points": []}
+    schedules = {"all_global": 1, "1:1": 2, "3:1": 4, "5:1": 6}
+    for T_ in (4096, 8192, 16384, 32768, 65536, 131072, 262144):
+        Bs = tokens // T_
+        x = si.prefill_layer(si.generator(1006, device="cuda"), Bs, T_, HQ, HKV, D, gated=True,
+                             device="cuda")
+        out = torch.empty_like(x["q"])
+        t = {}
+        for name, win in (("local", W), ("global", 0)):
+            cfg = zg.AttnConfig(window=win, gated=win > 0, rope_base=1e7)
+            ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, Bs, T_), dtype=torch.uint8,
+                             device=dev)
+            fn = lambda: zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"] if win else None,
+                                            out=out, workspace=ws)
+            t[name] = _time(torch, stream, fn, 3 if win else 2)
+            del ws
+        del x, out
+        point = {"T": T_, "B": Bs, "local_ms": round(t["local"], 3), "global_ms": round(t["global"], 3)}
+        for sname, every in schedules.items():
+            n_g = n_layers // every  # layers 1..n_layers that are multiples of `every`
+            ms = (n_layers - n_g) * t["local"] + n_g * t["global"]
+            point[sname] = {"n_global": n_g, "ms": round(ms, 2), "tokens_per_s": round(tokens / (ms * 1e-3), 1)}
+        point["5:1_vs_all_global"] = round(point["all_global"]["ms"] / point["5:1"]["ms"], 3)
+        res["points"].append(point)
+        log(f"[bench] sweep T={T_}: local {t['local']:.3f} ms, global {t['global']:.3f} ms")
+    return res
 
 
 def cpu_baseline(torch, si, budget_s=12.0):
