@@ -15,6 +15,8 @@ for Math and Agentic Search"):
 * zh-CN tutorial page (agifrontier.github.io): the architecture paragraph (same formula and numbers).
 * English explainer page (paperglide.net): Fig. 3 and Fig. 4 captions, and the toy KV-entry count
   (window 4, 8 tokens, 4 SWA + 1 global layers: 24 vs 40 entries).
+* FP8: the E4M3 format the pages train their forward matrix multiplications in (zh-TW page §3.1,
+  hyper-parameters), used here for the decode KV cache (``fp8.py``).
 
 Parity status per function is listed in each module's header.
 """
@@ -22,9 +24,11 @@ from .attention import (rms_norm, rope_inv_freq, partial_rope, qk_prologue, key_
                         prefill, prefill_rows, attention_probs_row, decode)
 from .kv import kv_bytes, kv_entries, is_global_layer, global_layers
 from .stack import stack_layer, stack, layer_is_global
+from .fp8 import e4m3_values, round_e4m3, decode_fp8_cache
 
 __all__ = [
     "rms_norm", "rope_inv_freq", "partial_rope", "qk_prologue", "key_set", "prefill",
     "prefill_rows", "attention_probs_row", "decode", "kv_bytes", "kv_entries",
     "is_global_layer", "global_layers", "stack_layer", "stack", "layer_is_global",
+    "e4m3_values", "round_e4m3", "decode_fp8_cache",
 ]
