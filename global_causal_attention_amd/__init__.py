@@ -15,7 +15,7 @@ from dataclasses import dataclass
 from ._abi import (LIB_PATH, ZgAttnCfg, ZgTokenStrides, load_library, ZG_OK, ZG_ERR_NULL,
                    ZG_ERR_SHAPE, ZG_ERR_UNSUPPORTED, ZG_ERR_WORKSPACE, ZG_ERR_HIP, EXPORTS)
 
-__all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached", "zg_attn_decode", "zg_kv_bytes",
+__all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached", "zg_attn_decode", "zg_attn_decode_fp8", "zg_kv_to_fp8", "zg_kv_bytes",
            "zg_attn_prefill_workspace_bytes", "zg_attn_decode_workspace_bytes", "zg_rmsnorm",
            "zg_gemm_bf16", "zg_attn_layer", "zg_attn_layer_workspace_bytes", "zg_last_error",
            "load_library", "LIB_PATH", "EXPORTS"]
@@ -211,6 +211,51 @@ def zg_attn_decode(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_cache,
         _ptr(gate if cfg.gated else None), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(k_cache),
         _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def zg_attn_decode_fp8(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_cache, seqlens, *,
+                       max_seqlen: int, k_scale: float = 1.0, v_scale: float = 1.0, q_norm_w=None,
+                       k_norm_w=None, out=None, workspace=None, stream=None):
+    """One decode step over E4M3 caches (torch.float8_e4m3fn or uint8 tensors of the bf16 cache
+    shape; see include/zg_attn.h). Updates the caches in place, returns out [B, Hq, 128] bf16."""
+    import torch
+    bf = torch.bfloat16
+    for t, n in ((q_new, "q_new"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, bf)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float8_e4m3fn or uint8 device tensor")
+    _need(seqlens, "seqlens", torch.int32)
+    if cfg.gated:
+        _need(gate, "gate", bf)
+    B = q_new.shape[0]
+    if out is None:
+        out = torch.empty_like(q_new)
+    need = zg_attn_decode_workspace_bytes(cfg, B, max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_new.device)
+    c = cfg.c()
+    _check(load_library().zg_attn_decode_fp8(
+        ctypes.byref(c), B, k_cache.shape[1], max_seqlen, _ptr(q_new), _ptr(k_new), _ptr(v_new),
+        _ptr(gate if cfg.gated else None), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(k_cache),
+        _ptr(v_cache), float(k_scale), float(v_scale), _ptr(seqlens), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def zg_kv_to_fp8(src, scale: float = 1.0, out=None, stream=None):
+    """E4M3 copy of a bf16 device tensor (values / scale, nearest-even, saturating at +-448)."""
+    import torch
+    _need(src, "src", torch.bfloat16)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    if out is None:
+        out = torch.empty(src.shape, dtype=torch.float8_e4m3fn, device=src.device)
+    _check(load_library().zg_kv_to_fp8(_ptr(src), _ptr(out), src.numel(), float(scale),
+                                       _stream(stream)))
     return out
 
 

@@ -380,12 +380,12 @@ size_t zg_attn_decode_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int64_t
   return bytes;
 }
 
-zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
-                         int64_t max_seqlen, const void* q_new, const void* k_new,
-                         const void* v_new, const void* gate, const float* q_norm_w,
-                         const float* k_norm_w, void* k_cache, void* v_cache,
-                         const int32_t* seqlens, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+static zg_status decode_impl(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                             int64_t max_seqlen, const void* q_new, const void* k_new,
+                             const void* v_new, const void* gate, const float* q_norm_w,
+                             const float* k_norm_w, void* k_cache, void* v_cache, bool fp8,
+                             float k_scale, float v_scale, const int32_t* seqlens, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   try {
     zg_status st = check_cfg(cfg);
     if (st != ZG_OK) return st;
@@ -402,6 +402,8 @@ zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride
     if (cfg->window == 0 && cache_stride < max_seqlen)
       return fail(ZG_ERR_SHAPE, "linear cache: cache_stride=%lld < max_seqlen=%lld",
                   (long long)cache_stride, (long long)max_seqlen);
+    if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+      return fail(ZG_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
     if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
         !aligned16(v_cache) || (q_norm_w && !aligned16(q_norm_w)) ||
         (k_norm_w && !aligned16(k_norm_w)))
@@ -436,12 +438,48 @@ zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride
     p.n_chunks = (int32_t)((keys + kDecodeChunk - 1) / kDecodeChunk);
     p.gated = cfg->gated;
     p.eps = cfg->rms_eps;
-    p.scale_log2 = scale_log2(cfg);
+    p.scale_log2 = scale_log2(cfg) * (fp8 ? k_scale : 1.0f);
     p.rope = rope_table(cfg);
+    p.fp8 = fp8 ? 1 : 0;
+    p.k_inv = 1.0f / k_scale;
+    p.v_inv = 1.0f / v_scale;
+    p.v_scale = v_scale;
     return hip_status(zg::launch_decode(p, reinterpret_cast<hipStream_t>(stream)), "decode launch");
   } catch (...) {
-    return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_decode");
+    return fail(ZG_ERR_HIP, "unexpected exception in decode");
   }
+}
+
+zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                         int64_t max_seqlen, const void* q_new, const void* k_new,
+                         const void* v_new, const void* gate, const float* q_norm_w,
+                         const float* k_norm_w, void* k_cache, void* v_cache,
+                         const int32_t* seqlens, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return decode_impl(cfg, B, cache_stride, max_seqlen, q_new, k_new, v_new, gate, q_norm_w,
+                     k_norm_w, k_cache, v_cache, false, 1.f, 1.f, seqlens, out, workspace,
+                     workspace_bytes, stream);
+}
+
+zg_status zg_attn_decode_fp8(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                             int64_t max_seqlen, const void* q_new, const void* k_new,
+                             const void* v_new, const void* gate, const float* q_norm_w,
+                             const float* k_norm_w, void* k_cache, void* v_cache, float k_scale,
+                             float v_scale, const int32_t* seqlens, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return decode_impl(cfg, B, cache_stride, max_seqlen, q_new, k_new, v_new, gate, q_norm_w,
+                     k_norm_w, k_cache, v_cache, true, k_scale, v_scale, seqlens, out, workspace,
+                     workspace_bytes, stream);
+}
+
+zg_status zg_kv_to_fp8(const void* src_bf16, void* dst_e4m3, int64_t n, float scale, void* stream) {
+  if (!src_bf16 || !dst_e4m3) return fail(ZG_ERR_NULL, "src and dst must be non-NULL");
+  if (n < 0 || n % 16 != 0) return fail(ZG_ERR_SHAPE, "n=%lld must be a non-negative multiple of 16", (long long)n);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(ZG_ERR_SHAPE, "scale must be finite and > 0");
+  if (!aligned16(src_bf16) || !aligned16(dst_e4m3)) return fail(ZG_ERR_SHAPE, "pointers must be 16-byte aligned");
+  zg::ToFp8Params p{static_cast<const uint16_t*>(src_bf16), static_cast<uint8_t*>(dst_e4m3), n,
+                    1.0f / scale};
+  return hip_status(zg::launch_to_fp8(p, reinterpret_cast<hipStream_t>(stream)), "to-fp8 launch");
 }
 
 zg_status zg_rmsnorm(int64_t rows, int32_t dim, const float* x, const float* w, float eps,

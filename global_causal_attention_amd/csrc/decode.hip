@@ -26,6 +26,28 @@ __device__ __forceinline__ int64_t n_valid_rows(int pos, int window) {
   return window > 0 ? (int64_t)min(pos + 1, window) : (int64_t)pos + 1;
 }
 
+// E4M3 (OCP 8-bit float, 4 exponent bits, 3 mantissa bits, largest finite 448): sixteen floats
+// times `inv` rounded to nearest-even E4M3, saturated to +-448 first (the conversion itself turns
+// values beyond the range into NaN), packed in element order.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.f, 448.f),
+                                                     __builtin_amdgcn_fmed3f(b, -448.f, 448.f), 0u, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, -448.f, 448.f),
+                                         __builtin_amdgcn_fmed3f(d, -448.f, 448.f), w, true);
+}
+__device__ __forceinline__ u32x4 pack16_e4m3(const float* x, float inv) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = pack4_e4m3(x[4 * i] * inv, x[4 * i + 1] * inv, x[4 * i + 2] * inv, x[4 * i + 3] * inv);
+  return w;
+}
+// Two E4M3 bytes (word `hi` of w) widened exactly to a bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // Sum over the 16 lanes of a DPP row, left in every lane: rotations by 8, 4, 2 and 1 (VALU only).
 __device__ __forceinline__ float row16_sum(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
@@ -68,7 +90,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeParams p) {
           const uint32_t w1 = pack_bf16(x[4 * i + 2], x[4 * i + 3]);
           dst[i] = f32x4{bf16lo(w0), bf16hi(w0), bf16lo(w1), bf16hi(w1)};
         }
-      } else {
+      } else if (!p.fp8) {
         const int64_t off = ((int64_t)b * p.rows + row) * p.Hkv * kHeadDim + (int64_t)h * kHeadDim;
         u32x4* kd = reinterpret_cast<u32x4*>(p.k_cache + off + 64 * half);
 #pragma unroll
@@ -78,6 +100,22 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeParams p) {
         u32x4* vd = reinterpret_cast<u32x4*>(p.v_cache + off + 64 * half);
 #pragma unroll
         for (int i = 0; i < 8; ++i) vd[i] = vs[i];
+      } else {
+        // E4M3 rows: one byte per element
+        const int64_t off = ((int64_t)b * p.rows + row) * p.Hkv * kHeadDim + (int64_t)h * kHeadDim;
+        u32x4* kd = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(p.k_cache) + off + 64 * half);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kd[i] = pack16_e4m3(x + 16 * i, p.k_inv);
+        const u32x4* vs = reinterpret_cast<const u32x4*>(
+            p.v_new + ((int64_t)b * p.Hkv + h) * kHeadDim + 64 * half);
+        u32x4* vd = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(p.v_cache) + off + 64 * half);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float vf[16];
+          unpack8(vs[2 * i], vf);
+          unpack8(vs[2 * i + 1], vf + 8);
+          vd[i] = pack16_e4m3(vf, p.v_inv);
+        }
       }
     }
     __syncthreads();
@@ -328,6 +366,230 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
   }
 }
 
+// The same split-KV attention over E4M3 caches (128 bytes per key and head). Pass A: 8 lanes per
+// key row, 16 bytes = 16 elements each; two elements at a time are widened exactly to a bf16 pair
+// and enter v_dot2_f32_bf16 with the matching q pair. Pass B: 8 lanes per value row (16 elements);
+// the E4M3 bytes of keys j and j + 32 are interleaved by v_perm_b32 before widening, so each bf16
+// pair holds one element of both keys and meets that key pair's P. Stored values stand for value *
+// scale: the key scale is folded into the score scale, the value scale applied to o.
+template <int G>
+__global__ __launch_bounds__(kDecThreads) void decode_attn_fp8_kernel(DecodeParams p) {
+  constexpr int kMaxChunk = kDecodeChunkKeys;
+  constexpr int KL = 8;                  // lanes per key row (pass A) and per value row (pass B)
+  constexpr int KPR = kDecThreads / KL;  // 32 keys per workgroup round
+  constexpr int UA = 8;                  // rounds per pass-A step
+  static_assert(kMaxChunk % 128 == 0, "pass B walks the chunk in blocks of 128 keys");
+  __shared__ float s_s[G * kMaxChunk];   // scores, then P pairs, then the cross-wave reduction
+  __shared__ float ml[G][2];
+  static_assert(G * kMaxChunk >= 4 * G * kHeadDim, "reduction fits the score rows");
+
+  const int chunk_id = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int pos = p.seqlens[b] - 1;
+  if (pos < 0 || (p.window == 0 && pos >= p.rows)) return;
+  const int64_t n_valid = min(n_valid_rows(pos, p.window), (int64_t)p.n_chunks * p.chunk);
+  const int64_t k0 = (int64_t)chunk_id * p.chunk;
+  if (k0 >= n_valid) return;
+  const int n = (int)min((int64_t)p.chunk, n_valid - k0);
+  const int n_chunks_b = (int)((n_valid + p.chunk - 1) / p.chunk);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row_stride = (int64_t)p.Hkv * kHeadDim;  // bytes
+  const int64_t head_off = ((int64_t)b * p.rows + k0) * row_stride + kvh * kHeadDim;
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.k_cache);
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.v_cache);
+  const int kq = tid / KL;
+  const int sub = tid % KL;
+
+  // ---- pass A: raw scores against the stored keys
+  {
+    uint32_t qp[G][8];  // q pairs of dims 16 sub + 2 i, + 1
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(
+          p.qhat + ((int64_t)b * p.Hq + kvh * G + h) * kHeadDim + 16 * sub);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 a = src[i];
+        qp[h][2 * i] = pack_bf16(a[0], a[1]);
+        qp[h][2 * i + 1] = pack_bf16(a[2], a[3]);
+      }
+    }
+    const uint8_t* kbase = kc + head_off + 16 * sub;
+    for (int j0 = 0; j0 < n; j0 += KPR * UA) {
+      u32x4 kr[UA];
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const int j = j0 + KPR * u + kq;
+        kr[u] = j < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (int64_t)j * row_stride))
+                      : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        uint32_t kp[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = kr[u][i];
+          kp[2 * i] = e4m3x2_bf16<false>(w);
+          kp[2 * i + 1] = e4m3x2_bf16<true>(w);
+        }
+        float d[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float a = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = dot2(kp[i], qp[h][i], a);
+          d[h] = group_sum<KL>(a);
+        }
+        const int j = j0 + KPR * u + kq;
+#pragma unroll
+        for (int h0 = 0; h0 < G; h0 += KL) {
+          if (j < n && h0 + sub < G) {
+            float v = d[h0];
+#pragma unroll
+            for (int h = h0 + 1; h < G && h < h0 + KL; ++h) v = (sub == h - h0) ? d[h] : v;
+            s_s[(h0 + sub) * kMaxChunk + j] = v;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- exact softmax over the chunk, one wave per head; bf16 P stored in key pairs (j, j + 32)
+  // (j % 64 < 32) over the head's score row: dword (j / 64) * 32 + j % 32 holds both
+  const int n_pad = (n + 127) & ~127;
+  for (int h = wave; h < G; h += 4) {
+    float* sh = s_s + h * kMaxChunk;
+    float mx = -INFINITY;
+    for (int j = lane; j < n; j += 64) mx = fmaxf(mx, sh[j]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+    const float c = p.scale_log2;
+    const float nmc = -mx * c;
+    float sum = 0.f;
+    for (int q = lane; q < n_pad / 2; q += 64) {
+      const int ja = (q >> 5) * 64 + (q & 31);  // ja >= q
+      const int jb = ja + 32;
+      const float ea = ja < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(sh[ja], c, nmc)) : 0.f;
+      const float eb = jb < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(sh[jb], c, nmc)) : 0.f;
+      const uint32_t w = pack_bf16(ea, eb);
+      sh[q] = __uint_as_float(w);
+      sum += bf16lo(w) + bf16hi(w);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += shfl_xor_f(sum, o);
+    if (lane == 0) {
+      ml[h][0] = mx * c;
+      ml[h][1] = sum;
+    }
+  }
+  __syncthreads();
+
+  // ---- pass B: o[h][d] = sum_j p[h][j] v[j][d] over key pairs (j, j + 32)
+  float acc[G][16];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
+  const uint8_t* vbase = vc + head_off + 16 * sub;
+  for (int j0 = 0; j0 < n; j0 += 128) {
+    u32x4 vr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + 32 * u + kq;
+      vr[u] = j < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + (int64_t)j * row_stride))
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int q = (j0 >> 6) * 32 + 32 * t + kq;  // key pair (j0 + 64 t + kq, + 32)
+      uint32_t pw[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pw[h] = __float_as_uint(s_s[h * kMaxChunk + q]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = vr[2 * t][i], bb = vr[2 * t + 1][i];  // dims 4 i .. 4 i + 3
+        const uint32_t lo = __builtin_amdgcn_perm(bb, a, 0x05010400u);  // a0 b0 a1 b1
+        const uint32_t hi = __builtin_amdgcn_perm(bb, a, 0x07030602u);  // a2 b2 a3 b3
+        const uint32_t d0 = e4m3x2_bf16<false>(lo), d1 = e4m3x2_bf16<true>(lo);
+        const uint32_t d2 = e4m3x2_bf16<false>(hi), d3 = e4m3x2_bf16<true>(hi);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[h][4 * i] = dot2(d0, pw[h], acc[h][4 * i]);
+          acc[h][4 * i + 1] = dot2(d1, pw[h], acc[h][4 * i + 1]);
+          acc[h][4 * i + 2] = dot2(d2, pw[h], acc[h][4 * i + 2]);
+          acc[h][4 * i + 3] = dot2(d3, pw[h], acc[h][4 * i + 3]);
+        }
+      }
+    }
+  }
+  // reduce the 8 key slots of a wave (lanes 8 apart), then the 4 waves through LDS
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float a = acc[h][e];
+      a += shfl_xor_f(a, 8);
+      a += shfl_xor_f(a, 16);
+      a += shfl_xor_f(a, 32);
+      acc[h][e] = a;
+    }
+  __syncthreads();  // every wave is done reading P
+  float* red = s_s;  // [4 waves][G][128]
+  if (lane < 8) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(wave * G + h) * kHeadDim + 16 * lane + e] = acc[h][e];
+  }
+  __syncthreads();
+
+  for (int i = tid; i < G * kHeadDim; i += kDecThreads) {
+    const int h = i / kHeadDim;
+    const int d = i - h * kHeadDim;
+    const float o = p.v_scale * (red[(0 * G + h) * kHeadDim + d] + red[(1 * G + h) * kHeadDim + d] +
+                                 red[(2 * G + h) * kHeadDim + d] + red[(3 * G + h) * kHeadDim + d]);
+    const int head = kvh * G + h;
+    if (n_chunks_b == 1) {
+      float y = o / ml[h][1];
+      if (p.gated) {
+        const float g = bf16lo(p.gate[((int64_t)b * p.Hq + head) * kHeadDim + d]);
+        y *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+      }
+      p.out[((int64_t)b * p.Hq + head) * kHeadDim + d] = (uint16_t)(pack_bf16(y, 0.f) & 0xffffu);
+    } else {
+      float* rec = p.partial + (((int64_t)b * p.Hq + head) * p.n_chunks + chunk_id) * kPartStride;
+      if (d == 0) {
+        rec[0] = ml[h][0];
+        rec[1] = ml[h][1];
+      }
+      rec[4 + d] = o;
+    }
+  }
+}
+
+// bf16 -> E4M3 of value * inv_scale, 16 elements per lane.
+__global__ __launch_bounds__(256) void to_fp8_kernel(ToFp8Params p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i * 16 >= p.n) return;
+  const u32x4* s = reinterpret_cast<const u32x4*>(p.src + 16 * i);
+  float x[16];
+  unpack8(s[0], x);
+  unpack8(s[1], x + 8);
+  *reinterpret_cast<u32x4*>(p.dst + 16 * i) = pack16_e4m3(x, p.inv_scale);
+}
+
+hipError_t launch_to_fp8(const ToFp8Params& p, hipStream_t s) {
+  const int64_t lanes = p.n / 16;
+  if (lanes == 0) return hipSuccess;
+  hipLaunchKernelGGL(to_fp8_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 // One workgroup per (head, sequence), one thread per output dim. The chunk weights exp2(m_c - M)
 // are formed once (chunks spread over the threads) and shared through LDS; the per-dim sums then
 // issue their loads independently of each other.
@@ -383,11 +645,15 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int G = p.Hq / p.Hkv;
   const dim3 grid(p.n_chunks, p.Hkv, p.B);
-  switch (G) {
-    case 1: hipLaunchKernelGGL(decode_attn_kernel<1>, grid, dim3(kDecThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(decode_attn_kernel<2>, grid, dim3(kDecThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(decode_attn_kernel<4>, grid, dim3(kDecThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(decode_attn_kernel<8>, grid, dim3(kDecThreads), 0, s, p); break;
+  switch (G * 2 + (p.fp8 ? 1 : 0)) {
+    case 2: hipLaunchKernelGGL(decode_attn_kernel<1>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 4: hipLaunchKernelGGL(decode_attn_kernel<2>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL(decode_attn_kernel<4>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 16: hipLaunchKernelGGL(decode_attn_kernel<8>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 3: hipLaunchKernelGGL(decode_attn_fp8_kernel<1>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 5: hipLaunchKernelGGL(decode_attn_fp8_kernel<2>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 9: hipLaunchKernelGGL(decode_attn_fp8_kernel<4>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 17: hipLaunchKernelGGL(decode_attn_fp8_kernel<8>, grid, dim3(kDecThreads), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   e = hipGetLastError();

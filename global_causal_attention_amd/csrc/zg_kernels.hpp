@@ -83,7 +83,20 @@ struct DecodeParams {
   float eps;
   float scale_log2;
   RopeTableH rope;
+  // E4M3 caches (one byte per element) holding k_hat / k_scale and v / v_scale: the new row is
+  // written as E4M3 of its value times k_inv / v_inv, and outputs are multiplied by v_scale
+  // (k_scale is folded into scale_log2 by the host).
+  int32_t fp8;
+  float k_inv, v_inv, v_scale;
 };
+
+struct ToFp8Params {
+  const uint16_t* src;  // bf16
+  uint8_t* dst;         // E4M3
+  int64_t n;            // elements, multiple of 16
+  float inv_scale;
+};
+hipError_t launch_to_fp8(const ToFp8Params& p, hipStream_t s);
 
 struct RmsNormParams {
   const float* x;

@@ -143,6 +143,29 @@ zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride
                          size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Decode over E4M3 KV caches: the FP8 format of the pages' forward pass (zh-TW translation,
+ * section 3.1, hyper-parameters: mixed FP8, E4M3 forward), here halving the cache bytes that bound
+ * decode (section 2.3). E4M3 is the OCP 8-bit float with 4 exponent bits (bias 7), 3 mantissa bits,
+ * no infinities, largest finite 448.
+ *   k_cache, v_cache: as for zg_attn_decode but one byte per element; an entry c stands for
+ *            c * k_scale (keys) or c * v_scale (values). The new token's k_hat / k_scale and
+ *            v_new / v_scale are rounded to nearest-even E4M3, saturating at +-448, and written to
+ *            the row of pos. k_scale, v_scale: finite and > 0.
+ *   Everything else as zg_attn_decode (same workspace size).
+ * Errors as zg_attn_decode; a bad scale -> ZG_ERR_SHAPE. */
+zg_status zg_attn_decode_fp8(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                             int64_t max_seqlen, const void* q_new, const void* k_new,
+                             const void* v_new, const void* gate, const float* q_norm_w,
+                             const float* k_norm_w, void* k_cache, void* v_cache, float k_scale,
+                             float v_scale, const int32_t* seqlens, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* bf16 -> E4M3 conversion of n elements (e.g. a bf16 cache into an E4M3 cache): dst[i] =
+ * E4M3(src[i] / scale), nearest-even, saturating at +-448. n a multiple of 16, 16-byte aligned
+ * device pointers, scale finite and > 0; asynchronous on the stream. */
+zg_status zg_kv_to_fp8(const void* src_bf16, void* dst_e4m3, int64_t n, float scale, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * KV-cache bytes of an n_layers stack (pure host arithmetic; zh-TW translation, section 2.3):
  *   sum over layers l = 1..n_layers of  rows(l) * 2 * n_kv_heads * head_dim * elem_bytes * batch,
  *   rows(l) = seqlen if layer l is global (global_every > 0 && l % global_every == 0, or window <= 0)
