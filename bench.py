@@ -9,7 +9,8 @@ softmax on bf16 MFMA, sigmoid gate. value = B*T / (time of one block) in tokens/
 
 Also measured in the same run (reported beside the headline):
   * the B=64 decode step over a 128-slot ring (local layer) and a linear cache with context lengths
-    uniform on [8192, 65536] (global layer), cold caches, as GB/s of KV read against HBM peak;
+    uniform on [8192, 65536] (global layer), cold caches, as GB/s of KV read against HBM peak; the
+    linear step again over E4M3 caches;
   * one gated local and one global layer at B=1, T=262144 (base 1e7), against the HBM and MFMA
     rooflines;
   * the 32-layer attention stack with projections at B=1, T=65536 (27 gated local + 5 global
@@ -83,7 +84,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    log(f"[bench] device {torch.cuda.get_device_name(0)}; building inputs B={B} T={T}")
+    log(f"[bench] device {torch.cuda.get_device_name(0)}")
 
     result = {
         "metric": "gated-SWA/global attn prefill tokens/s + %MFMA peak; decode HBM GB/s %peak",
@@ -115,6 +116,7 @@ def main():
 
 def bench_block(torch, zg, si, dev, stream, args):
     """The timed 5:1 block at B=4, T=16384 (the headline value and roofline)."""
+    log(f"[bench] building inputs B={B} T={T}")
     gen = si.generator(SEED, device="cuda")
     swa = si.prefill_layer(gen, B, T, HQ, HKV, D, gated=True, device="cuda")
     glo = si.prefill_layer(gen, B, T, HQ, HKV, D, gated=False, device="cuda")
@@ -251,6 +253,36 @@ def bench_decode(torch, zg, si, dev, stream, reps):
         res[name] = {"ms_median": round(med, 4), "kv_bytes": kv_bytes, "GBps": round(bw / 1e9, 1),
                      "hbm_frac": round(bw / HBM_PEAK, 4), "tokens_per_s": round(Bd / (med * 1e-3), 1)}
         log(f"[bench] decode {name}: {med:.4f} ms, {bw / 1e9:.1f} GB/s")
+    # the same step over E4M3 caches (converted once from the bf16 ones, outside the timing)
+    lin_k8 = zg.zg_kv_to_fp8(x["lin_k"])
+    lin_v8 = zg.zg_kv_to_fp8(x["lin_v"])
+
+    def lin8():
+        zg.zg_attn_decode_fp8(cfg_l, x["q_new"], x["k_new"], x["v_new"], None, lin_k8, lin_v8,
+                              seqlens, max_seqlen=hi, out=out, workspace=ws_l)
+
+    for _ in range(3):
+        lin8()
+    times = []
+    for _ in range(reps):
+        flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lin8()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    med = times[len(times) // 2]
+    kv8 = sum_len * HKV * D * 2
+    res["linear_e4m3"] = {"ms_median": round(med, 4), "kv_bytes": kv8,
+                          "GBps": round(kv8 / (med * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(kv8 / (med * 1e-3) / HBM_PEAK, 4),
+                          "tokens_per_s": round(Bd / (med * 1e-3), 1),
+                          "speedup_vs_bf16": round(res["linear"]["ms_median"] / med, 3)}
+    log(f"[bench] decode linear E4M3: {med:.4f} ms, {kv8 / (med * 1e-3) / 1e9:.1f} GB/s")
+    del lin_k8, lin_v8
     res["workload"] = "B=64, Hq=32 Hkv=8 D=128, ring W=128 gated; linear L~U[8192,65536] ungated; base 1e7; cold MALL"
     from global_causal_attention_amd.counters import lookup_traffic
     parts = [lookup_traffic("decode_prep_kernel", 16384),
