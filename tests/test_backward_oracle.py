@@ -1,0 +1,58 @@
+"""Pins of the oracle's layer backward (oracle/backward.py): central finite differences of
+sum(dy * y), y = the forward oracle's layer output, for every input, on small shapes (the chain rule
+and the forward are written independently, so a dropped term, a wrong sign or a transposed operand
+in the backward shows up as a mismatch). Also the log-sum-exp rows against a direct evaluation."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _case(seed, B, T, Hq, Hkv, D, gated):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, Hq, D))
+    k = rng.standard_normal((B, T, Hkv, D))
+    v = rng.standard_normal((B, T, Hkv, D))
+    g = rng.standard_normal((B, T, Hq, D)) if gated else None
+    dy = rng.standard_normal((B, T, Hq, D))
+    return q, k, v, g, dy
+
+
+@pytest.mark.parametrize("window,gated,rot", [(0, False, 6), (3, True, 6), (4, True, 0), (2, False, 8)])
+def test_backward_matches_finite_differences(window, gated, rot):
+    B, T, Hq, Hkv, D = 2, 7, 4, 2, 16
+    q, k, v, g, dy = _case(10 + window + rot, B, T, Hq, Hkv, D, gated)
+    kw = dict(window=window, gated=gated, rot_dim=rot, rope_base=100.0, eps=1e-6, pos0=3)
+
+    def loss(q_, k_, v_, g_):
+        return float(np.sum(dy * oracle.prefill(q_, k_, v_, g_, **kw)))
+
+    dq, dk, dv, dg = oracle.layer_backward(q, k, v, g, dy, **kw)
+    rng = np.random.default_rng(99)
+    h = 1e-6
+    inputs = [("q", q, dq), ("k", k, dk), ("v", v, dv)] + ([("g", g, dg)] if gated else [])
+    for name, x, grad in inputs:
+        for _ in range(12):
+            idx = tuple(rng.integers(0, n) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v, "g": g}
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"], args["g"])
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"], args["g"])
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+def test_row_lse_direct():
+    q, k, _, _, _ = _case(5, 1, 9, 4, 2, 16, False)
+    lse = oracle.row_lse(q, k, window=3, rot_dim=6, rope_base=100.0)
+    qh = oracle.qk_prologue(q[0], np.arange(9), None, rot_dim=6, rope_base=100.0, eps=1e-6)
+    kh = oracle.qk_prologue(k[0], np.arange(9), None, rot_dim=6, rope_base=100.0, eps=1e-6)
+    for t in range(9):
+        for h in range(4):
+            lo = max(0, t - 2)
+            s = [qh[t, h] @ kh[j, h // 2] / 4.0 for j in range(lo, t + 1)]
+            assert abs(lse[0, t, h] - np.log(np.sum(np.exp(s)))) < 1e-12
