@@ -15,7 +15,8 @@ from dataclasses import dataclass
 from ._abi import (LIB_PATH, ZgAttnCfg, ZgTokenStrides, load_library, ZG_OK, ZG_ERR_NULL,
                    ZG_ERR_SHAPE, ZG_ERR_UNSUPPORTED, ZG_ERR_WORKSPACE, ZG_ERR_HIP, EXPORTS)
 
-__all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached", "zg_attn_decode", "zg_attn_decode_fp8", "zg_kv_to_fp8", "zg_kv_bytes",
+__all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached",
+           "zg_attn_forward_train", "zg_attn_backward", "zg_attn_backward_workspace_bytes", "zg_attn_decode", "zg_attn_decode_fp8", "zg_kv_to_fp8", "zg_kv_bytes",
            "zg_attn_prefill_workspace_bytes", "zg_attn_decode_workspace_bytes", "zg_rmsnorm",
            "zg_gemm_bf16", "zg_attn_layer", "zg_attn_layer_workspace_bytes", "zg_last_error",
            "load_library", "LIB_PATH", "EXPORTS"]
@@ -128,6 +129,82 @@ def zg_attn_prefill(cfg: AttnConfig, q, k, v, gate=None, *, q_norm_w=None, k_nor
         _ptr(q_norm_w), _ptr(k_norm_w), ctypes.byref(strides), _ptr(out), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def _packed(t, name, shape):
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor of shape {tuple(shape)}")
+
+
+def zg_attn_forward_train(cfg: AttnConfig, q, k, v, gate=None, *, out=None, lse=None,
+                          workspace=None, stream=None):
+    """Forward for training (see include/zg_attn.h): packed q, gate [B, T, Hq, 128] and k, v
+    [B, T, Hkv, 128] bf16, positions 0 .. T-1, norm weights 1. Returns (out, lse) with lse the
+    [B, T, Hq] fp32 natural-log log-sum-exp of each query row's scaled scores."""
+    import torch
+    bf = torch.bfloat16
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    for t, n, shp in ((q, "q", (B, T, Hq, D)), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D))):
+        _need(t, n, bf)
+        _packed(t, n, shp)
+    if cfg.gated:
+        _need(gate, "gate", bf)
+        _packed(gate, "gate", (B, T, Hq, D))
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=bf, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", bf)
+    _packed(out, "out", (B, T, Hq, D))
+    _need(lse, "lse", torch.float32)
+    _packed(lse, "lse", (B, T, Hq))
+    need = zg_attn_prefill_workspace_bytes(cfg, B, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    c = cfg.c()
+    _check(load_library().zg_attn_forward_train(
+        ctypes.byref(c), B, T, _ptr(q), _ptr(k), _ptr(v), _ptr(gate if cfg.gated else None),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out, lse
+
+
+def zg_attn_backward_workspace_bytes(cfg: AttnConfig, B: int, T: int) -> int:
+    c = cfg.c()
+    return load_library().zg_attn_backward_workspace_bytes(ctypes.byref(c), B, T)
+
+
+def zg_attn_backward(cfg: AttnConfig, q, k, v, gate, out, dout, lse, *, workspace=None,
+                     stream=None):
+    """Backward pass (see include/zg_attn.h) from the forward's inputs, its out and lse and the
+    output gradient dout. Returns (dq, dk, dv, dgate); dgate is None when not gated."""
+    import torch
+    bf = torch.bfloat16
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    for t, n, shp in ((q, "q", (B, T, Hq, D)), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D)),
+                      (out, "out", (B, T, Hq, D)), (dout, "dout", (B, T, Hq, D))):
+        _need(t, n, bf)
+        _packed(t, n, shp)
+    if cfg.gated:
+        _need(gate, "gate", bf)
+        _packed(gate, "gate", (B, T, Hq, D))
+    _need(lse, "lse", torch.float32)
+    _packed(lse, "lse", (B, T, Hq))
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dgate = torch.empty_like(q) if cfg.gated else None
+    need = zg_attn_backward_workspace_bytes(cfg, B, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    c = cfg.c()
+    _check(load_library().zg_attn_backward(
+        ctypes.byref(c), B, T, _ptr(q), _ptr(k), _ptr(v), _ptr(gate if cfg.gated else None),
+        _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv, dgate
 
 
 def zg_attn_prefill_cached_workspace_bytes(cfg: AttnConfig, B: int, T: int) -> int:

@@ -41,6 +41,11 @@ EXPORTS = {
     "zg_attn_decode_fp8": (ctypes.c_int, [_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _F32, _F32, _P, _P, _P, _SZ, _P]),
     "zg_kv_to_fp8": (ctypes.c_int, [_P, _P, _I64, _F32, _P]),
+    "zg_attn_forward_train": (ctypes.c_int, [_CFG, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                             _P]),
+    "zg_attn_backward_workspace_bytes": (_SZ, [_CFG, _I32, _I32]),
+    "zg_attn_backward": (ctypes.c_int, [_CFG, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _SZ, _P]),
     "zg_kv_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32, _I32, _I64, _I64]),
     "zg_last_error": (ctypes.c_char_p, []),
     "zg_rmsnorm": (ctypes.c_int, [_I64, _I32, _P, _P, _F32, _P, _P]),

@@ -214,6 +214,179 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
   }
 }
 
+// ---- training: forward with row log-sum-exp, and the backward pass ----
+static zg_status check_train(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
+  zg_status st = check_cfg(cfg);
+  if (st != ZG_OK) return st;
+  if (cfg->n_q_heads != 4 * cfg->n_kv_heads)
+    return fail(ZG_ERR_UNSUPPORTED, "training kernels: n_q_heads must be 4 * n_kv_heads (got %d / %d)",
+                cfg->n_q_heads, cfg->n_kv_heads);
+  if (B < 1 || T < 1) return fail(ZG_ERR_SHAPE, "B=%d T=%d must be >= 1", B, T);
+  const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+  if ((int64_t)B * T * Hq * kD >= (int64_t(1) << 40)) return fail(ZG_ERR_SHAPE, "B*T*Hq*D too large");
+  // the forward kernel addresses one sequence's q, K and V rows through 32-bit byte offsets
+  if ((int64_t)(T + 64) * 2 * Hq * kD >= (int64_t(1) << 32))
+    return fail(ZG_ERR_UNSUPPORTED, "T * Hq * 256 bytes must stay below 4 GiB");
+  if ((int64_t)((T + 63) / 64) * B * Hkv >= (int64_t(1) << 31)) return fail(ZG_ERR_SHAPE, "grid too large");
+  return ZG_OK;
+}
+
+zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, const void* q,
+                                const void* k, const void* v, const void* gate, void* out,
+                                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    zg_status st = check_train(cfg, B, T);
+    if (st != ZG_OK) return st;
+    if (!q || !k || !v || !out || !lse) return fail(ZG_ERR_NULL, "q, k, v, out and lse must be non-NULL");
+    if (cfg->gated && !gate) return fail(ZG_ERR_NULL, "gate must be non-NULL when gated=1");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) ||
+        (cfg->gated && !aligned16(gate)))
+      return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    const size_t need = zg_attn_prefill_workspace_bytes(cfg, B, T);
+    if (!workspace || workspace_bytes < need)
+      return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned16(workspace)) return fail(ZG_ERR_SHAPE, "workspace must be 16-byte aligned");
+    const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const zg::RopeTableH rt = rope_table(cfg);
+    zg::KPrepParams kp{};
+    kp.k = static_cast<const uint16_t*>(k);
+    kp.khat = static_cast<uint16_t*>(workspace);
+    kp.sk = Hkv * kD;
+    kp.B = B;
+    kp.T = T;
+    kp.Hkv = (int32_t)Hkv;
+    kp.out_rows = T;
+    kp.eps = cfg->rms_eps;
+    kp.rope = rt;
+    st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
+    if (st != ZG_OK) return st;
+    zg::PrefillParams pp{};
+    pp.q = static_cast<const uint16_t*>(q);
+    pp.khat = static_cast<const uint16_t*>(workspace);
+    pp.v = static_cast<const uint16_t*>(v);
+    pp.gate = static_cast<const uint16_t*>(gate);
+    pp.out = static_cast<uint16_t*>(out);
+    pp.sq = Hq * kD;
+    pp.sv = Hkv * kD;
+    pp.sg = Hq * kD;
+    pp.so = Hq * kD;
+    pp.B = B;
+    pp.T = T;
+    pp.Hq = (int32_t)Hq;
+    pp.Hkv = (int32_t)Hkv;
+    pp.window = cfg->window >= T ? 0 : cfg->window;
+    pp.n_qtiles = (T + 63) / 64;
+    pp.kv_rows = T;
+    pp.n_keys = T;
+    pp.lse = lse;
+    pp.eps = cfg->rms_eps;
+    pp.scale_log2 = scale_log2(cfg);
+    pp.rope = rt;
+    return hip_status(zg::launch_prefill_general(pp, 4, cfg->gated != 0, hs), "prefill launch");
+  } catch (...) {
+    return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_forward_train");
+  }
+}
+
+size_t zg_attn_backward_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
+  if (!cfg || B < 1 || T < 1 || cfg->n_q_heads < 1 || cfg->n_kv_heads < 1) return 0;
+  const size_t bt = (size_t)B * T, hq = cfg->n_q_heads, hk = cfg->n_kv_heads;
+  return 2 * align256(bt * hq * kD * 2) + align256(bt * hk * kD * 2) + align256(bt * hq * 16 * 2) +
+         align256(bt * hq * kD * 4) + align256(bt * hk * kD * 4);
+}
+
+zg_status zg_attn_backward(const zg_attn_cfg* cfg, int32_t B, int32_t T, const void* q,
+                           const void* k, const void* v, const void* gate, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* dgate, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    zg_status st = check_train(cfg, B, T);
+    if (st != ZG_OK) return st;
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+      return fail(ZG_ERR_NULL, "q, k, v, out, dout, lse, dq, dk and dv must be non-NULL");
+    if (cfg->gated && (!gate || !dgate))
+      return fail(ZG_ERR_NULL, "gate and dgate must be non-NULL when gated=1");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+        !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        (cfg->gated && (!aligned16(gate) || !aligned16(dgate))))
+      return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    const size_t need = zg_attn_backward_workspace_bytes(cfg, B, T);
+    if (!workspace || workspace_bytes < need)
+      return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned16(workspace)) return fail(ZG_ERR_SHAPE, "workspace must be 16-byte aligned");
+    const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+    const size_t bt = (size_t)B * T;
+    char* ws = static_cast<char*>(workspace);
+    zg::BwdParams bp{};
+    bp.qc = reinterpret_cast<uint16_t*>(ws);
+    ws += align256(bt * Hq * kD * 2);
+    bp.dO = reinterpret_cast<uint16_t*>(ws);
+    ws += align256(bt * Hq * kD * 2);
+    bp.khat = reinterpret_cast<uint16_t*>(ws);
+    ws += align256(bt * Hkv * kD * 2);
+    bp.aux = reinterpret_cast<uint16_t*>(ws);
+    ws += align256(bt * Hq * 16 * 2);
+    bp.dqh = reinterpret_cast<float*>(ws);
+    ws += align256(bt * Hq * kD * 4);
+    bp.dkh = reinterpret_cast<float*>(ws);
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const zg::RopeTableH rt = rope_table(cfg);
+    // q_hat * scale * log2 e and k_hat in bf16: the operands the forward multiplied
+    zg::KPrepParams kp{};
+    kp.k = static_cast<const uint16_t*>(q);
+    kp.khat = bp.qc;
+    kp.sk = Hq * kD;
+    kp.B = B;
+    kp.T = T;
+    kp.Hkv = (int32_t)Hq;
+    kp.out_rows = T;
+    kp.eps = cfg->rms_eps;
+    kp.rope = rt;
+    kp.fold = 1;
+    kp.fold_scale = scale_log2(cfg);
+    st = hip_status(zg::launch_kprep(kp, hs), "kprep launch (q)");
+    if (st != ZG_OK) return st;
+    kp.k = static_cast<const uint16_t*>(k);
+    kp.khat = bp.khat;
+    kp.sk = Hkv * kD;
+    kp.Hkv = (int32_t)Hkv;
+    kp.fold = 0;
+    kp.fold_scale = 1.f;
+    st = hip_status(zg::launch_kprep(kp, hs), "kprep launch (k)");
+    if (st != ZG_OK) return st;
+
+    bp.q = static_cast<const uint16_t*>(q);
+    bp.k = static_cast<const uint16_t*>(k);
+    bp.v = static_cast<const uint16_t*>(v);
+    bp.gate = cfg->gated ? static_cast<const uint16_t*>(gate) : nullptr;
+    bp.out = static_cast<const uint16_t*>(out);
+    bp.dout = static_cast<const uint16_t*>(dout);
+    bp.lse = lse;
+    bp.dq = static_cast<uint16_t*>(dq);
+    bp.dk = static_cast<uint16_t*>(dk);
+    bp.dv = static_cast<uint16_t*>(dv);
+    bp.dgate = cfg->gated ? static_cast<uint16_t*>(dgate) : nullptr;
+    bp.B = B;
+    bp.T = T;
+    bp.Hq = (int32_t)Hq;
+    bp.Hkv = (int32_t)Hkv;
+    bp.window = cfg->window >= T ? 0 : cfg->window;
+    bp.gated = cfg->gated;
+    bp.n_qtiles = (T + 63) / 64;
+    bp.pos0 = 0;
+    bp.eps = cfg->rms_eps;
+    bp.scale = (float)(cfg->softmax_scale > 0.f ? (double)cfg->softmax_scale : 1.0 / std::sqrt((double)kD));
+    bp.rope = rt;
+    return hip_status(zg::launch_backward(bp, hs), "backward launch");
+  } catch (...) {
+    return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_backward");
+  }
+}
+
 size_t zg_attn_prefill_cached_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
   if (!cfg || B < 1 || T < 1 || cfg->n_kv_heads < 1) return 0;
   if (cfg->window <= 0) return 0;  // linear caches: keys are read from the cache itself

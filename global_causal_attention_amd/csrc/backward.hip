@@ -1,0 +1,626 @@
+// Backward pass of one attention layer for gfx950: gradients of q, k, v and the gate logits of
+//   y = A(q_hat, k_hat, v) * sigmoid(g),  q_hat / k_hat = RoPE(RMSNorm(q / k)),
+// banded (sliding window) or full causal, GQA with 4 query heads per KV head, head dim 128.
+//
+// Method: ZGCM-1 zh-TW translation page, section 2.1 "Model overview" and Figure 3 (the layer's
+// forward: QK-RMSNorm, partial RoPE, window or full causal attention, the sigmoid gate); section 2.2
+// and section 3.1 report training throughput, i.e. forward plus this backward. The chain rule is
+// taken in the usual flash-attention form: the softmax is recomputed from the forward's row
+// log-sum-exp L, and with D_t = sum_d dO_t,d O_t,d the score gradient is dS = P (dP - D),
+// dP = dO V^T.
+//
+// Kernels (one launch each, in this order):
+//  1. bwd_pre   per (token, query head): dO = dy * sigmoid(g), dg = dy * y * (1 - sigmoid(g)),
+//               D = sum dy * y, and a 16-value bf16 row (-L log2 e and -D, each split exactly into
+//               three bf16 terms) that an extra matrix-core step subtracts from the scores.
+//  2. bwd_q     per (sequence, KV head, 64 queries): streams K_hat/V tiles like the forward and
+//               accumulates dq_hat = scale * dS K_hat.
+//  3. bwd_kv    per (sequence, KV head, 64 keys): keeps the tile's K_hat and V as matrix-core
+//               operands in registers, one wave per query head streams that head's rows
+//               (q_hat, dO, the -L/-D row) through its own LDS buffers, accumulates
+//               dV = P^T dO and dk_hat = scale * dS^T q_hat; the 4 heads' sums meet in LDS.
+//  4. prologue_bwd  dq, dk from dq_hat, dk_hat through RoPE (rotation by the negated angle) and
+//               RMSNorm (weight 1).
+#include "zg_mfma.hpp"
+
+namespace zg {
+
+namespace {
+
+constexpr int kG = 4;                    // query heads per KV head
+constexpr int kNk = 64;                  // keys per tile
+constexpr int kRow = 256;                // LDS bytes per staged 128-dim bf16 row
+constexpr int kTileBytes = kNk * kRow;   // 16384
+constexpr int kQLds = 4 * kTileBytes;    // bwd_q: two K_hat buffers, then two V buffers
+
+// bwd_kv: per wave two buffers of (32 q_hat rows, 32 dO rows, 32 rows of 16 bf16)
+constexpr int kStepQ = 32;
+constexpr int kQcOff = 0;
+constexpr int kDoOff = kStepQ * kRow;          // 8192
+constexpr int kAuxOff = 2 * kStepQ * kRow;     // 16384
+constexpr int kStepBytes = kAuxOff + kStepQ * 32;  // 17408
+constexpr int kKvWaves = kG;
+constexpr int kKvVTile = kKvWaves * 2 * kStepBytes;  // 139264: the tile's V rows, shared
+constexpr int kKvLds = kKvVTile + kTileBytes;        // 155648
+static_assert(kKvLds <= 160 * 1024, "LDS budget");
+static_assert(kKvWaves * 32 * 64 * 16 <= kKvVTile, "cross-wave reduction fits the stream buffers");
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-byte chunk c of a staged row r lives at chunk c ^ swz(r) (as in the forward kernels).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// x = a + b + c exactly to fp32 precision, each term a bf16 value.
+__device__ __forceinline__ u32x2 split3_bf16(float x) {
+  const float a = bf16lo(pack_bf16(x, 0.f));
+  const float r = x - a;
+  const float b = bf16lo(pack_bf16(r, 0.f));
+  const float c = r - b;
+  return u32x2{pack_bf16(a, b), pack_bf16(c, 0.f)};
+}
+
+__device__ __forceinline__ bf16x8 ones3(bool on) {
+  const __bf16 o = (__bf16)1.0f, z = (__bf16)0.0f;
+  return on ? bf16x8{o, o, o, z, z, z, z, z} : bf16x8{};
+}
+
+// Raw buffer resource over `bytes` bytes from `base` (both wave-uniform); loads past the end
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
+}
+
+// One 1 KB LDS-direct load: lane l's 16 bytes at voff go to LDS address m0 + 16 l.
+__device__ __forceinline__ void lds_dma(uint32_t m0, uint32_t voff, __amdgpu_buffer_rsrc_t r) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(m0), "v"(voff), "s"(r), "s"(0) : "memory", "m0");
+}
+
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing read of a staged tile for an A operand whose K index runs over rows: lane gets rows
+// 16 st + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3} (the order the score layout packs its
+// weights in) of dims 32 db + (lane & 31).
+struct TrOffsets {
+  int off[2][4];
+  __device__ __forceinline__ explicit TrOffsets(int lane) {
+    const int hi = lane >> 5;
+    const int tr_row = 4 * hi + ((lane & 15) >> 2);
+    const int tr_dch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int row = 8 * x + tr_row;
+        off[x][db] = row * kRow + 16 * ((4 * db + tr_dch) ^ swz(row)) + 8 * (lane & 1);
+      }
+  }
+  __device__ __forceinline__ bf16x8 read(const unsigned char* buf, int st, int db) const {
+    const unsigned char* base = buf + st * 16 * kRow;
+    const i16x4 a = lds_read_tr(base + off[0][db]);
+    const i16x4 b = lds_read_tr(base + off[1][db]);
+    const i16x4 both[2] = {a, b};
+    return __builtin_bit_cast(bf16x8, both);
+  }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// 1. Per (token, query head) row; 16 lanes per row, 8 dims each.
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  const int64_t n_rows = (int64_t)p.B * p.T * p.Hq;
+  if (row >= n_rows) return;  // whole 16-lane groups exit together
+  const int64_t off = row * kHeadDim + 8 * c;
+  float y[8], dy[8], d_o[8];
+  unpack8(*reinterpret_cast<const u32x4*>(p.out + off), y);
+  unpack8(*reinterpret_cast<const u32x4*>(p.dout + off), dy);
+  float dsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dsum = fmaf(dy[i], y[i], dsum);
+  if (p.gated) {
+    float g[8], dg[8];
+    unpack8(*reinterpret_cast<const u32x4*>(p.gate + off), g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float s = 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g[i] * kLog2e));
+      d_o[i] = dy[i] * s;
+      dg[i] = dy[i] * y[i] * (1.0f - s);
+    }
+    *reinterpret_cast<u32x4*>(p.dgate + off) = pack8(dg);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d_o[i] = dy[i];
+  }
+  *reinterpret_cast<u32x4*>(p.dO + off) = pack8(d_o);
+  dsum += shfl_xor_f(dsum, 1);
+  dsum += shfl_xor_f(dsum, 2);
+  dsum += shfl_xor_f(dsum, 4);
+  dsum += shfl_xor_f(dsum, 8);
+  if (c < 2) {
+    const float x = (c == 0) ? -p.lse[row] * kLog2e : -dsum;
+    const u32x2 s = split3_bf16(x);
+    *reinterpret_cast<u32x4*>(p.aux + row * 16 + 8 * c) = u32x4{s[0], s[1], 0u, 0u};
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2. dq_hat. Workgroup = 8 waves = (sequence, KV head, 64 queries); wave w owns query head w % 4
+// and queries 32 (w / 4) .. +31 of the tile. Scores are transposed as in the forward,
+// S^T = K_hat Q^T (one query per lane), and dP^T = V dO^T in the same layout, so the weights
+// dS^T pack straight into the B operand of dQ^T = K_hat^T dS^T. Keys stream in tiles of 64
+// through two K_hat and two V buffers (waves 0-3 load K_hat rows, 4-7 V rows), one barrier per
+// tile; q_hat, dO and the -L/-D row are B operands held in registers.
+__global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int per_tile = p.B * p.Hkv;
+  const int t_idx = blockIdx.x / per_tile;
+  const int bh = blockIdx.x - t_idx * per_tile;
+  const int qtile = (p.window == 0) ? (p.n_qtiles - 1 - t_idx) : t_idx;  // heavy tiles first
+  const int b = bh / p.Hkv;
+  const int kvh = bh - b * p.Hkv;
+  constexpr int MQ = 64;
+  const int r0 = qtile * MQ;
+  const int T = p.T;
+  const int W = p.window;
+  const int head = kvh * kG + (wave & 3);
+  const int qbase = r0 + 32 * (wave >> 2);
+  const int my_row = qbase + l32;
+  const bool valid = my_row < T;
+
+  // B operands of this lane's query: dims 16 st + 8 hi .. + 7
+  bf16x8 qf[8], dof[8], auxb;
+  if (valid) {
+    const int64_t rq = ((int64_t)b * T + my_row) * p.Hq + head;
+    const bf16x8* qs = reinterpret_cast<const bf16x8*>(p.qc + rq * kHeadDim + 8 * hi);
+    const bf16x8* ds = reinterpret_cast<const bf16x8*>(p.dO + rq * kHeadDim + 8 * hi);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      qf[st] = qs[2 * st];
+      dof[st] = ds[2 * st];
+    }
+    auxb = *reinterpret_cast<const bf16x8*>(p.aux + rq * 16 + 8 * hi);
+  } else {
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      qf[st] = bf16x8{};
+      dof[st] = bf16x8{};
+    }
+    auxb = bf16x8{};
+  }
+  // A operands of the extra K step: (1, 1, 1) against the -L terms (dims 0-2 of the row) for the
+  // scores, against the -D terms (dims 8-10) for dP
+  const bf16x8 one_l = ones3(hi == 0);
+  const bf16x8 one_d = ones3(hi == 1);
+
+  // key tiles of the workgroup
+  const int q_last = min(r0 + MQ, T) - 1;
+  int k_begin = 0;
+  if (W > 0) k_begin = max(0, r0 - W + 1) & ~(kNk - 1);
+  const int n_tiles = (q_last + 1 - k_begin + kNk - 1) / kNk;
+
+  // tile streaming: 16 rows per wave, 4 LDS-direct loads of 4 rows
+  const bool v_loader = wave >= 4;
+  const int wg = wave & 3;
+  const int row_bytes = p.Hkv * kHeadDim * 2;
+  const uint16_t* slab = (v_loader ? p.v : p.khat) + ((int64_t)b * T * p.Hkv + kvh) * kHeadDim;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (v_loader ? 2 * kTileBytes : 0);
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    voff[i] = (uint32_t)(row * row_bytes + 16 * ((lane & 15) ^ swz(row)));
+  }
+  auto dma_tile = [&](int t) {  // tile t into buffer t & 1
+    const int row0 = k_begin + t * kNk + 16 * wg;
+    const __amdgpu_buffer_rsrc_t r =
+        rsrc_of(slab + (int64_t)row0 * p.Hkv * kHeadDim, (int64_t)min(16, T - row0) * row_bytes);
+    const uint32_t base = lds0 + (t & 1) * kTileBytes + 16 * wg * kRow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma(base + 4 * i * kRow, voff[i], r);
+  };
+
+  int k_off[8];  // A operand of K step st: tile row l32 (+32 per key block), dims 16 st + 8 hi
+#pragma unroll
+  for (int st = 0; st < 8; ++st) k_off[st] = l32 * kRow + 16 * ((2 * st + hi) ^ swz(l32));
+  const TrOffsets tr(lane);
+  auto rd_a = [&](const unsigned char* buf, int st, int kb) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(buf + k_off[st] + kb * 32 * kRow);
+  };
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dq[i] = f32x16{};
+
+  dma_tile(0);
+  vm_wait();
+  __syncthreads();
+  for (int j = 0; j < n_tiles; ++j) {
+    if (j + 1 < n_tiles) dma_tile(j + 1);
+    const unsigned char* kbuf = smem + (j & 1) * kTileBytes;
+    const unsigned char* vbuf = smem + 2 * kTileBytes + (j & 1) * kTileBytes;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(rd_a(kbuf, st, kb), qf[st], s[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(one_l, auxb, s[kb]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(rd_a(vbuf, st, kb), dof[st], dp[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(one_d, auxb, dp[kb]);
+
+    // masked scores to -inf (P = 0); register r of key block kb is key kt + 32 kb + 8 (r / 4) +
+    // 4 hi + r % 4 of this lane's query
+    const int kt = k_begin + j * kNk;
+    if ((kt + kNk - 1 > qbase) || ((W > 0) && (kt < qbase + 31 - W + 1))) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool ok = (key <= my_row) && (W == 0 || key > my_row - W);
+          s[kb][r] = ok ? s[kb][r] : -INFINITY;
+        }
+    }
+    // dS = P (dP - D) with P = exp2(S - L log2 e)
+    u32x4 pk[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        pk[2 * kb + (r >> 3)][(r >> 1) & 3] =
+            pack_bf16(__builtin_amdgcn_exp2f(s[kb][r]) * dp[kb][r],
+                      __builtin_amdgcn_exp2f(s[kb][r + 1]) * dp[kb][r + 1]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        dq[db] = mfma32(tr.read(kbuf, st, db), __builtin_bit_cast(bf16x8, pk[st]), dq[db]);
+    vm_wait();
+    __syncthreads();
+  }
+
+  if (valid) {
+    float* dst = p.dqh + (((int64_t)b * T + my_row) * p.Hq + head) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x4 v = {dq[db][4 * rq] * p.scale, dq[db][4 * rq + 1] * p.scale,
+                         dq[db][4 * rq + 2] * p.scale, dq[db][4 * rq + 3] * p.scale};
+        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * rq + 4 * hi) = v;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 3. dv and dk_hat. Workgroup = 4 waves = (sequence, KV head, 64 keys); wave w is query head
+// 4 kvh + w. Scores are kept untransposed, S = Q K_hat^T (one key per lane, 16 queries per key
+// block in registers), so P and dS pack into the B operands of dV^T = dO^T P and
+// dK^T = Q^T dS, whose A operands are transposing reads of the staged dO and q_hat rows.
+// Each wave streams its own head's rows 32 queries at a time into two private buffers: no
+// workgroup barrier until the final cross-head sum.
+__global__ __launch_bounds__(kKvWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_kv_kernel(BwdParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int per_tile = p.B * p.Hkv;
+  const int ktile = blockIdx.x / per_tile;  // for full causal attention, tile 0 has the most work
+  const int bh = blockIdx.x - ktile * per_tile;
+  const int b = bh / p.Hkv;
+  const int kvh = bh - b * p.Hkv;
+  const int T = p.T;
+  const int W = p.window;
+  const int k0 = ktile * kNk;
+  const int head = kvh * kG + wave;
+
+  // queries that see a key of the tile: k0 .. min(T, k0 + 63 + W) - 1
+  const int t_end = (W > 0) ? min(T, k0 + kNk - 1 + W) : T;
+  const int n_steps = (t_end - k0 + kStepQ - 1) / kStepQ;
+
+  // V rows of the tile into LDS (shared by the 4 heads; 16 rows per wave), K_hat rows as B
+  // operands in registers: key k0 + 32 kb + l32, dims 16 st + 8 hi .. + 7
+  {
+    const int kv_row_bytes = p.Hkv * kHeadDim * 2;
+    const int row0 = k0 + 16 * wave;
+    const __amdgpu_buffer_rsrc_t r =
+        rsrc_of(p.v + (((int64_t)b * T + row0) * p.Hkv + kvh) * kHeadDim,
+                (int64_t)min(16, T - row0) * kv_row_bytes);
+    const uint32_t base = (uint32_t)(uintptr_t)smem + kKvVTile + 16 * wave * kRow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      lds_dma(base + 4 * i * kRow, (uint32_t)(row * kv_row_bytes + 16 * ((lane & 15) ^ swz(row))), r);
+    }
+  }
+  bf16x8 kB[2][8];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = k0 + 32 * kb + l32;
+    if (key < T) {
+      const int64_t r = ((int64_t)b * T + key) * p.Hkv + kvh;
+      const bf16x8* ks = reinterpret_cast<const bf16x8*>(p.khat + r * kHeadDim + 8 * hi);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) kB[kb][st] = ks[2 * st];
+    } else {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) kB[kb][st] = bf16x8{};
+    }
+  }
+  const bf16x8 one_l = ones3(hi == 0);
+  const bf16x8 one_d = ones3(hi == 1);
+
+  // this wave's stream: rows (b, t, head) of q_hat, dO (256 bytes) and the -L/-D row (32 bytes)
+  const int qrow_bytes = p.Hq * kHeadDim * 2;
+  const int arow_bytes = p.Hq * 16 * 2;
+  const int64_t seq_row0 = (int64_t)b * T * p.Hq + head;  // row index of (b, 0, head)
+  const uint32_t wbase = (uint32_t)(uintptr_t)smem + wave * 2 * kStepBytes;
+  const uint32_t avoff = (uint32_t)((lane >> 1) * arow_bytes + 16 * (lane & 1));
+  auto dma_step = [&](int i) {  // queries k0 + 32 i .. + 31 into buffer i & 1
+    const int t0 = k0 + kStepQ * i;
+    const int n = min(kStepQ, T - t0);
+    const int64_t row = seq_row0 + (int64_t)t0 * p.Hq;
+    const __amdgpu_buffer_rsrc_t rq = rsrc_of(p.qc + row * kHeadDim, (int64_t)n * qrow_bytes);
+    const __amdgpu_buffer_rsrc_t rd = rsrc_of(p.dO + row * kHeadDim, (int64_t)n * qrow_bytes);
+    const __amdgpu_buffer_rsrc_t ra = rsrc_of(p.aux + row * 16, (int64_t)n * arow_bytes);
+    const uint32_t buf = wbase + (i & 1) * kStepBytes;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = 4 * k + (lane >> 4);
+      const uint32_t voff = (uint32_t)(row * qrow_bytes + 16 * ((lane & 15) ^ swz(row)));
+      lds_dma(buf + kQcOff + 4 * k * kRow, voff, rq);
+      lds_dma(buf + kDoOff + 4 * k * kRow, voff, rd);
+    }
+    lds_dma(buf + kAuxOff, avoff, ra);
+  };
+
+  int a_off[8];  // A operand of K step st: staged row l32, dims 16 st + 8 hi
+#pragma unroll
+  for (int st = 0; st < 8; ++st) a_off[st] = l32 * kRow + 16 * ((2 * st + hi) ^ swz(l32));
+  const TrOffsets tr(lane);
+
+  f32x16 dv[4][2], dk[4][2];  // [dim block][key block]: D[dim 32 db + ..][key 32 kb + l32]
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      dv[db][kb] = f32x16{};
+      dk[db][kb] = f32x16{};
+    }
+
+  const unsigned char* vtile = smem + kKvVTile;
+  dma_step(0);
+  vm_wait();
+  __syncthreads();  // every wave's V rows are in LDS
+  for (int i = 0; i < n_steps; ++i) {
+    vm_wait();  // this step's rows are in LDS (the wave's own loads)
+    if (i + 1 < n_steps) dma_step(i + 1);
+    const unsigned char* buf = smem + wave * 2 * kStepBytes + (i & 1) * kStepBytes;
+    const unsigned char* qbuf = buf + kQcOff;
+    const unsigned char* obuf = buf + kDoOff;
+    const bf16x8 auxa = *reinterpret_cast<const bf16x8*>(buf + kAuxOff + 32 * l32 + 16 * hi);
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qbuf + a_off[st]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(a, kB[kb][st], s[kb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(auxa, one_l, s[kb]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(obuf + a_off[st]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        dp[kb] = mfma32(a, *reinterpret_cast<const bf16x8*>(vtile + a_off[st] + kb * 32 * kRow), dp[kb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(auxa, one_d, dp[kb]);
+
+    // masked scores to -inf (P = 0); register r of key block kb is query t0 + 8 (r / 4) + 4 hi +
+    // r % 4 against key k0 + 32 kb + l32. Rows past T were read as zeros, so their dP is finite.
+    const int t0 = k0 + kStepQ * i;
+    if ((t0 < k0 + kNk - 1) || ((W > 0) && (t0 + kStepQ - 1 >= k0 + W)) || (t0 + kStepQ > T)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = k0 + 32 * kb + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = t0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool ok = (key <= t) && (W == 0 || key > t - W) && (t < T);
+          s[kb][r] = ok ? s[kb][r] : -INFINITY;
+        }
+      }
+    }
+    // P = exp2(S - L log2 e), dS = P (dP - D), packed as B operands
+    u32x4 pp[2][2], ps[2][2];  // [key block][query K step]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(s[kb][r]);
+        const float p1 = __builtin_amdgcn_exp2f(s[kb][r + 1]);
+        pp[kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0, p1);
+        ps[kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0 * dp[kb][r], p1 * dp[kb][r + 1]);
+      }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 ao = tr.read(obuf, st, db);
+        const bf16x8 aq = tr.read(qbuf, st, db);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          dv[db][kb] = mfma32(ao, __builtin_bit_cast(bf16x8, pp[kb][st]), dv[db][kb]);
+          dk[db][kb] = mfma32(aq, __builtin_bit_cast(bf16x8, ps[kb][st]), dk[db][kb]);
+        }
+      }
+  }
+
+  // sum over the 4 heads: each wave stores its partial sums, then reduces a quarter of them
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    __syncthreads();  // the buffers (or the previous round's sums) are free
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x16& a = which ? dk[db][kb] : dv[db][kb];
+          red[(wave * 32 + (db * 2 + kb) * 4 + rq) * 64 + lane] =
+              f32x4{a[4 * rq], a[4 * rq + 1], a[4 * rq + 2], a[4 * rq + 3]};
+        }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int blk = 8 * wave + u;
+      f32x4 acc = red[blk * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < kKvWaves; ++w) acc += red[(w * 32 + blk) * 64 + lane];
+      const int db = blk >> 3, kb = (blk >> 2) & 1, rq = blk & 3;
+      const int key = k0 + 32 * kb + l32;
+      if (key < T) {
+        const int64_t r = (((int64_t)b * T + key) * p.Hkv + kvh) * kHeadDim + 32 * db + 8 * rq + 4 * hi;
+        if (which) {
+          *reinterpret_cast<f32x4*>(p.dkh + r) = acc * kLn2;  // scores were in log2 units
+        } else {
+          *reinterpret_cast<u32x2*>(p.dv + r) =
+              u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 4. dx from dx_hat for x_hat = RoPE(RMSNorm(x)) (weight 1): rotate back by the negated angle,
+// then dx = (dxn - xn mean(dxn . xn)) / r with r = sqrt(mean(x^2) + eps). Two lanes per row.
+__global__ __launch_bounds__(256) void prologue_bwd_kernel(BwdParams p, int is_k) {
+  __shared__ float stage[64 * 128];
+  const int lane_pair = threadIdx.x >> 1;
+  const int half = threadIdx.x & 1;
+  const int H = is_k ? p.Hkv : p.Hq;
+  const int64_t row = (int64_t)blockIdx.x * 128 + lane_pair;
+  if (row >= (int64_t)p.B * p.T * H) return;  // both lanes of a pair exit together
+  const int t = (int)((row / H) % p.T);
+  const uint16_t* src = (is_k ? p.k : p.q) + row * kHeadDim + 64 * half;
+  const float* gsrc = (is_k ? p.dkh : p.dqh) + row * kHeadDim + 64 * half;
+  uint16_t* dst = (is_k ? p.dk : p.dq) + row * kHeadDim + 64 * half;
+  float x[64], g[64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unpack8(reinterpret_cast<const u32x4*>(src)[i], x + 8 * i);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(gsrc)[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[4 * i + j] = v[j];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
+  ss += shfl_xor_f(ss, 1);
+  const float inv = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
+  const int h = p.rope.half;
+  if (half == 0 && h > 0) {
+    float* st = stage + lane_pair;  // [dim][row], 128 rows
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if (i < 2 * h) st[i * 128] = g[i];
+#pragma unroll
+    for (int i = 0; i < kMaxRotHalf; ++i) {
+      if (i < h) {
+        float c, s;
+        rope_cs(p.pos0 + t, p.rope.rev[i], c, s);
+        const float a = st[i * 128];
+        const float bb = st[(i + h) * 128];
+        st[i * 128] = a * c + bb * s;
+        st[(i + h) * 128] = bb * c - a * s;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if (i < 2 * h) g[i] = st[i * 128];
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) dot += g[i] * x[i];
+  dot += shfl_xor_f(dot, 1);
+  const float mean = dot * inv * (1.0f / kHeadDim);  // mean(dxn . xn)
+  float dx[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) dx[i] = (g[i] - x[i] * inv * mean) * inv;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) reinterpret_cast<u32x4*>(dst)[i] = pack8(dx + 8 * i);
+}
+
+// ---------------------------------------------------------------------------------------------
+hipError_t launch_backward(const BwdParams& p, hipStream_t s) {
+  const int64_t q_rows = (int64_t)p.B * p.T * p.Hq;
+  const int64_t k_rows = (int64_t)p.B * p.T * p.Hkv;
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((q_rows + 15) / 16)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kQLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_q_kernel, dim3((unsigned)((int64_t)p.n_qtiles * p.B * p.Hkv)),
+                     dim3(kThreads), kQLds, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_kv_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kKvLds);
+  if (e != hipSuccess) return e;
+  const int64_t n_ktiles = (p.T + kNk - 1) / kNk;
+  hipLaunchKernelGGL(bwd_kv_kernel, dim3((unsigned)(n_ktiles * p.B * p.Hkv)), dim3(kKvWaves * 64),
+                     kKvLds, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  hipLaunchKernelGGL(prologue_bwd_kernel, dim3((unsigned)((q_rows + 127) / 128)), dim3(256), 0, s,
+                     p, 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prologue_bwd_kernel, dim3((unsigned)((k_rows + 127) / 128)), dim3(256), 0, s,
+                     p, 1);
+  return hipGetLastError();
+}
+
+}  // namespace zg

@@ -422,6 +422,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   if (my_row < T) {
     const float l_tot = l_run + shfl_xor_f(l_run, 32);
     const float inv = 1.0f / l_tot;
+    if (p.lse && hi == 0)  // scores are in log2 units relative to m_ref
+      p.lse[((int64_t)b * T + my_row) * p.Hq + head] = (m_ref + __log2f(l_tot)) * 0.6931471805599453f;
     const int64_t tok = (int64_t)b * T + my_row;
     uint16_t* dst = p.out + tok * p.so + (int64_t)head * kHeadDim;
     const uint16_t* gsrc = GATED ? p.gate + tok * p.sg + (int64_t)head * kHeadDim : nullptr;

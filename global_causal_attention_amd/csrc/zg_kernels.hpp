@@ -52,6 +52,9 @@ struct PrefillParams {
   // Plain prefill: kv_rows = n_keys = T, qoff = 0.
   int64_t kv_rows;
   int32_t n_keys, qoff;
+  // optional [B, T, Hq] fp32: natural-log log-sum-exp of each query row's scaled scores (general
+  // kernel only; the backward pass recomputes the softmax from it)
+  float* lse;
   float eps;
   float scale_log2;  // softmax scale * log2(e)
   RopeTableH rope;
@@ -97,6 +100,27 @@ struct ToFp8Params {
   float inv_scale;
 };
 hipError_t launch_to_fp8(const ToFp8Params& p, hipStream_t s);
+
+// Backward pass of one attention layer (4 query heads per KV head, head dim 128, packed
+// [B, T, H, 128] tensors, positions 0 .. T-1, norm weights 1).
+struct BwdParams {
+  const uint16_t *q, *k, *v, *gate, *out, *dout;  // bf16 inputs (gate null when ungated)
+  const float* lse;                              // [B, T, Hq] natural log, from the forward
+  uint16_t *dq, *dk, *dv, *dgate;                // bf16 outputs (dgate null when ungated)
+  // workspace
+  uint16_t* qc;    // [B, T, Hq, 128] bf16(q_hat * scale * log2 e), as the forward's operand
+  uint16_t* khat;  // [B, T, Hkv, 128] bf16(k_hat)
+  uint16_t* dO;    // [B, T, Hq, 128] bf16(dout * sigmoid(gate))
+  uint16_t* aux;   // [B, T, Hq, 16] bf16: (-L2 hi, -L2 lo, 0 x 6, -D hi, -D lo, 0 x 6)
+  float* dqh;      // [B, T, Hq, 128] gradient of q_hat
+  float* dkh;      // [B, T, Hkv, 128] gradient of k_hat
+  int32_t B, T, Hq, Hkv, window, gated;
+  int32_t n_qtiles;
+  int64_t pos0;
+  float eps, scale;  // scale: the softmax scale (natural units)
+  RopeTableH rope;
+};
+hipError_t launch_backward(const BwdParams& p, hipStream_t s);
 
 struct RmsNormParams {
   const float* x;

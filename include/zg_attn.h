@@ -113,6 +113,42 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
                                  size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Training: forward with row log-sum-exp, and the backward pass of one attention layer.
+ * (zh-TW translation, section 2.2 and section 3.1 quote training throughput; the layer is the
+ * section 2.1 / Fig. 3 forward above.) Restrictions of these entry points: n_q_heads = 4 *
+ * n_kv_heads (ZGCM-1's 32 / 8), packed tensors (q, gate, out, dout, dq, dgate [B, T, Hq, 128];
+ * k, v, dk, dv [B, T, Hkv, 128], all bf16), positions 0 .. T-1, norm weights 1 (no weight
+ * gradients). Other head ratios -> ZG_ERR_UNSUPPORTED.
+ *
+ * zg_attn_forward_train: out as zg_attn_prefill, plus lse [B, T, Hq] fp32, the natural-log
+ * log-sum-exp of each query row's scaled scores over its key set (what the backward recomputes the
+ * softmax from). workspace >= zg_attn_prefill_workspace_bytes(cfg, B, T).
+ *
+ * zg_attn_backward: gradients of L = sum(dout * out) with respect to q, k, v and the gate logits
+ * (dgate, written only when cfg->gated), given the forward's inputs, its out and lse:
+ *   dO = dout * sigmoid(gate) (dout when ungated), dgate = dout * out * (1 - sigmoid(gate)),
+ *   D = rowsum(dout * out), P = exp(scale q_hat . k_hat - lse), dS = P (dO . v - D),
+ *   dv = P^T dO, dq_hat = scale dS k_hat, dk_hat = scale dS^T q_hat, and dq, dk through RoPE's
+ *   transpose and RMSNorm's derivative. dq, dk, dv, dgate are overwritten (bf16).
+ * Numerics: q_hat, k_hat, dO, P and dS are rounded to bf16 at the matrix-core inputs; sums and the
+ * norm/RoPE derivatives are fp32.
+ *   workspace >= zg_attn_backward_workspace_bytes(cfg, B, T) (bf16 q_hat, k_hat, dO, a 32-byte row
+ *   per query for lse and D, fp32 dq_hat and dk_hat: about B T (1056 Hq + 768 Hkv) bytes).
+ * Errors: NULL -> ZG_ERR_NULL; B < 1, T < 1 -> ZG_ERR_SHAPE; unsupported head ratio, head_dim,
+ * rot_dim, or T * Hq * 256 bytes >= 4 GiB -> ZG_ERR_UNSUPPORTED; small workspace ->
+ * ZG_ERR_WORKSPACE. */
+zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, const void* q,
+                                const void* k, const void* v, const void* gate, void* out,
+                                float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t zg_attn_backward_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T);
+
+zg_status zg_attn_backward(const zg_attn_cfg* cfg, int32_t B, int32_t T, const void* q,
+                           const void* k, const void* v, const void* gate, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* dgate, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Decode: one new token per sequence, attending over a KV cache of normalised, rotated keys.
  * (zh-TW translation, section 2.3: local layers keep a fixed 128-token window, global layers keep
  * the whole sequence; decoding is memory-bandwidth bound.)
