@@ -375,6 +375,11 @@ void bwd_kv_kernel(BwdParams p) {
       for (int st = 0; st < 8; ++st) kB[kb][st] = bf16x8{};
     }
   }
+  vm_wait();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(kB[kb][st]));  // loaded: no waits in the loop
   const bf16x8 one_l = ones3(hi == 0);
   const bf16x8 one_d = ones3(hi == 1);
 
@@ -427,68 +432,112 @@ void bwd_kv_kernel(BwdParams p) {
     const unsigned char* qbuf = buf + kQcOff;
     const unsigned char* obuf = buf + kDoOff;
     const bf16x8 auxa = *reinterpret_cast<const bf16x8*>(buf + kAuxOff + 32 * l32 + 16 * hi);
+    const int t0 = k0 + kStepQ * i;
+    const bool need_mask =
+        (t0 < k0 + kNk - 1) || ((W > 0) && (t0 + kStepQ - 1 >= k0 + W)) || (t0 + kStepQ > T);
+
+    // Scores and dP, 18 slots of two MFMAs (one per key block): slots 0-7 S over dims 16 st,
+    // slot 8 subtracts L log2 e, slots 9-16 dP, slot 17 subtracts D. A operands are read two
+    // slots ahead, the V rows (dP's B operands) likewise. Slots 9-16 also turn the finished
+    // scores into P = exp2(S) and pack P as dV's B operand.
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
     }
+    auto opA = [&](int k) -> bf16x8 {
+      if (k < 8) return *reinterpret_cast<const bf16x8*>(qbuf + a_off[k]);
+      if (k == 8 || k == 17) return auxa;
+      return *reinterpret_cast<const bf16x8*>(obuf + a_off[k - 9]);
+    };
+    auto opV = [&](int k, int kb) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(vtile + a_off[k - 9] + kb * 32 * kRow);
+    };
+    u32x4 pp[2][2], ps[2][2];  // [key block][query K step]: P and dS as B operands
+    bf16x8 ra[2], rv[2][2];
+    ra[0] = opA(0);
+    ra[1] = opA(1);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qbuf + a_off[st]);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(a, kB[kb][st], s[kb]);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(auxa, one_l, s[kb]);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(obuf + a_off[st]);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        dp[kb] = mfma32(a, *reinterpret_cast<const bf16x8*>(vtile + a_off[st] + kb * 32 * kRow), dp[kb]);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(auxa, one_d, dp[kb]);
-
-    // masked scores to -inf (P = 0); register r of key block kb is query t0 + 8 (r / 4) + 4 hi +
-    // r % 4 against key k0 + 32 kb + l32. Rows past T were read as zeros, so their dP is finite.
-    const int t0 = k0 + kStepQ * i;
-    if ((t0 < k0 + kNk - 1) || ((W > 0) && (t0 + kStepQ - 1 >= k0 + W)) || (t0 + kStepQ > T)) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = k0 + 32 * kb + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = t0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = (key <= t) && (W == 0 || key > t - W) && (t < T);
-          s[kb][r] = ok ? s[kb][r] : -INFINITY;
-        }
+    for (int k = 0; k < 18; ++k) {
+      const bf16x8 a = ra[k & 1];
+      if (k + 2 < 18) ra[k & 1] = opA(k + 2);
+      bf16x8 b0, b1;
+      if (k < 8) {
+        b0 = kB[0][k];
+        b1 = kB[1][k];
+      } else if (k == 8) {
+        b0 = one_l;
+        b1 = one_l;
+      } else if (k < 17) {
+        b0 = rv[k & 1][0];
+        b1 = rv[k & 1][1];
+      } else {
+        b0 = one_d;
+        b1 = one_d;
       }
-    }
-    // P = exp2(S - L log2 e), dS = P (dP - D), packed as B operands
-    u32x4 pp[2][2], ps[2][2];  // [key block][query K step]
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(s[kb][r]);
-        const float p1 = __builtin_amdgcn_exp2f(s[kb][r + 1]);
-        pp[kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0, p1);
-        ps[kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0 * dp[kb][r], p1 * dp[kb][r + 1]);
+      if (k + 2 >= 9 && k + 2 <= 16) {
+        rv[k & 1][0] = opV(k + 2, 0);
+        rv[k & 1][1] = opV(k + 2, 1);
       }
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 ao = tr.read(obuf, st, db);
-        const bf16x8 aq = tr.read(qbuf, st, db);
+      if (k < 9) {
+        s[0] = mfma32(a, b0, s[0]);
+        s[1] = mfma32(a, b1, s[1]);
+      } else {
+        dp[0] = mfma32(a, b0, dp[0]);
+        dp[1] = mfma32(a, b1, dp[1]);
+      }
+      if (k == 8 && need_mask) {
+        // register r of key block kb: query t0 + 8 (r / 4) + 4 hi + r % 4, key k0 + 32 kb + l32;
+        // masked scores become -inf (P = 0). Rows past T were read as zeros: their dP is finite.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          dv[db][kb] = mfma32(ao, __builtin_bit_cast(bf16x8, pp[kb][st]), dv[db][kb]);
-          dk[db][kb] = mfma32(aq, __builtin_bit_cast(bf16x8, ps[kb][st]), dk[db][kb]);
+          const int key = k0 + 32 * kb + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = t0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = (key <= t) && (W == 0 || key > t - W) && (t < T);
+            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+          }
         }
       }
+      if (k >= 9 && k < 17) {  // 4 of the 32 weights: key block kb, registers 4 c .. 4 c + 3
+        const int kb = (k - 9) >> 2, c = (k - 9) & 3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[kb][4 * c + j] = __builtin_amdgcn_exp2f(s[kb][4 * c + j]);
+        pp[kb][c >> 1][2 * (c & 1)] = pack_bf16(s[kb][4 * c], s[kb][4 * c + 1]);
+        pp[kb][c >> 1][2 * (c & 1) + 1] = pack_bf16(s[kb][4 * c + 2], s[kb][4 * c + 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // dV^T += dO^T P over 8 slots (dim block db, query K step st), each slot also forming 4 of
+    // the dS = P (dP - D) weights; then dK^T += Q^T dS. Transposing reads two slots ahead.
+    auto opT = [&](int k) { return tr.read(k < 8 ? obuf : qbuf, (k & 7) >> 2, k & 3); };
+    bf16x8 rt[2];
+    rt[0] = opT(0);
+    rt[1] = opT(1);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int st = (k & 7) >> 2, db = k & 3;
+      const bf16x8 a = rt[k & 1];
+      if (k + 2 < 16) rt[k & 1] = opT(k + 2);
+      if (k < 8) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          dv[db][kb] = mfma32(a, __builtin_bit_cast(bf16x8, pp[kb][st]), dv[db][kb]);
+        const int kb = k >> 2, c = k & 3;  // dS of key block kb, registers 4 c .. 4 c + 3
+        ps[kb][c >> 1][2 * (c & 1)] =
+            pack_bf16(s[kb][4 * c] * dp[kb][4 * c], s[kb][4 * c + 1] * dp[kb][4 * c + 1]);
+        ps[kb][c >> 1][2 * (c & 1) + 1] =
+            pack_bf16(s[kb][4 * c + 2] * dp[kb][4 * c + 2], s[kb][4 * c + 3] * dp[kb][4 * c + 3]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          dk[db][kb] = mfma32(a, __builtin_bit_cast(bf16x8, ps[kb][st]), dk[db][kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // sum over the 4 heads: each wave stores its partial sums, then reduces a quarter of them
