@@ -68,6 +68,7 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer stack")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked prefill")
     ap.add_argument("--no-sweep", action="store_true", help="skip the context sweep")
+    ap.add_argument("--no-backward", action="store_true", help="skip the training (backward) layers")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the timed 5:1 block (profiling the other workloads alone; value null)")
     args = ap.parse_args()
@@ -107,6 +108,8 @@ def main():
         result["chunked_prefill"] = bench_chunked(torch, zg, si, dev, stream)
     if not args.no_sweep:
         result["context_sweep"] = bench_sweep(torch, zg, si, dev, stream)
+    if not args.no_backward:
+        result["training"] = bench_backward(torch, zg, si, dev, stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, si)
@@ -434,6 +437,46 @@ def bench_chunked(torch, zg, si, dev, stream, Bc=4, ctx=16384, Tc=2048):
         log(f"[bench] chunked {name}: {ms:.3f} ms")
         del kc, vc, ws
     del x, out
+    return res
+
+
+def bench_backward(torch, zg, si, dev, stream, Bb=B, Tb=T):
+    """Training layers at the prefill shape: forward with the row log-sum-exp, then the backward
+    pass (dq, dk, dv, dgate), for a gated local layer (W=128) and an ungated global layer (base
+    1e6). FLOPs follow the usual convention: forward 4 D per (query, key) pair and head, backward
+    2.5 times that (the score recomputation included). The local layer's minimum HBM traffic is
+    its inputs and outputs once: q, gate, out, dout, dq, dgate ([B, T, Hq, D] bf16), k, v, dk, dv
+    ([B, T, Hkv, D] bf16) and lse."""
+    log(f"[bench] training layers: B={Bb} T={Tb}")
+    gen = si.generator(1007, device="cuda")
+    res = {"workload": f"B={Bb}, T={Tb}, Hq=32 Hkv=8 D=128, rot 42, base 1e6: forward with "
+                       f"log-sum-exp + backward (dq, dk, dv, dgate)"}
+    total = 0.0
+    for name, win in (("swa", W), ("global", 0)):
+        x = si.prefill_layer(gen, Bb, Tb, HQ, HKV, D, gated=win > 0, device="cuda")
+        dy = si.randn_bf16(gen, (Bb, Tb, HQ, D), device="cuda")
+        cfg = zg.AttnConfig(window=win, gated=win > 0, rope_base=ROPE_BASE)
+        g = x["gate"] if win else None
+        out, lse = zg.zg_attn_forward_train(cfg, x["q"], x["k"], x["v"], g)
+        fws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, Bb, Tb), dtype=torch.uint8, device=dev)
+        bws = torch.empty(zg.zg_attn_backward_workspace_bytes(cfg, Bb, Tb), dtype=torch.uint8, device=dev)
+        f_ms = _time(torch, stream, lambda: zg.zg_attn_forward_train(
+            cfg, x["q"], x["k"], x["v"], g, out=out, lse=lse, workspace=fws), 5)
+        b_ms = _time(torch, stream, lambda: zg.zg_attn_backward(
+            cfg, x["q"], x["k"], x["v"], g, out, dy, lse, workspace=bws), 5)
+        flop = Bb * HQ * n_pairs(Tb, win) * 4 * D
+        r = {"fwd_ms": round(f_ms, 3), "bwd_ms": round(b_ms, 3),
+             "bwd_TFLOPs": round(2.5 * flop / (b_ms * 1e-3) / 1e12, 1),
+             "bwd_mfma_frac": round(2.5 * flop / (b_ms * 1e-3) / MFMA_BF16_PEAK, 4)}
+        if win:
+            nbytes = Bb * Tb * (HQ * D * 2 * 6 + HKV * D * 2 * 4 + HQ * 4)
+            r.update({"bwd_min_bytes": nbytes, "bwd_hbm_frac": round(nbytes / (b_ms * 1e-3) / HBM_PEAK, 4)})
+        res[name] = r
+        total += (5 if win else 1) * (f_ms + b_ms)
+        log(f"[bench] training {name}: fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms")
+        del x, dy, out, lse, fws, bws
+    res["block_5to1_ms"] = round(total, 3)
+    res["block_5to1_tokens_per_s"] = round(Bb * Tb / (total * 1e-3), 1)
     return res
 
 

@@ -246,6 +246,13 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = f32x16{};
 
+  // the operands above are loaded: pinning them here keeps the loop free of waits on them (which
+  // would also wait for the tile loads in flight)
+  vm_wait();
+#pragma unroll
+  for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(qf[st]), "+v"(dof[st]));
+  asm volatile("" : "+v"(auxb));
+
   dma_tile(0);
   vm_wait();
   __syncthreads();
@@ -253,52 +260,79 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
     if (j + 1 < n_tiles) dma_tile(j + 1);
     const unsigned char* kbuf = smem + (j & 1) * kTileBytes;
     const unsigned char* vbuf = smem + 2 * kTileBytes + (j & 1) * kTileBytes;
+    const int kt = k_begin + j * kNk;
+    const bool need_mask = (kt + kNk - 1 > qbase) || ((W > 0) && (kt < qbase + 31 - W + 1));
+
+    // S^T and dP^T in 18 slots of two MFMAs (one per key block): slots 0-7 S over dims 16 st,
+    // slot 8 subtracts L log2 e, slots 9-16 dP, slot 17 subtracts D. Slots 9-16 also turn the
+    // finished scores into P = exp2(S).
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
     }
+    auto opA = [&](int k, int kb) -> bf16x8 {
+      if (k < 8) return rd_a(kbuf, k, kb);
+      if (k == 8) return one_l;
+      if (k == 17) return one_d;
+      return rd_a(vbuf, k - 9, kb);
+    };
+    bf16x8 ra0 = opA(0, 0);
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int k = 0; k < 18; ++k) {
+      // key block 0's operand was read a slot ahead; key block 1's is read now and used by the
+      // slot's second MFMA
+      const bf16x8 a0 = ra0, a1 = opA(k, 1);
+      if (k + 1 < 18) ra0 = opA(k + 1, 0);
+      const bf16x8 bq = (k < 8) ? qf[k] : (k == 8 || k == 17) ? auxb : dof[k - 9];
+      if (k < 9) {
+        s[0] = mfma32(a0, bq, s[0]);
+        s[1] = mfma32(a1, bq, s[1]);
+      } else {
+        dp[0] = mfma32(a0, bq, dp[0]);
+        dp[1] = mfma32(a1, bq, dp[1]);
+      }
+      if (k == 8 && need_mask) {
+        // masked scores to -inf (P = 0); register r of key block kb is key kt + 32 kb +
+        // 8 (r / 4) + 4 hi + r % 4 of this lane's query
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(rd_a(kbuf, st, kb), qf[st], s[kb]);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(one_l, auxb, s[kb]);
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = (key <= my_row) && (W == 0 || key > my_row - W);
+            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+          }
+      }
+      if (k >= 9 && k < 17) {
+        const int kb = (k - 9) >> 2, c = (k - 9) & 3;
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(rd_a(vbuf, st, kb), dof[st], dp[kb]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(one_d, auxb, dp[kb]);
-
-    // masked scores to -inf (P = 0); register r of key block kb is key kt + 32 kb + 8 (r / 4) +
-    // 4 hi + r % 4 of this lane's query
-    const int kt = k_begin + j * kNk;
-    if ((kt + kNk - 1 > qbase) || ((W > 0) && (kt < qbase + 31 - W + 1))) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = (key <= my_row) && (W == 0 || key > my_row - W);
-          s[kb][r] = ok ? s[kb][r] : -INFINITY;
-        }
+        for (int jj = 0; jj < 4; ++jj) s[kb][4 * c + jj] = __builtin_amdgcn_exp2f(s[kb][4 * c + jj]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // dS = P (dP - D) with P = exp2(S - L log2 e)
+
+    // dS = P (dP - D) packed as dQ^T's B operand: pk[st] holds key step st (key block st / 2,
+    // registers 8 (st % 2) .. + 7); dQ^T += K^T dS^T over 16 slots (key step st, dim block db),
+    // transposing reads one slot ahead, slot (st, c) forming pair c of pk[st + 1]
     u32x4 pk[4];
+    auto form = [&](int st, int c) {
+      const int kb = st >> 1, r = 8 * (st & 1) + 2 * c;
+      pk[st][c] = pack_bf16(s[kb][r] * dp[kb][r], s[kb][r + 1] * dp[kb][r + 1]);
+    };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int c = 0; c < 4; ++c) form(0, c);
+    bf16x8 rt = tr.read(kbuf, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; r += 2)
-        pk[2 * kb + (r >> 3)][(r >> 1) & 3] =
-            pack_bf16(__builtin_amdgcn_exp2f(s[kb][r]) * dp[kb][r],
-                      __builtin_amdgcn_exp2f(s[kb][r + 1]) * dp[kb][r + 1]);
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        dq[db] = mfma32(tr.read(kbuf, st, db), __builtin_bit_cast(bf16x8, pk[st]), dq[db]);
+    for (int k = 0; k < 16; ++k) {
+      const int st = k >> 2, db = k & 3;
+      const bf16x8 a = rt;
+      if (k + 1 < 16) rt = tr.read(kbuf, (k + 1) >> 2, (k + 1) & 3);
+      dq[db] = mfma32(a, __builtin_bit_cast(bf16x8, pk[st]), dq[db]);
+      if (st < 3) form(st + 1, db);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     vm_wait();
     __syncthreads();
   }
