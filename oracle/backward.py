@@ -102,3 +102,94 @@ def row_lse(q, k, *, window, rot_dim=42, rope_base=1e4, eps=1e-6, scale=None, po
             m = np.max(s, axis=1)
             out[b, t] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
     return out
+
+
+def layer_backward_rows(q, k, v, gate, dy, *, window, gated, q_rows, k_rows, rot_dim=42,
+                        rope_base=1e4, eps=1e-6, scale=None, pos0=0):
+    """The gradients of layer_backward for ONE sequence, evaluated only where asked: dq (and
+    dgate) at query rows `q_rows`, dk and dv at key rows `k_rows`, plus the natural-log row
+    log-sum-exp at `q_rows`. q, gate, dy: [T, Hq, D]; k, v: [T, Hkv, D] (any float dtype, widened
+    to fp64 row by row). Same chain rule as layer_backward, restricted to the rows it touches:
+
+      dq[t]  needs row t's softmax (its key set), dP[t, j] = dO[t] . v[j] and D[t] = sum_j P dP;
+      dk[j], dv[j] sum over the queries t whose key set holds j (t in [j, j + W) or [j, T)), each
+             needing its own full softmax row and D[t].
+
+    Returns (dq [len(q_rows), Hq, D], dk [len(k_rows), Hkv, D], dv [len(k_rows), Hkv, D],
+    dgate [len(q_rows), Hq, D] or None, lse [len(q_rows), Hq])."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+    q_rows = [int(t) for t in q_rows]
+    k_rows = [int(j) for j in k_rows]
+
+    # queries whose softmax rows are needed, and the keys those rows read
+    need_t = set(q_rows)
+    for j in k_rows:
+        hi = min(T, j + window) if window > 0 else T
+        need_t.update(range(j, hi))
+    need_t = sorted(need_t)
+    k_lo = min(key_set(t, window)[0] for t in need_t)
+    k_hi = max(need_t) + 1
+    keys = np.arange(k_lo, k_hi)
+    kh = qk_prologue(f64(k[k_lo:k_hi]), pos0 + keys, None, rot_dim=rot_dim, rope_base=rope_base,
+                     eps=eps)                                              # [nk, Hkv, D]
+    vk = f64(v[k_lo:k_hi])
+
+    rows = {}  # t -> (qhat [Hq, D], P [Hq, n], dO [Hq, D], dS [Hq, n], lo, o [Hq, D])
+    for t in need_t:
+        lo, hi = key_set(t, window)
+        qh = qk_prologue(f64(q[t])[None], np.array([pos0 + t]), None, rot_dim=rot_dim,
+                         rope_base=rope_base, eps=eps)[0]                  # [Hq, D]
+        P = np.empty((Hq, hi - lo))
+        o = np.empty((Hq, D))
+        dO = f64(dy[t]).copy()
+        dP = np.empty((Hq, hi - lo))
+        for h in range(Hq):
+            c = h // G
+            s = scale * kh[lo - k_lo:hi - k_lo, c] @ qh[h]
+            m = s.max()
+            e = np.exp(s - m)
+            P[h] = e / e.sum()
+            o[h] = P[h] @ vk[lo - k_lo:hi - k_lo, c]
+        if gated:
+            sg = _sigmoid(f64(gate[t]))
+            dO = dO * sg
+        for h in range(Hq):
+            dP[h] = vk[lo - k_lo:hi - k_lo, h // G] @ dO[h]
+        Dt = np.sum(P * dP, axis=1, keepdims=True)
+        rows[t] = (qh, P, dO, P * (dP - Dt), lo, o)
+
+    dq = np.empty((len(q_rows), Hq, D))
+    dg = np.empty((len(q_rows), Hq, D)) if gated else None
+    lse = np.empty((len(q_rows), Hq))
+    for n, t in enumerate(q_rows):
+        qh, P, dO, dS, lo, o = rows[t]
+        hi = t + 1
+        dqh = np.stack([scale * dS[h] @ kh[lo - k_lo:hi - k_lo, h // G] for h in range(Hq)])
+        dq[n] = _prologue_backward(f64(q[t])[None], np.array([pos0 + t]), dqh[None],
+                                   rot_dim=rot_dim, rope_base=rope_base, eps=eps)[0]
+        for h in range(Hq):
+            s = scale * kh[lo - k_lo:hi - k_lo, h // G] @ qh[h]
+            lse[n, h] = s.max() + np.log(np.sum(np.exp(s - s.max())))
+        if gated:
+            sg = _sigmoid(f64(gate[t]))
+            dg[n] = f64(dy[t]) * o * sg * (1.0 - sg)
+
+    dk = np.zeros((len(k_rows), Hkv, D))
+    dv = np.zeros((len(k_rows), Hkv, D))
+    for n, j in enumerate(k_rows):
+        dkh = np.zeros((Hkv, D))
+        hi = min(T, j + window) if window > 0 else T
+        for t in range(j, hi):
+            qh, P, dO, dS, lo, _ = rows[t]
+            for h in range(Hq):
+                c = h // G
+                dv[n, c] += P[h, j - lo] * dO[h]
+                dkh[c] += scale * dS[h, j - lo] * qh[h]
+        dk[n] = _prologue_backward(f64(k[j])[None], np.array([pos0 + j]), dkh[None],
+                                   rot_dim=rot_dim, rope_base=rope_base, eps=eps)[0]
+    return dq, dk, dv, dg, lse

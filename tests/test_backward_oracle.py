@@ -56,3 +56,25 @@ def test_row_lse_direct():
             lo = max(0, t - 2)
             s = [qh[t, h] @ kh[j, h // 2] / 4.0 for j in range(lo, t + 1)]
             assert abs(lse[0, t, h] - np.log(np.sum(np.exp(s)))) < 1e-12
+
+
+@pytest.mark.parametrize("window,gated", [(0, False), (3, True), (5, False), (0, True)])
+def test_backward_rows_match_whole_sequence(window, gated):
+    """The row-sampled backward (used at the full bench size, where the whole-sequence form is too
+    slow) equals the whole-sequence one (pinned above by finite differences) on every row, and its
+    log-sum-exp equals row_lse."""
+    B, T, Hq, Hkv, D = 2, 11, 4, 2, 16
+    q, k, v, g, dy = _case(40 + window, B, T, Hq, Hkv, D, gated)
+    kw = dict(window=window, gated=gated, rot_dim=6, rope_base=100.0, eps=1e-6, pos0=2)
+    dq, dk, dv, dg = oracle.layer_backward(q, k, v, g, dy, **kw)
+    lse = oracle.row_lse(q, k, window=window, rot_dim=6, rope_base=100.0, eps=1e-6, pos0=2)
+    rows_q, rows_k = [0, 3, 4, 10], [0, 1, 6, 9, 10]
+    for b in range(B):
+        rq, rk, rv, rg, rl = oracle.layer_backward_rows(
+            q[b], k[b], v[b], None if g is None else g[b], dy[b], q_rows=rows_q, k_rows=rows_k, **kw)
+        np.testing.assert_allclose(rq, dq[b, rows_q], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rk, dk[b, rows_k], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rv, dv[b, rows_k], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rl, lse[b, rows_q], rtol=1e-12, atol=1e-12)
+        if gated:
+            np.testing.assert_allclose(rg, dg[b, rows_q], rtol=1e-10, atol=1e-12)

@@ -97,3 +97,63 @@ def test_backward_rejects_unsupported_ratio():
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
     with pytest.raises(zg.ZGError):
         zg.zg_attn_forward_train(cfg, q, k, v)
+
+
+def _sample_rows(gen, T, fixed, n_rand):
+    r = torch.randint(0, T, (n_rand,), generator=gen).tolist()
+    return sorted(set(int(t) for t in list(fixed) + r if 0 <= t < T))
+
+
+@pytest.mark.parametrize("layer", ["swa", "global"])
+def test_backward_fullsize_sampled(layer):
+    """B=4, T=16384 with the inputs and launch configuration of bench.py's training layers (the
+    same seed and draw order): the whole backward runs on the GPU; dq, dgate and the log-sum-exp
+    are checked on sampled query rows and dk, dv on sampled key rows of the first and last
+    sequence, against the row-restricted chain rule (oracle.layer_backward_rows). For the global
+    layer the sampled keys sit in the last 64 positions, whose query sets are short enough for the
+    oracle; every sampled query row reads its whole prefix."""
+    B, T, Hq, Hkv = 4, 16384, 32, 8
+    print(f"[case] backward full size {layer} B={B} T={T}", flush=True)
+    gen = si.generator(1007, device="cuda")
+    for name, win in (("swa", 128), ("global", 0)):  # bench.py's draw order
+        x = si.prefill_layer(gen, B, T, Hq, Hkv, D, gated=win > 0, device="cuda")
+        dy = si.randn_bf16(gen, (B, T, Hq, D), device="cuda")
+        if name == layer:
+            break
+    W, gated = (128, True) if layer == "swa" else (0, False)
+    cfg = zg.AttnConfig(window=W, gated=gated, rope_base=1e6)
+    g = x["gate"] if gated else None
+    out, lse = zg.zg_attn_forward_train(cfg, x["q"], x["k"], x["v"], g)
+    dq, dk, dv, dg = zg.zg_attn_backward(cfg, x["q"], x["k"], x["v"], g, out, dy, lse)
+    torch.cuda.synchronize()
+
+    pick = torch.Generator().manual_seed(5)
+    got = {n: [] for n in ("dq", "dk", "dv", "dgate", "lse")}
+    ref = {n: [] for n in got}
+    for b in (0, B - 1):
+        q_rows = _sample_rows(pick, T, [0, 1, 63, 64, 127, 128, 2047, 2048, 8191, T - 65, T - 64,
+                                        T - 2, T - 1], 4)
+        if W:
+            k_rows = _sample_rows(pick, T, [0, 63, 64, 4095, T - 129, T - 1], 3)
+        else:
+            k_rows = [T - 64, T - 63, T - 33, T - 2, T - 1]
+        cpu = lambda t: t[b].float().cpu().numpy()
+        rq, rk, rv, rg, rl = oracle.layer_backward_rows(
+            cpu(x["q"]), cpu(x["k"]), cpu(x["v"]), cpu(g) if gated else None, cpu(dy),
+            window=W, gated=gated, q_rows=q_rows, k_rows=k_rows, rope_base=1e6)
+        got["dq"].append(f64(dq[b, q_rows])); ref["dq"].append(rq)
+        got["dk"].append(f64(dk[b, k_rows])); ref["dk"].append(rk)
+        got["dv"].append(f64(dv[b, k_rows])); ref["dv"].append(rv)
+        got["lse"].append(f64(lse[b, q_rows])); ref["lse"].append(rl)
+        if gated:
+            got["dgate"].append(f64(dg[b, q_rows])); ref["dgate"].append(rg)
+    lse_err = float(np.abs(np.concatenate(got["lse"]) - np.concatenate(ref["lse"])).max())
+    print(f"[parity] lse: max_abs={lse_err:.3e}", flush=True)
+    assert lse_err <= LSE_ABS
+    for name in ("dq", "dk", "dv", "dgate"):
+        if not ref[name]:
+            continue
+        rel_max, rel_rms = _check(torch.from_numpy(np.concatenate(got[name])),
+                                  np.concatenate(ref[name]), name)
+        assert rel_rms <= REL_RMS, f"{name}: relative RMS error {rel_rms:.3e}"
+        assert rel_max <= REL_MAX, f"{name}: max error {rel_max:.3e} of max|ref|"
