@@ -293,8 +293,7 @@ zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, co
 size_t zg_attn_backward_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
   if (!cfg || B < 1 || T < 1 || cfg->n_q_heads < 1 || cfg->n_kv_heads < 1) return 0;
   const size_t bt = (size_t)B * T, hq = cfg->n_q_heads, hk = cfg->n_kv_heads;
-  return 2 * align256(bt * hq * kD * 2) + align256(bt * hk * kD * 2) + align256(bt * hq * 16 * 2) +
-         align256(bt * hq * kD * 4) + align256(bt * hk * kD * 4);
+  return 2 * align256(bt * hq * kD * 2) + align256(bt * hk * kD * 2) + align256(bt * hq * 16 * 2);
 }
 
 zg_status zg_attn_backward(const zg_attn_cfg* cfg, int32_t B, int32_t T, const void* q,
@@ -328,10 +327,6 @@ zg_status zg_attn_backward(const zg_attn_cfg* cfg, int32_t B, int32_t T, const v
     bp.khat = reinterpret_cast<uint16_t*>(ws);
     ws += align256(bt * Hkv * kD * 2);
     bp.aux = reinterpret_cast<uint16_t*>(ws);
-    ws += align256(bt * Hq * 16 * 2);
-    bp.dqh = reinterpret_cast<float*>(ws);
-    ws += align256(bt * Hq * kD * 4);
-    bp.dkh = reinterpret_cast<float*>(ws);
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const zg::RopeTableH rt = rope_table(cfg);

@@ -13,14 +13,15 @@
 //  1. bwd_pre   per (token, query head): dO = dy * sigmoid(g), dg = dy * y * (1 - sigmoid(g)),
 //               D = sum dy * y, and a 16-value bf16 row (-L log2 e and -D, each split exactly into
 //               three bf16 terms) that an extra matrix-core step subtracts from the scores.
-//  2. bwd_q     per (sequence, KV head, 64 queries): streams K_hat/V tiles like the forward and
-//               accumulates dq_hat = scale * dS K_hat.
-//  3. bwd_kv    per (sequence, KV head, 64 keys): keeps the tile's K_hat and V as matrix-core
-//               operands in registers, one wave per query head streams that head's rows
-//               (q_hat, dO, the -L/-D row) through its own LDS buffers, accumulates
-//               dV = P^T dO and dk_hat = scale * dS^T q_hat; the 4 heads' sums meet in LDS.
-//  4. prologue_bwd  dq, dk from dq_hat, dk_hat through RoPE (rotation by the negated angle) and
-//               RMSNorm (weight 1).
+//  2. bwd_q     per (sequence, KV head, 64 queries): streams K_hat/V tiles like the forward,
+//               accumulates dq_hat = scale * dS K_hat and turns it into dq in its epilogue.
+//  3. bwd_kv    per (sequence, KV head, 64 keys): keeps the tile's K_hat as matrix-core operands
+//               in registers and its V rows in LDS, one wave per query head streams that head's
+//               rows (q_hat, dO, the -L/-D row) through its own LDS buffers, accumulates
+//               dV = P^T dO and dk_hat = scale * dS^T q_hat; the 4 heads' sums meet in LDS and
+//               dk_hat becomes dk in the epilogue.
+// The epilogues take x_hat's gradient back through RoPE (rotation by the negated angle) and
+// RMSNorm (weight 1) from rows staged in LDS.
 #include "zg_mfma.hpp"
 
 namespace zg {
@@ -109,6 +110,61 @@ struct TrOffsets {
     return __builtin_bit_cast(bf16x8, both);
   }
 };
+
+constexpr int kStageRow = 132;  // floats per staged fp32 row: 528 bytes, rows 4 banks apart
+
+// dx of one 128-dim row from its x_hat gradient staged in LDS (fp32 at `srow`, rotated in place)
+// for x_hat = RoPE(RMSNorm(x)), weight 1, at position pos: rotate back by the negated angle, then
+// dx = (dxn - xn mean(dxn . xn)) / r with r = sqrt(mean(x^2) + eps). Two adjacent lanes per row
+// (half = lane & 1 holds dims 64 half .. +63; the rotated dims all lie in half 0); x and dx are bf16
+// rows in global memory.
+__device__ __forceinline__ void dx_from_staged(float* srow, const uint16_t* xrow, uint16_t* drow,
+                                               int half, int64_t pos, const RopeTableH& rt,
+                                               float eps) {
+  const int h = rt.half;
+  if (half == 0 && h > 0) {
+#pragma unroll
+    for (int i = 0; i < kMaxRotHalf; ++i) {
+      if (i < h) {
+        float c, s;
+        rope_cs(pos, rt.rev[i], c, s);
+        const float a = srow[i];
+        const float b = srow[i + h];
+        srow[i] = a * c + b * s;
+        srow[i + h] = b * c - a * s;
+      }
+    }
+  }
+  float g[64], x[64];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(srow + 64 * half + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[4 * i + j] = v[j];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unpack8(reinterpret_cast<const u32x4*>(xrow + 64 * half)[i], x + 8 * i);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
+  ss += shfl_xor_f(ss, 1);
+  const float inv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) dot += g[i] * x[i];
+  dot += shfl_xor_f(dot, 1);
+  const float mean = dot * inv * (1.0f / kHeadDim);  // mean(dxn . xn)
+  float dx[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) dx[i] = (g[i] - x[i] * inv * mean) * inv;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) reinterpret_cast<u32x4*>(drow + 64 * half)[i] = pack8(dx + 8 * i);
+}
+
+constexpr int kQStageLds = kWaves * 32 * kStageRow * 4;  // bwd_q epilogue: 32 rows per wave
+constexpr int kQLdsTotal = kQStageLds > kQLds ? kQStageLds : kQLds;
+static_assert(kQLdsTotal <= 160 * 1024, "LDS budget");
+static_assert(64 * kStageRow * 4 <= kKvVTile, "bwd_kv epilogue staging fits");
 
 }  // namespace
 
@@ -337,16 +393,25 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
     __syncthreads();
   }
 
-  if (valid) {
-    float* dst = p.dqh + (((int64_t)b * T + my_row) * p.Hq + head) * kHeadDim;
+  // epilogue: dq_hat rows (one query per lane, 4 dims per register group) staged in the freed
+  // tile buffers, then dq with two lanes per row
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * kStageRow;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const f32x4 v = {dq[db][4 * rq] * p.scale, dq[db][4 * rq + 1] * p.scale,
-                         dq[db][4 * rq + 2] * p.scale, dq[db][4 * rq + 3] * p.scale};
-        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * rq + 4 * hi) = v;
-      }
+    for (int rq = 0; rq < 4; ++rq) {
+      const f32x4 v = {dq[db][4 * rq] * p.scale, dq[db][4 * rq + 1] * p.scale,
+                       dq[db][4 * rq + 2] * p.scale, dq[db][4 * rq + 3] * p.scale};
+      *reinterpret_cast<f32x4*>(stage + l32 * kStageRow + 32 * db + 8 * rq + 4 * hi) = v;
+    }
+  __syncthreads();
+  {
+    const int r = lane >> 1, half = lane & 1;
+    const int t = qbase + r;
+    if (t < T) {  // both lanes of a row agree
+      const int64_t row = (((int64_t)b * T + t) * p.Hq + head) * kHeadDim;
+      dx_from_staged(stage + r * kStageRow, p.q + row, p.dq + row, half, p.pos0 + t, p.rope, p.eps);
+    }
   }
 }
 
@@ -575,7 +640,9 @@ void bwd_kv_kernel(BwdParams p) {
   }
 
   // sum over the 4 heads: each wave stores its partial sums, then reduces a quarter of them
+  // (dim block `wave` of both key blocks): dv straight to memory, dk_hat staged as rows
   f32x4* red = reinterpret_cast<f32x4*>(smem);
+  f32x4 dks[8];
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     __syncthreads();  // the buffers (or the previous round's sums) are free
@@ -596,95 +663,49 @@ void bwd_kv_kernel(BwdParams p) {
       f32x4 acc = red[blk * 64 + lane];
 #pragma unroll
       for (int w = 1; w < kKvWaves; ++w) acc += red[(w * 32 + blk) * 64 + lane];
-      const int db = blk >> 3, kb = (blk >> 2) & 1, rq = blk & 3;
-      const int key = k0 + 32 * kb + l32;
-      if (key < T) {
-        const int64_t r = (((int64_t)b * T + key) * p.Hkv + kvh) * kHeadDim + 32 * db + 8 * rq + 4 * hi;
-        if (which) {
-          *reinterpret_cast<f32x4*>(p.dkh + r) = acc * kLn2;  // scores were in log2 units
-        } else {
+      if (which) {
+        dks[u] = acc * kLn2;  // scores were in log2 units
+      } else {
+        const int db = blk >> 3, kb = (blk >> 2) & 1, rq = blk & 3;
+        const int key = k0 + 32 * kb + l32;
+        if (key < T) {
+          const int64_t r = (((int64_t)b * T + key) * p.Hkv + kvh) * kHeadDim + 32 * db + 8 * rq + 4 * hi;
           *reinterpret_cast<u32x2*>(p.dv + r) =
               u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
         }
       }
     }
   }
-}
-
-// ---------------------------------------------------------------------------------------------
-// 4. dx from dx_hat for x_hat = RoPE(RMSNorm(x)) (weight 1): rotate back by the negated angle,
-// then dx = (dxn - xn mean(dxn . xn)) / r with r = sqrt(mean(x^2) + eps). Two lanes per row.
-__global__ __launch_bounds__(256) void prologue_bwd_kernel(BwdParams p, int is_k) {
-  __shared__ float stage[64 * 128];
-  const int lane_pair = threadIdx.x >> 1;
-  const int half = threadIdx.x & 1;
-  const int H = is_k ? p.Hkv : p.Hq;
-  const int64_t row = (int64_t)blockIdx.x * 128 + lane_pair;
-  if (row >= (int64_t)p.B * p.T * H) return;  // both lanes of a pair exit together
-  const int t = (int)((row / H) % p.T);
-  const uint16_t* src = (is_k ? p.k : p.q) + row * kHeadDim + 64 * half;
-  const float* gsrc = (is_k ? p.dkh : p.dqh) + row * kHeadDim + 64 * half;
-  uint16_t* dst = (is_k ? p.dk : p.dq) + row * kHeadDim + 64 * half;
-  float x[64], g[64];
+  __syncthreads();  // every wave has read its sums
+  float* stage = reinterpret_cast<float*>(smem);  // [64 keys][kStageRow]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) unpack8(reinterpret_cast<const u32x4*>(src)[i], x + 8 * i);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(gsrc)[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) g[4 * i + j] = v[j];
+  for (int u = 0; u < 8; ++u) {
+    const int kb = (u >> 2) & 1, rq = u & 3;
+    *reinterpret_cast<f32x4*>(stage + (32 * kb + l32) * kStageRow + 32 * wave + 8 * rq + 4 * hi) = dks[u];
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
-  ss += shfl_xor_f(ss, 1);
-  const float inv = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
-  const int h = p.rope.half;
-  if (half == 0 && h > 0) {
-    float* st = stage + lane_pair;  // [dim][row], 128 rows
-#pragma unroll
-    for (int i = 0; i < 64; ++i)
-      if (i < 2 * h) st[i * 128] = g[i];
-#pragma unroll
-    for (int i = 0; i < kMaxRotHalf; ++i) {
-      if (i < h) {
-        float c, s;
-        rope_cs(p.pos0 + t, p.rope.rev[i], c, s);
-        const float a = st[i * 128];
-        const float bb = st[(i + h) * 128];
-        st[i * 128] = a * c + bb * s;
-        st[(i + h) * 128] = bb * c - a * s;
-      }
+  __syncthreads();
+  if (wave < 2) {  // dk: two lanes per key row, 32 rows per wave
+    const int r = 32 * wave + (lane >> 1), half = lane & 1;
+    const int key = k0 + r;
+    if (key < T) {
+      const int64_t row = (((int64_t)b * T + key) * p.Hkv + kvh) * kHeadDim;
+      dx_from_staged(stage + r * kStageRow, p.k + row, p.dk + row, half, p.pos0 + key, p.rope, p.eps);
     }
-#pragma unroll
-    for (int i = 0; i < 64; ++i)
-      if (i < 2 * h) g[i] = st[i * 128];
   }
-  float dot = 0.f;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) dot += g[i] * x[i];
-  dot += shfl_xor_f(dot, 1);
-  const float mean = dot * inv * (1.0f / kHeadDim);  // mean(dxn . xn)
-  float dx[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) dx[i] = (g[i] - x[i] * inv * mean) * inv;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) reinterpret_cast<u32x4*>(dst)[i] = pack8(dx + 8 * i);
 }
 
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_backward(const BwdParams& p, hipStream_t s) {
   const int64_t q_rows = (int64_t)p.B * p.T * p.Hq;
-  const int64_t k_rows = (int64_t)p.B * p.T * p.Hkv;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((q_rows + 15) / 16)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kQLds);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kQLdsTotal);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_q_kernel, dim3((unsigned)((int64_t)p.n_qtiles * p.B * p.Hkv)),
-                     dim3(kThreads), kQLds, s, p);
+                     dim3(kThreads), kQLdsTotal, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -694,15 +715,6 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t s) {
   const int64_t n_ktiles = (p.T + kNk - 1) / kNk;
   hipLaunchKernelGGL(bwd_kv_kernel, dim3((unsigned)(n_ktiles * p.B * p.Hkv)), dim3(kKvWaves * 64),
                      kKvLds, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  hipLaunchKernelGGL(prologue_bwd_kernel, dim3((unsigned)((q_rows + 127) / 128)), dim3(256), 0, s,
-                     p, 0);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prologue_bwd_kernel, dim3((unsigned)((k_rows + 127) / 128)), dim3(256), 0, s,
-                     p, 1);
   return hipGetLastError();
 }
 

@@ -111,9 +111,7 @@ struct BwdParams {
   uint16_t* qc;    // [B, T, Hq, 128] bf16(q_hat * scale * log2 e), as the forward's operand
   uint16_t* khat;  // [B, T, Hkv, 128] bf16(k_hat)
   uint16_t* dO;    // [B, T, Hq, 128] bf16(dout * sigmoid(gate))
-  uint16_t* aux;   // [B, T, Hq, 16] bf16: (-L2 hi, -L2 lo, 0 x 6, -D hi, -D lo, 0 x 6)
-  float* dqh;      // [B, T, Hq, 128] gradient of q_hat
-  float* dkh;      // [B, T, Hkv, 128] gradient of k_hat
+  uint16_t* aux;   // [B, T, Hq, 16] bf16: (-L log2 e, -D), each as three bf16 terms + zeros
   int32_t B, T, Hq, Hkv, window, gated;
   int32_t n_qtiles;
   int64_t pos0;

@@ -132,8 +132,8 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
  *   transpose and RMSNorm's derivative. dq, dk, dv, dgate are overwritten (bf16).
  * Numerics: q_hat, k_hat, dO, P and dS are rounded to bf16 at the matrix-core inputs; sums and the
  * norm/RoPE derivatives are fp32.
- *   workspace >= zg_attn_backward_workspace_bytes(cfg, B, T) (bf16 q_hat, k_hat, dO, a 32-byte row
- *   per query for lse and D, fp32 dq_hat and dk_hat: about B T (1056 Hq + 768 Hkv) bytes).
+ *   workspace >= zg_attn_backward_workspace_bytes(cfg, B, T) (bf16 q_hat, k_hat, dO and a 32-byte
+ *   row per query for lse and D: about B T (544 Hq + 256 Hkv) bytes).
  * Errors: NULL -> ZG_ERR_NULL; B < 1, T < 1 -> ZG_ERR_SHAPE; unsupported head ratio, head_dim,
  * rot_dim, or T * Hq * 256 bytes >= 4 GiB -> ZG_ERR_UNSUPPORTED; small workspace ->
  * ZG_ERR_WORKSPACE. */
