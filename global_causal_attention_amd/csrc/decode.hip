@@ -14,7 +14,7 @@
 //     A sequence with one chunk writes its output directly; otherwise the chunk writes (max, sum,
 //     unnormalised o) partials.
 //  3. decode_combine: log-sum-exp merge of the partials, gate, bf16 store.
-#include "zg_common.hpp"
+#include "zg_mfma.hpp"
 
 namespace zg {
 
@@ -572,6 +572,272 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_fp8_kernel(DecodePara
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Matrix-core variant for 4 query heads per KV head (bf16 or E4M3 caches). The same split-KV
+// chunks, exact chunk softmax and partial records as decode_attn_kernel; the dot products run on
+// v_mfma_f32_32x32x16_bf16 with the 4 heads padded to the 32 rows of the MFMA (the padding costs
+// matrix-core time only, which decode has to spare), so the vector work per cache element drops to
+// the E4M3 widening. Each wave takes every fourth block of 32 keys of the chunk.
+//  Scores: S[h][key] = sum_d q[h][d] K[key][d]; in K step st, lane half hi covers dims
+//  64 hi + 8 st .. + 7, so a lane reads one contiguous half row of its key (B operand) and the
+//  heads' q values in the same order (A operand, rows 4..31 zero). Heads land in registers 0..3
+//  of lanes 0..31, one key per lane.
+//  Output: O[h][d] = sum_key P[h][key] V[key][d]; V rows are staged per wave as bf16 in
+//  chunk-swizzled LDS rows and read transposed (ds_read_b64_tr_b16: lane gets keys
+//  16 st + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3} of one dim), and the softmax stores P in
+//  that key order, so one 16-byte LDS read per lane gives the A operand.
+namespace {
+constexpr int kMfRow = 256;                  // LDS bytes per staged bf16 V row
+constexpr int kMfTile = 32 * kMfRow;          // one 32-key V block
+constexpr int kMfWaveLds = kMfTile;           // one block per wave
+__device__ __forceinline__ int mf_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// key of position r (0..15) within a 16-key step of the permuted P order
+__device__ __forceinline__ int mf_key(int r) {
+  const int hi = r >> 3, j = r & 7;
+  return j < 4 ? 4 * hi + j : 8 + 4 * hi + (j - 4);
+}
+}  // namespace
+
+template <bool FP8>
+__global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int G = 4;
+  constexpr int kMaxChunk = kDecodeChunkKeys;
+  static_assert(kMaxChunk % 32 == 0, "blocks of 32 keys");
+  static_assert(G * kMaxChunk >= 4 * G * kHeadDim, "the score rows also hold the final reduction");
+  __shared__ float s_s[G * kMaxChunk];
+  __shared__ float ml[G][2];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[4 * kMfWaveLds];
+
+  // KV heads vary fastest across the grid: the workgroups of one chunk read the same cache rows
+  const int kvh = blockIdx.x;
+  const int chunk_id = blockIdx.y;
+  const int b = blockIdx.z;
+  const int pos = p.seqlens[b] - 1;
+  if (pos < 0 || (p.window == 0 && pos >= p.rows)) return;
+  const int64_t n_valid = min(n_valid_rows(pos, p.window), (int64_t)p.n_chunks * p.chunk);
+  const int64_t k0 = (int64_t)chunk_id * p.chunk;
+  if (k0 >= n_valid) return;
+  const int n = (int)min((int64_t)p.chunk, n_valid - k0);
+  const int n_chunks_b = (int)((n_valid + p.chunk - 1) / p.chunk);
+  const int n_blk = (n + 31) >> 5;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  constexpr int EB = FP8 ? 1 : 2;                                  // bytes per cache element
+  const int64_t row_bytes = (int64_t)p.Hkv * kHeadDim * EB;
+  const unsigned char* kc = reinterpret_cast<const unsigned char*>(p.k_cache) +
+                            ((int64_t)b * p.rows + k0) * row_bytes + (int64_t)kvh * kHeadDim * EB;
+  const unsigned char* vc = reinterpret_cast<const unsigned char*>(p.v_cache) +
+                            ((int64_t)b * p.rows + k0) * row_bytes + (int64_t)kvh * kHeadDim * EB;
+  const bf16x8 zero8 = bf16x8{};
+  unsigned char* wtile = vt + wave * kMfWaveLds;
+
+  // One 32-key block of cache rows: lane pieces of 16 bytes, 16 (bf16) or 8 (E4M3) lanes per row,
+  // loaded into registers, then widened and written as bf16 rows of 16 chunks, chunk c at
+  // c ^ swz(row). Rows at or past n read as zeros.
+  constexpr int NV = FP8 ? 4 : 8;  // 16-byte pieces per lane and block
+  // register sets of loaded rows: E4M3 blocks are half the bytes, so a wave keeps its next two
+  // in flight; bf16 keeps one (two would cost the occupancy)
+  constexpr bool TWO = FP8;
+  u32x4 rawA[NV], rawB[NV];
+  auto load_rows = [&](u32x4 (&vraw)[NV], const unsigned char* base, int blk) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = 64 * i + lane;
+      const int row = FP8 ? (idx >> 3) : (idx >> 4), pc = FP8 ? (idx & 7) : (idx & 15);
+      const int key = 32 * blk + row;
+      vraw[i] = key < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)key * row_bytes) + pc)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage_rows = [&](const u32x4 (&vraw)[NV], unsigned char* tile) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = 64 * i + lane;
+      if (FP8) {
+        const int row = idx >> 3, pc = idx & 7;
+        const u32x4 w = vraw[i];
+        const u32x4 lo = {e4m3x2_bf16<false>(w[0]), e4m3x2_bf16<true>(w[0]),
+                          e4m3x2_bf16<false>(w[1]), e4m3x2_bf16<true>(w[1])};
+        const u32x4 up = {e4m3x2_bf16<false>(w[2]), e4m3x2_bf16<true>(w[2]),
+                          e4m3x2_bf16<false>(w[3]), e4m3x2_bf16<true>(w[3])};
+        *reinterpret_cast<u32x4*>(tile + row * kMfRow + 16 * ((2 * pc) ^ mf_swz(row))) = lo;
+        *reinterpret_cast<u32x4*>(tile + row * kMfRow + 16 * ((2 * pc + 1) ^ mf_swz(row))) = up;
+      } else {
+        const int row = idx >> 4, ch = idx & 15;
+        *reinterpret_cast<u32x4*>(tile + row * kMfRow + 16 * (ch ^ mf_swz(row))) = vraw[i];
+      }
+    }
+  };
+
+  // ---- pass A
+  {
+    bf16x8 qa[8];  // head l32 (< 4), dims 64 hi + 8 st .. + 7
+    if (l32 < G) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(
+          p.qhat + ((int64_t)b * p.Hq + kvh * G + l32) * kHeadDim + 64 * hi);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const f32x4 a = src[2 * st], c = src[2 * st + 1];
+        const u32x4 w = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(c[0], c[1]),
+                         pack_bf16(c[2], c[3])};
+        qa[st] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) qa[st] = zero8;
+    }
+    // K rows of this wave's blocks: coalesced row loads (the next block's while the current one
+    // is scored), widened to bf16 and staged as swizzled rows; the B operand of K step st is the
+    // 16-byte chunk 8 hi + st of row l32
+    int kb_off[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) kb_off[st] = l32 * kMfRow + 16 * ((8 * hi + st) ^ mf_swz(l32));
+    auto score_block = [&](u32x4 (&vraw)[NV], int blk, int ahead) {
+      stage_rows(vraw, wtile);
+      if (blk + ahead < n_blk) load_rows(vraw, kc, blk + ahead);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are in LDS
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+        sacc = mfma32(qa[st], *reinterpret_cast<const bf16x8*>(wtile + kb_off[st]), sacc);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the tile is rewritten
+      const int key = 32 * blk + l32;
+      if (hi == 0 && key < n) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_s[h * kMaxChunk + key] = sacc[h];
+      }
+    };
+    if (wave < n_blk) load_rows(rawA, kc, wave);
+    if (TWO) {
+      if (wave + 4 < n_blk) load_rows(rawB, kc, wave + 4);
+      for (int blk = wave; blk < n_blk; blk += 8) {
+        score_block(rawA, blk, 8);
+        if (blk + 4 < n_blk) score_block(rawB, blk + 4, 8);
+      }
+    } else {
+      for (int blk = wave; blk < n_blk; blk += 4) score_block(rawA, blk, 4);
+    }
+  }
+  // this wave's first V blocks are loaded while the softmax runs
+  if (wave < n_blk) load_rows(rawA, vc, wave);
+  if (TWO && wave + 4 < n_blk) load_rows(rawB, vc, wave + 4);
+  __syncthreads();
+
+  // ---- exact softmax over the chunk, one wave per head; bf16 P in the permuted key order over
+  // the head's score row (dword q = positions 2q, 2q+1 of step q / 8; its keys are >= q, and a
+  // later pass of the loop never reads a float an earlier pass wrote)
+  const int n_pad = (n + 31) & ~31;
+  for (int h = wave; h < G; h += 4) {
+    float* sh = s_s + h * kMaxChunk;
+    float mx = -INFINITY;
+    for (int j = lane; j < n; j += 64) mx = fmaxf(mx, sh[j]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+    const float c = p.scale_log2;
+    const float nmc = -mx * c;
+    float sum = 0.f;
+    for (int q = lane; q < n_pad / 2; q += 64) {
+      const int ja = 16 * (q >> 3) + mf_key(2 * (q & 7));
+      const int jb = ja + 1;
+      const float ea = ja < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(sh[ja], c, nmc)) : 0.f;
+      const float eb = jb < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(sh[jb], c, nmc)) : 0.f;
+      const uint32_t w = pack_bf16(ea, eb);
+      sh[q] = __uint_as_float(w);
+      sum += bf16lo(w) + bf16hi(w);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += shfl_xor_f(sum, o);
+    if (lane == 0) {
+      ml[h][0] = mx * c;
+      ml[h][1] = sum;
+    }
+  }
+  __syncthreads();
+
+  // ---- pass B: per 32-key block, stage V as bf16 rows, then two 16-key steps x 4 dim blocks
+  int tr_off[2][4];
+  {
+    const int tr_row = 4 * hi + ((lane & 15) >> 2);
+    const int tr_dch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int row = 8 * x + tr_row;
+        tr_off[x][db] = row * kMfRow + 16 * ((4 * db + tr_dch) ^ mf_swz(row)) + 8 * (lane & 1);
+      }
+  }
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  auto pv_block = [&](u32x4 (&vraw)[NV], int blk, int ahead) {
+    unsigned char* tile = wtile;
+    stage_rows(vraw, tile);
+    if (blk + ahead < n_blk) load_rows(vraw, vc, blk + ahead);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are in LDS
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2) {
+      const int pstep = 2 * blk + st2;           // 16-key step of the chunk
+      bf16x8 pa = zero8;
+      if (l32 < G) pa = *reinterpret_cast<const bf16x8*>(s_s + l32 * kMaxChunk + 8 * pstep + 4 * hi);
+      const unsigned char* base = tile + st2 * 16 * kMfRow;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const i16x4 a = lds_read_tr(base + tr_off[0][db]);
+        const i16x4 c = lds_read_tr(base + tr_off[1][db]);
+        const i16x4 both[2] = {a, c};
+        o[db] = mfma32(pa, __builtin_bit_cast(bf16x8, both), o[db]);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the tile is rewritten
+  };
+  if (TWO) {
+    for (int blk = wave; blk < n_blk; blk += 8) {
+      pv_block(rawA, blk, 8);
+      if (blk + 4 < n_blk) pv_block(rawB, blk + 4, 8);
+    }
+  } else {
+    for (int blk = wave; blk < n_blk; blk += 4) pv_block(rawA, blk, 4);
+  }
+  __syncthreads();  // every wave is done reading P
+  float* red = s_s;  // [4 waves][G][128]
+  if (hi == 0) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int h = 0; h < G; ++h) red[(wave * G + h) * kHeadDim + 32 * db + l32] = o[db][h];
+  }
+  __syncthreads();
+
+  const float vs = FP8 ? p.v_scale : 1.0f;
+  for (int i = tid; i < G * kHeadDim; i += kDecThreads) {
+    const int h = i / kHeadDim;
+    const int d = i - h * kHeadDim;
+    const float ov = vs * (red[(0 * G + h) * kHeadDim + d] + red[(1 * G + h) * kHeadDim + d] +
+                           red[(2 * G + h) * kHeadDim + d] + red[(3 * G + h) * kHeadDim + d]);
+    const int head = kvh * G + h;
+    if (n_chunks_b == 1) {
+      float y = ov / ml[h][1];
+      if (p.gated) {
+        const float g = bf16lo(p.gate[((int64_t)b * p.Hq + head) * kHeadDim + d]);
+        y *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+      }
+      p.out[((int64_t)b * p.Hq + head) * kHeadDim + d] = (uint16_t)(pack_bf16(y, 0.f) & 0xffffu);
+    } else {
+      float* rec = p.partial + (((int64_t)b * p.Hq + head) * p.n_chunks + chunk_id) * kPartStride;
+      if (d == 0) {
+        rec[0] = ml[h][0];
+        rec[1] = ml[h][1];
+      }
+      rec[4 + d] = ov;
+    }
+  }
+}
+
 // bf16 -> E4M3 of value * inv_scale, 16 elements per lane.
 __global__ __launch_bounds__(256) void to_fp8_kernel(ToFp8Params p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -645,14 +911,15 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int G = p.Hq / p.Hkv;
   const dim3 grid(p.n_chunks, p.Hkv, p.B);
+  const dim3 grid_h(p.Hkv, p.n_chunks, p.B);
   switch (G * 2 + (p.fp8 ? 1 : 0)) {
     case 2: hipLaunchKernelGGL(decode_attn_kernel<1>, grid, dim3(kDecThreads), 0, s, p); break;
     case 4: hipLaunchKernelGGL(decode_attn_kernel<2>, grid, dim3(kDecThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(decode_attn_kernel<4>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL(decode_mfma_kernel<false>, grid_h, dim3(kDecThreads), 0, s, p); break;
     case 16: hipLaunchKernelGGL(decode_attn_kernel<8>, grid, dim3(kDecThreads), 0, s, p); break;
     case 3: hipLaunchKernelGGL(decode_attn_fp8_kernel<1>, grid, dim3(kDecThreads), 0, s, p); break;
     case 5: hipLaunchKernelGGL(decode_attn_fp8_kernel<2>, grid, dim3(kDecThreads), 0, s, p); break;
-    case 9: hipLaunchKernelGGL(decode_attn_fp8_kernel<4>, grid, dim3(kDecThreads), 0, s, p); break;
+    case 9: hipLaunchKernelGGL(decode_mfma_kernel<true>, grid_h, dim3(kDecThreads), 0, s, p); break;
     case 17: hipLaunchKernelGGL(decode_attn_fp8_kernel<8>, grid, dim3(kDecThreads), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
