@@ -289,13 +289,13 @@ def bench_decode(torch, zg, si, dev, stream, reps):
     res["workload"] = "B=64, Hq=32 Hkv=8 D=128, ring W=128 gated; linear L~U[8192,65536] ungated; base 1e7; cold MALL"
     from global_causal_attention_amd.counters import lookup_traffic
     parts = [lookup_traffic("decode_prep_kernel", 16384),
-             lookup_traffic("decode_attn_kernel<4>", Bd * HKV * 16 * 1024),
+             lookup_traffic("decode_mfma_kernel<false>", Bd * HKV * 16 * 1024),
              lookup_traffic("decode_combine_kernel", 262144)]
     res["roofline"] = {"bound": "hbm", "achieved": res["linear"]["GBps"], "peak": HBM_PEAK / 1e9,
                        "unit": "GB/s", "frac": res["linear"]["hbm_frac"],
                        "traffic": None if None in parts else sum(parts),
                        "kernel": "global decode launch (decode_prep_kernel + "
-                                 "decode_attn_kernel<4> + decode_combine_kernel)"}
+                                 "decode_mfma_kernel<false> + decode_combine_kernel)"}
     del x, flush
     return res
 

@@ -41,6 +41,11 @@ KERNEL_SOURCES = {
     "prefill_swa_kernel": ["prefill_swa.hip"] + _COMMON,
     "decode_prep_kernel": ["decode.hip"] + _COMMON,
     "decode_attn_kernel": ["decode.hip"] + _COMMON,
+    "decode_attn_fp8_kernel": ["decode.hip"] + _COMMON,
+    "decode_mfma_kernel": ["decode.hip"] + _COMMON,
+    "bwd_pre_kernel": ["backward.hip"] + _COMMON,
+    "bwd_q_kernel": ["backward.hip"] + _COMMON,
+    "bwd_kv_kernel": ["backward.hip"] + _COMMON,
     "decode_combine_kernel": ["decode.hip"] + _COMMON,
 }
 
