@@ -256,6 +256,28 @@ def bench_decode(torch, zg, si, dev, stream, reps):
         res[name] = {"ms_median": round(med, 4), "kv_bytes": kv_bytes, "GBps": round(bw / 1e9, 1),
                      "hbm_frac": round(bw / HBM_PEAK, 4), "tokens_per_s": round(Bd / (med * 1e-3), 1)}
         log(f"[bench] decode {name}: {med:.4f} ms, {bw / 1e9:.1f} GB/s")
+    # streaming-read reference: the probe reads the 8 GiB linear K cache (cold MALL) with the same
+    # non-temporal 16-byte loads the decode kernels use
+    sink = torch.empty(4 * 2048, dtype=torch.int32, device=dev)
+    pbytes = x["lin_k"].numel() * x["lin_k"].element_size()
+    zg.zg_hbm_read_probe(x["lin_k"], sink)
+    ptimes = []
+    for _ in range(5):
+        flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        zg.zg_hbm_read_probe(x["lin_k"], sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ptimes.append(e0.elapsed_time(e1))
+    ptimes.sort()
+    pbw = pbytes / (ptimes[2] * 1e-3)
+    res["read_probe"] = {"bytes": pbytes, "ms_median": round(ptimes[2], 4),
+                         "GBps": round(pbw / 1e9, 1), "frac_of_spec": round(pbw / HBM_PEAK, 4)}
+    for name in ("ring", "linear"):
+        res[name]["frac_of_read_probe"] = round(res[name]["GBps"] * 1e9 / pbw, 4)
+    log(f"[bench] streaming read probe: {pbw / 1e9:.1f} GB/s")
     # the same step over E4M3 caches (converted once from the bf16 ones, outside the timing)
     lin_k8 = zg.zg_kv_to_fp8(x["lin_k"])
     lin_v8 = zg.zg_kv_to_fp8(x["lin_v"])
@@ -283,7 +305,8 @@ def bench_decode(torch, zg, si, dev, stream, reps):
                           "GBps": round(kv8 / (med * 1e-3) / 1e9, 1),
                           "hbm_frac": round(kv8 / (med * 1e-3) / HBM_PEAK, 4),
                           "tokens_per_s": round(Bd / (med * 1e-3), 1),
-                          "speedup_vs_bf16": round(res["linear"]["ms_median"] / med, 3)}
+                          "speedup_vs_bf16": round(res["linear"]["ms_median"] / med, 3),
+                          "frac_of_read_probe": round(kv8 / (med * 1e-3) / pbw, 4)}
     log(f"[bench] decode linear E4M3: {med:.4f} ms, {kv8 / (med * 1e-3) / 1e9:.1f} GB/s")
     del lin_k8, lin_v8
     res["workload"] = "B=64, Hq=32 Hkv=8 D=128, ring W=128 gated; linear L~U[8192,65536] ungated; base 1e7; cold MALL"

@@ -16,7 +16,8 @@ from ._abi import (LIB_PATH, ZgAttnCfg, ZgTokenStrides, load_library, ZG_OK, ZG_
                    ZG_ERR_SHAPE, ZG_ERR_UNSUPPORTED, ZG_ERR_WORKSPACE, ZG_ERR_HIP, EXPORTS)
 
 __all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached",
-           "zg_attn_forward_train", "zg_attn_backward", "zg_attn_backward_workspace_bytes", "zg_attn_decode", "zg_attn_decode_fp8", "zg_kv_to_fp8", "zg_kv_bytes",
+           "zg_attn_forward_train", "zg_attn_backward", "zg_attn_backward_workspace_bytes",
+           "zg_hbm_read_probe", "zg_attn_decode", "zg_attn_decode_fp8", "zg_kv_to_fp8", "zg_kv_bytes",
            "zg_attn_prefill_workspace_bytes", "zg_attn_decode_workspace_bytes", "zg_rmsnorm",
            "zg_gemm_bf16", "zg_attn_layer", "zg_attn_layer_workspace_bytes", "zg_last_error",
            "load_library", "LIB_PATH", "EXPORTS"]
@@ -346,6 +347,18 @@ def zg_kv_bytes(n_layers, global_every, n_kv_heads, head_dim, window, elem_bytes
                       seqlen) < 0:
         raise ZGError(ZG_ERR_SHAPE, zg_last_error())
     return r
+
+
+def zg_hbm_read_probe(src, sink=None, n_blocks=2048, stream=None):
+    """Streaming-read probe over the bytes of the device tensor `src` (see include/zg_attn.h);
+    returns the sink tensor (one meaningless word per wave)."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(4 * n_blocks, dtype=torch.int32, device=src.device)
+    _check(load_library().zg_hbm_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink), n_blocks,
+                                            _stream(stream)))
+    return sink
 
 
 def zg_rmsnorm(x, eps=1e-6, w=None, out=None, stream=None):

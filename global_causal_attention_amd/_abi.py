@@ -48,6 +48,7 @@ EXPORTS = {
                                         _P, _P, _SZ, _P]),
     "zg_kv_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32, _I32, _I64, _I64]),
     "zg_last_error": (ctypes.c_char_p, []),
+    "zg_hbm_read_probe": (ctypes.c_int, [_P, _I64, _P, _I32, _P]),
     "zg_rmsnorm": (ctypes.c_int, [_I64, _I32, _P, _P, _F32, _P, _P]),
     "zg_gemm_bf16": (ctypes.c_int, [_I64, _I32, _I32, _P, _P, _P, _P, _I64, _P]),
     "zg_attn_layer_workspace_bytes": (_SZ, [_CFG, _I32, _I32]),

@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libzgattn.so")
-SOURCES = ["prefill.hip", "prefill_swa.hip", "decode.hip", "stack.hip", "backward.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "prefill_swa.hip", "decode.hip", "stack.hip", "backward.hip", "probe.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
          "-Wno-unused-function",

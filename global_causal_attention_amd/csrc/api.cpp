@@ -650,6 +650,16 @@ zg_status zg_kv_to_fp8(const void* src_bf16, void* dst_e4m3, int64_t n, float sc
   return hip_status(zg::launch_to_fp8(p, reinterpret_cast<hipStream_t>(stream)), "to-fp8 launch");
 }
 
+zg_status zg_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t n_blocks,
+                            void* stream) {
+  if (!src || !sink) return fail(ZG_ERR_NULL, "src and sink must be non-NULL");
+  if (bytes < 16 || bytes % 16 != 0) return fail(ZG_ERR_SHAPE, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
+  if (n_blocks < 1 || n_blocks > (1 << 20)) return fail(ZG_ERR_SHAPE, "n_blocks=%d out of range", n_blocks);
+  if (!aligned16(src)) return fail(ZG_ERR_SHAPE, "src must be 16-byte aligned");
+  return hip_status(zg::launch_read_probe(src, bytes, sink, n_blocks, reinterpret_cast<hipStream_t>(stream)),
+                    "read probe launch");
+}
+
 zg_status zg_rmsnorm(int64_t rows, int32_t dim, const float* x, const float* w, float eps,
                      void* y_bf16, void* stream) {
   if (!x || !y_bf16) return fail(ZG_ERR_NULL, "x and y must be non-NULL");

@@ -156,6 +156,8 @@ struct RowCopyParams {
 hipError_t launch_row_copy(const RowCopyParams& p, hipStream_t s);
 
 hipError_t launch_kprep(const KPrepParams& p, hipStream_t s);
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t n_blocks,
+                             hipStream_t s);
 // True when launch_prefill takes the streaming kernel for short windows (which reads seg_steps and
 // expects keys prepared with KPrepParams::fold set).
 bool prefill_uses_swa(int window, int group, int rot_half);

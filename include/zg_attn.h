@@ -215,6 +215,15 @@ uint64_t zg_kv_bytes(int32_t n_layers, int32_t global_every, int32_t n_kv_heads,
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* zg_last_error(void);
 
+/* Measurement helper (not part of the attention path): reads `bytes` (a positive multiple of 16)
+ * from the device buffer `src` with streaming non-temporal 16-byte loads over `n_blocks`
+ * workgroups of 256 lanes and writes one word per wave to `sink` (device, >= 4 * n_blocks words;
+ * its values are meaningless). Timing it gives the device's streaming-read bandwidth, the
+ * reference beside the 8 TB/s specification for the memory-bound kernels. Errors: NULL ->
+ * ZG_ERR_NULL; bad sizes or alignment -> ZG_ERR_SHAPE. */
+zg_status zg_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t n_blocks,
+                            void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Building blocks of one Pre-LN attention layer with projections (zh-TW translation, section 2.1
  * and Fig. 3: a normalised hidden state h feeds parallel q/k/v/gate projections; o_proj follows;

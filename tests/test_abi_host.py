@@ -122,3 +122,36 @@ def test_prefill_cached_rejects_bad_arguments():
     st = lib.zg_attn_prefill_cached(ctypes.byref(cr), 1, 8, 0, 16, 16, 16, None, None, None, None,
                                     16, 16, 0, 16, None, 0, None)
     assert st == zg.ZG_ERR_WORKSPACE
+
+
+def test_training_entry_points_reject_bad_arguments():
+    lib = zg.load_library()
+    c = zg.AttnConfig(window=128, gated=True).c()
+    # the training kernels take 4 query heads per KV head only
+    c8 = zg.AttnConfig(n_q_heads=8, n_kv_heads=1, window=0, gated=False).c()
+    st = lib.zg_attn_forward_train(ctypes.byref(c8), 1, 8, 16, 16, 16, None, 16, 16, 16, 1 << 20, None)
+    assert st == zg.ZG_ERR_UNSUPPORTED
+    # gated without a gate
+    st = lib.zg_attn_forward_train(ctypes.byref(c), 1, 8, 16, 16, 16, None, 16, 16, 16, 1 << 20, None)
+    assert st == zg.ZG_ERR_NULL
+    # missing lse
+    st = lib.zg_attn_backward(ctypes.byref(c), 1, 8, 16, 16, 16, 16, 16, 16, None, 16, 16, 16, 16,
+                              16, 1 << 30, None)
+    assert st == zg.ZG_ERR_NULL
+    # workspace too small
+    need = lib.zg_attn_backward_workspace_bytes(ctypes.byref(c), 1, 8)
+    assert need > 0
+    st = lib.zg_attn_backward(ctypes.byref(c), 1, 8, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                              16, need - 1, None)
+    assert st == zg.ZG_ERR_WORKSPACE
+    st = lib.zg_attn_backward(ctypes.byref(c), 0, 8, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                              16, need, None)
+    assert st == zg.ZG_ERR_SHAPE
+
+
+def test_read_probe_rejects_bad_arguments():
+    lib = zg.load_library()
+    assert lib.zg_hbm_read_probe(None, 1024, 16, 4, None) == zg.ZG_ERR_NULL
+    assert lib.zg_hbm_read_probe(16, 1000, 16, 4, None) == zg.ZG_ERR_SHAPE
+    assert lib.zg_hbm_read_probe(16, 1024, 16, 0, None) == zg.ZG_ERR_SHAPE
+    assert lib.zg_hbm_read_probe(8, 1024, 16, 4, None) == zg.ZG_ERR_SHAPE
