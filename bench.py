@@ -69,6 +69,7 @@ def main():
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked prefill")
     ap.add_argument("--no-sweep", action="store_true", help="skip the context sweep")
     ap.add_argument("--no-backward", action="store_true", help="skip the training (backward) layers")
+    ap.add_argument("--no-shard", action="store_true", help="skip the one-GPU-share layers")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the timed 5:1 block (profiling the other workloads alone; value null)")
     args = ap.parse_args()
@@ -110,6 +111,11 @@ def main():
         result["context_sweep"] = bench_sweep(torch, zg, si, dev, stream)
     if not args.no_backward:
         result["training"] = bench_backward(torch, zg, si, dev, stream)
+    if not args.no_shard:
+        full = None
+        if "swa_ms" in result.get("layers", {}):
+            full = {"swa": result["layers"]["swa_ms"], "global": result["layers"]["global_ms"]}
+        result["shard_share"] = bench_shard(torch, zg, si, dev, stream, full)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, si)
@@ -500,6 +506,39 @@ def bench_backward(torch, zg, si, dev, stream, Bb=B, Tb=T):
         del x, dy, out, lse, fws, bws
     res["block_5to1_ms"] = round(total, 3)
     res["block_5to1_tokens_per_s"] = round(Bb * Tb / (total * 1e-3), 1)
+    return res
+
+
+def bench_shard(torch, zg, si, dev, stream, full_ms=None, Bs=B, Ts=T):
+    """One GPU's share of a layer when the attention core is split over the 8 KV-head groups
+    (4 query heads, 1 KV head, no exchange): B=4, T=16384, one gated local and one global layer
+    (base 1e6). `vs_eighth_of_full` compares with 1/8 of the full layer's time from the block
+    when that section ran."""
+    log(f"[bench] one-GPU share: B={Bs} T={Ts} Hq=4 Hkv=1")
+    x = si.prefill_layer(si.generator(1008, device="cuda"), Bs, Ts, 4, 1, D, gated=True,
+                         device="cuda")
+    out = torch.empty_like(x["q"])
+    res = {"workload": f"B={Bs}, T={Ts}, Hq=4 Hkv=1 D=128 (one KV-head group of 8), base 1e6"}
+    for name, win in (("swa", W), ("global", 0)):
+        cfg = zg.AttnConfig(n_q_heads=4, n_kv_heads=1, window=win, gated=win > 0,
+                            rope_base=ROPE_BASE)
+        ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, Bs, Ts), dtype=torch.uint8, device=dev)
+        fn = lambda: zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"] if win else None,
+                                        out=out, workspace=ws)
+        ms = _time(torch, stream, fn, 10)
+        r = {"ms_median": round(ms, 4), "tokens_per_s": round(Bs * Ts / (ms * 1e-3), 1)}
+        flop = Bs * 4 * n_pairs(Ts, win) * 4 * D
+        if win:
+            nbytes = Bs * Ts * (4 * D * 2 * 3 + D * 2 * 2)
+            r["hbm_frac"] = round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)
+        else:
+            r["mfma_frac"] = round(flop / (ms * 1e-3) / MFMA_BF16_PEAK, 4)
+        if full_ms and name in full_ms:
+            r["vs_eighth_of_full"] = round(full_ms[name] / 8 / ms, 4)
+        res[name] = r
+        log(f"[bench] share {name}: {ms:.4f} ms")
+        del ws
+    del x, out
     return res
 
 
