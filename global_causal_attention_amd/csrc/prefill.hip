@@ -45,36 +45,182 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
-// K prologue: khat[b,t,h,:] = bf16(RoPE(RMSNorm(k[b,t,h,:]))), packed [B, T, Hkv, 128].
-// Two lanes per row; 128 rows per 256-thread block.
+// K prologue: khat[b,t,h,:] = bf16(fold(RoPE(RMSNorm(k[b,t,h,:])))), packed [B, T, Hkv, 128]
+// (also run on q, with Hq rows per token, where a caller wants q_hat materialised).
+// Sixteen lanes per 256-byte head row, lane c holding dims 8c..8c+7, so each load or store
+// instruction moves four whole rows as one contiguous kilobyte. A wave takes 8 rows per pass (two
+// per 16-lane group) and strides over the rows; the next pass's rows are loaded before this pass
+// is processed. RMSNorm reduces over the group with four lane exchanges. RoPE pairs (i, i + h) are
+// exchanged through the wave's own LDS rows: lane c rotates pairs c and c + 16 of its group's row,
+// so each lane needs only two frequencies, picked once.
+constexpr int kKpRowsPerWave = 8;
+constexpr int kKpStage = 68;  // floats per staged row (64 used; padded)
+
 __global__ __launch_bounds__(256) void kprep_kernel(KPrepParams p) {
-  __shared__ float stage[128 * 64];
-  const int lane_pair = threadIdx.x >> 1;
-  const int half = threadIdx.x & 1;
-  const int64_t row = (int64_t)blockIdx.x * 128 + lane_pair;
-  const int64_t n_rows = (int64_t)p.B * p.T * p.Hkv;
-  if (row >= n_rows) return;  // rows come in lane pairs, so both lanes of a pair exit together
-  const int64_t bt = row / p.Hkv;
-  const int h = (int)(row - bt * p.Hkv);
-  const int t = (int)(bt % p.T);
-  const uint16_t* src = p.k + bt * p.sk + (int64_t)h * kHeadDim + 64 * half;
-  float x[64];
-  const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+  __shared__ __attribute__((aligned(16))) float stage[4][kKpRowsPerWave][kKpStage];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4;
+  const int c = lane & 15;
+  const int Hkv = p.Hkv, T = p.T;
+  const int64_t n_rows = (int64_t)p.B * T * Hkv;
+  const int h = p.rope.half;
+  const int rot = 2 * h;
+  const bool rotates = 8 * c < rot;  // this lane holds rotated dims
+
+  // per-lane constants: norm weights, fold factors, the lane's two rotary frequencies
+  float wv[8], fv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) unpack8(s4[i], x + 8 * i);
-  norm_rope_row(x, half, p.k_norm_w, p.eps, p.pos0 + t, p.rope, stage, lane_pair, 128);
-  if (p.fold) {
-    const int rot = 2 * p.rope.half;
+  for (int j = 0; j < 8; ++j) {
+    const int d = 8 * c + j;
+    wv[j] = p.k_norm_w ? p.k_norm_w[d] : 1.0f;
+    fv[j] = (d >= rot && p.fold_w) ? p.fold_scale * p.fold_w[d] : p.fold_scale;
+  }
+  double rev0 = 0.0, rev1 = 0.0;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const int d = 64 * half + i;
-      x[i] *= (d >= rot && p.fold_w) ? p.fold_scale * p.fold_w[d] : p.fold_scale;
+  for (int j = 0; j < 16; ++j) {
+    if (c == j) {
+      rev0 = p.rope.rev[j];
+      rev1 = p.rope.rev[j + 16];
     }
   }
-  const int64_t orow = ((bt / p.T) * p.out_rows + p.out_row0 + t) * p.Hkv + h;
-  u32x4* d4 = reinterpret_cast<u32x4*>(p.khat + orow * kHeadDim + 64 * half);
+
+  // wave-uniform coordinates (b, t, h) of the pass's first row, advanced by a fixed stride
+  const int64_t stride = (int64_t)gridDim.x * 4 * kKpRowsPerWave;
+  int64_t base = ((int64_t)blockIdx.x * 4 + wave) * kKpRowsPerWave;
+  if (base >= n_rows) return;
+  int64_t bt0 = base / Hkv;
+  int h0 = (int)(base - bt0 * Hkv);
+  int64_t b0 = bt0 / T;
+  int t0 = (int)(bt0 - b0 * T);
+  const int64_t s_bt = stride / Hkv;
+  const int s_h = (int)(stride - s_bt * Hkv);
+  const int64_t s_b = s_bt / T;
+  const int s_t = (int)(s_bt - s_b * T);
+
+  // row r of the pass (r = grp + 4 i) -> source offset, output row, position
+  struct RowAt {
+    int64_t src, orow, pos;
+    bool valid;
+  };
+  auto row_at = [&](int64_t bse, int64_t b_, int t_, int h_, int r) -> RowAt {
+    int hh = h_ + r;
+    int tt = t_;
+    int64_t bb = b_;
+    while (hh >= Hkv) { hh -= Hkv; ++tt; }
+    while (tt >= T) { tt -= T; ++bb; }
+    RowAt o;
+    o.valid = bse + r < n_rows;
+    o.src = (bb * T + tt) * p.sk + (int64_t)hh * kHeadDim + 8 * c;
+    o.orow = (bb * p.out_rows + p.out_row0 + tt) * Hkv + hh;
+    o.pos = p.pos0 + tt;
+    return o;
+  };
+  auto load = [&](const RowAt& ra) -> u32x4 {
+    return ra.valid ? *reinterpret_cast<const u32x4*>(p.k + ra.src) : u32x4{0u, 0u, 0u, 0u};
+  };
+
+  RowAt cur[2];
+  u32x4 raw[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) d4[i] = pack8(x + 8 * i);
+  for (int i = 0; i < 2; ++i) {
+    cur[i] = row_at(base, b0, t0, h0, grp + 4 * i);
+    raw[i] = load(cur[i]);
+  }
+  float* st = &stage[wave][0][0];
+  while (true) {
+    // next pass: coordinates and loads go out before this pass is processed
+    const int64_t nbase = base + stride;
+    const bool more = nbase < n_rows;
+    h0 += s_h;
+    t0 += s_t;
+    b0 += s_b;
+    if (h0 >= Hkv) { h0 -= Hkv; ++t0; }
+    if (t0 >= T) { t0 -= T; ++b0; }
+    RowAt nxt[2];
+    u32x4 nraw[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      nxt[i] = row_at(nbase, b0, t0, h0, grp + 4 * i);
+      nraw[i] = more ? load(nxt[i]) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    float x[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      unpack8(raw[i], x[i]);
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += x[i][j] * x[i][j];
+      ss += shfl_xor_f(ss, 1);
+      ss += shfl_xor_f(ss, 2);
+      ss += shfl_xor_f(ss, 4);
+      ss += shfl_xor_f(ss, 8);
+      const float inv = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[i][j] *= inv * wv[j];
+    }
+    if (h > 0) {
+      // stage the rotated dims of both rows, rotate pairs c and c + 16, read back
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float* sr = st + (grp + 4 * i) * kKpStage + 8 * c;
+        if (rotates) {
+          *reinterpret_cast<f32x4*>(sr) = f32x4{x[i][0], x[i][1], x[i][2], x[i][3]};
+          *reinterpret_cast<f32x4*>(sr + 4) = f32x4{x[i][4], x[i][5], x[i][6], x[i][7]};
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS ops complete in order
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float* sr = st + (grp + 4 * i) * kKpStage;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int pi = c + 16 * k;
+          if (pi < h) {
+            float cs, sn;
+            rope_cs(cur[i].pos, k ? rev1 : rev0, cs, sn);
+            const float a = sr[pi];
+            const float b = sr[pi + h];
+            sr[pi] = a * cs - b * sn;
+            sr[pi + h] = b * cs + a * sn;
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float* sr = st + (grp + 4 * i) * kKpStage + 8 * c;
+        if (rotates) {
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(sr);
+          const f32x4 hi4 = *reinterpret_cast<const f32x4*>(sr + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[i][j] = lo[j];
+            x[i][4 + j] = hi4[j];
+          }
+        }
+      }
+      // the next pass rewrites these rows: its writes must not overtake this pass's reads
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (p.fold) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[i][j] *= fv[j];
+      }
+      if (cur[i].valid)
+        *reinterpret_cast<u32x4*>(p.khat + cur[i].orow * kHeadDim + 8 * c) = pack8(x[i]);
+    }
+    if (!more) break;
+    base = nbase;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      cur[i] = nxt[i];
+      raw[i] = nraw[i];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -478,7 +624,9 @@ hipError_t launch_row_copy(const RowCopyParams& p, hipStream_t s) {
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_kprep(const KPrepParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.T * p.Hkv;
-  const int64_t blocks = (rows + 127) / 128;
+  if (rows == 0) return hipSuccess;
+  // 32 rows per block per pass; at most 8 blocks per CU (256 CUs), the waves stride over the rest
+  const int64_t blocks = std::min<int64_t>((rows + 31) / 32, 256 * 8);
   hipLaunchKernelGGL(kprep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
