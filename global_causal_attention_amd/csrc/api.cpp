@@ -82,6 +82,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
+// Runs of 64-query steps per workgroup of the banded streaming kernel, so that the grid roughly
+// fills the device.
+static int32_t swa_seg_steps(int64_t B, int64_t T, int64_t Hkv) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t steps = (T + 63) / 64;
+  const int64_t per_bh = B * Hkv;
+  const int64_t n_seg = std::max<int64_t>(1, std::min<int64_t>(steps, cus / per_bh));
+  return (int32_t)((steps + n_seg - 1) / n_seg);
+}
+
 extern "C" {
 
 const char* zg_last_error(void) { return g_err.c_str(); }
@@ -198,16 +210,7 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     pp.rope = rt;
     if ((int64_t)pp.n_qtiles * B * Hkv >= (int64_t(1) << 31))
       return fail(ZG_ERR_SHAPE, "grid too large");
-    if (swa) {
-      // split each sequence into runs of 64-query steps so that the grid roughly fills the device
-      int dev = 0, cus = 256;
-      if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      const int64_t steps = (T + 63) / 64;
-      const int64_t per_bh = (int64_t)B * Hkv;
-      const int64_t n_seg = std::max<int64_t>(1, std::min<int64_t>(steps, cus / per_bh));
-      pp.seg_steps = (int32_t)((steps + n_seg - 1) / n_seg);
-    }
+    if (swa) pp.seg_steps = swa_seg_steps(B, T, Hkv);
     return hip_status(zg::launch_prefill(pp, G, cfg->gated != 0, hs), "prefill launch");
   } catch (...) {
     return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_prefill");
@@ -386,7 +389,9 @@ size_t zg_attn_prefill_cached_workspace_bytes(const zg_attn_cfg* cfg, int32_t B,
   if (!cfg || B < 1 || T < 1 || cfg->n_kv_heads < 1) return 0;
   if (cfg->window <= 0) return 0;  // linear caches: keys are read from the cache itself
   const size_t rows = (size_t)cfg->window - 1 + T;  // ring context + the new tokens
-  return 2 * align256((size_t)B * rows * cfg->n_kv_heads * kD * 2);
+  const size_t row_bytes = (size_t)cfg->n_kv_heads * kD * 2;
+  // staged K and V, then the new rows' unfolded k_hat for the ring (streaming-kernel path)
+  return 2 * align256((size_t)B * rows * row_bytes) + align256((size_t)B * T * row_bytes);
 }
 
 zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t pos0,
@@ -440,10 +445,20 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
     // ring's context followed by the new tokens
     uint16_t* ks = kc;
     uint16_t* vs = vc;
+    uint16_t* k_raw = nullptr;  // unfolded k_hat of the new rows, for the ring write
     int64_t kv_rows = cache_stride, row0 = pos0;
+    const zg::RopeTableH rt = rope_table(cfg);
+    const int G = (int)(Hq / Hkv);
+    const int window = (ring && W < n_keys) ? (int)W : 0;  // a window covering every key is causal
+    // Rings whose context offset suits it run on the banded streaming kernel, which takes keys
+    // with the softmax scale and the q-norm weights folded in: the context rows are folded as they
+    // are gathered, and the new rows' unfolded k_hat goes to the ring from a separate copy.
+    const bool swa = ring && zg::prefill_uses_swa(window, G, rt.half) &&
+                     zg::prefill_swa_offset_ok(n_ctx, window);
     if (ring) {
       ks = static_cast<uint16_t*>(workspace);
       vs = ks + align256((size_t)B * (W - 1 + T) * row * 2) / 2;
+      if (swa) k_raw = vs + align256((size_t)B * (W - 1 + T) * row * 2) / 2;
       kv_rows = n_keys;
       row0 = n_ctx;
       if (n_ctx > 0) {
@@ -456,12 +471,17 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
           g.src_stride = row; g.dst_stride = row;
           g.src_ring = W; g.dst_ring = 0;
           g.row_elems = (int32_t)row; g.rows = (int32_t)n_ctx; g.B = B;
+          if (swa && which == 0) {
+            g.fold = 1;
+            g.rot_dim = 2 * rt.half;
+            g.fold_scale = scale_log2(cfg);
+            g.fold_w = q_norm_w;
+          }
           st = hip_status(zg::launch_row_copy(g, hs), "ring gather launch");
           if (st != ZG_OK) return st;
         }
       }
     }
-    const zg::RopeTableH rt = rope_table(cfg);
     zg::KPrepParams kp{};
     kp.k = static_cast<const uint16_t*>(k);
     kp.khat = ks;
@@ -475,6 +495,12 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
     kp.out_row0 = row0;
     kp.eps = cfg->rms_eps;
     kp.rope = rt;
+    if (swa) {
+      kp.fold = 1;
+      kp.fold_scale = scale_log2(cfg);
+      kp.fold_w = q_norm_w;
+      kp.khat_raw = k_raw;
+    }
     st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
     if (st != ZG_OK) return st;
     zg::RowCopyParams vcp{};
@@ -487,7 +513,6 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
     st = hip_status(zg::launch_row_copy(vcp, hs), "v copy launch");
     if (st != ZG_OK) return st;
 
-    const int G = (int)(Hq / Hkv);
     const int mq = 256 / G;
     zg::PrefillParams pp{};
     pp.q = static_cast<const uint16_t*>(q);
@@ -505,7 +530,7 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
     pp.Hq = (int32_t)Hq;
     pp.Hkv = (int32_t)Hkv;
     pp.pos0 = pos0;
-    pp.window = (ring && W < n_keys) ? (int32_t)W : 0;  // a window covering every key is causal
+    pp.window = window;
     pp.n_qtiles = (T + mq - 1) / mq;
     pp.kv_rows = kv_rows;
     pp.n_keys = (int32_t)n_keys;
@@ -515,17 +540,23 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
     pp.rope = rt;
     if ((int64_t)pp.n_qtiles * B * Hkv >= (int64_t(1) << 31))
       return fail(ZG_ERR_SHAPE, "grid too large");
-    st = hip_status(zg::launch_prefill_general(pp, G, cfg->gated != 0, hs), "prefill launch");
+    if (swa) {
+      pp.seg_steps = swa_seg_steps(B, T, Hkv);
+      st = hip_status(zg::launch_prefill_swa(pp, cfg->gated != 0, hs), "prefill launch");
+    } else {
+      st = hip_status(zg::launch_prefill_general(pp, G, cfg->gated != 0, hs), "prefill launch");
+    }
     if (st != ZG_OK) return st;
     if (ring) {
       // the ring keeps the last W positions; written after the attention has read the context
       const int64_t first = std::max<int64_t>(pos0, pos0 + T - W);
       for (int which = 0; which < 2; ++which) {
         zg::RowCopyParams w{};
-        w.src = which ? vs : ks;
+        const bool raw = swa && which == 0;  // K: the unfolded rows
+        w.src = which ? vs : (raw ? k_raw : ks);
         w.dst = which ? vc : kc;
-        w.src_bstride = kv_rows; w.dst_bstride = W;
-        w.src_row0 = n_ctx + (first - pos0); w.dst_row0 = first;
+        w.src_bstride = raw ? T : kv_rows; w.dst_bstride = W;
+        w.src_row0 = (raw ? 0 : n_ctx) + (first - pos0); w.dst_row0 = first;
         w.src_stride = row; w.dst_stride = row;
         w.src_ring = 0; w.dst_ring = W;
         w.row_elems = (int32_t)row; w.rows = (int32_t)(pos0 + T - first); w.B = B;

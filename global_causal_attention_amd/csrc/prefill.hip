@@ -206,6 +206,8 @@ __global__ __launch_bounds__(256) void kprep_kernel(KPrepParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      if (p.khat_raw && cur[i].valid)
+        *reinterpret_cast<u32x4*>(p.khat_raw + (base + grp + 4 * i) * kHeadDim + 8 * c) = pack8(x[i]);
       if (p.fold) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[i][j] *= fv[j];
@@ -610,7 +612,17 @@ __global__ __launch_bounds__(256) void row_copy_kernel(RowCopyParams p) {
   int64_t rs = p.src_row0 + j, rd = p.dst_row0 + j;
   if (p.src_ring > 0) rs %= p.src_ring;
   if (p.dst_ring > 0) rd %= p.dst_ring;
-  const u32x4 v = *reinterpret_cast<const u32x4*>(p.src + (b * p.src_bstride + rs) * p.src_stride + 8 * c);
+  u32x4 v = *reinterpret_cast<const u32x4*>(p.src + (b * p.src_bstride + rs) * p.src_stride + 8 * c);
+  if (p.fold) {
+    float x[8];
+    unpack8(v, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = (8 * c + e) & (kHeadDim - 1);
+      x[e] *= (d >= p.rot_dim && p.fold_w) ? p.fold_scale * p.fold_w[d] : p.fold_scale;
+    }
+    v = pack8(x);
+  }
   *reinterpret_cast<u32x4*>(p.dst + (b * p.dst_bstride + rd) * p.dst_stride + 8 * c) = v;
 }
 

@@ -76,17 +76,22 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
   const int hg = wave & 3;
   const int qb = wave >> 2;
   const int head = kvh * 4 + hg;
-  const int t_seg0 = seg * p.seg_steps;   // first 64-query step (= tile index) of the run
+  const int t_seg0 = seg * p.seg_steps;   // first 64-query step of the run
   const int n_steps = min(p.seg_steps, (T + 63) / 64 - t_seg0);
+  // Query row t reads key rows up to qoff + t (qoff > 0: a cached context precedes the new
+  // rows). The newest key tile of step tc is tq0 + tc; with qoff = 0 or 63 (mod 64) and W <= 128
+  // a step's keys span at most three 64-key tiles, which the ring holds.
+  const int qoff = p.qoff;
+  const int tq0 = (qoff + 63) >> 6;
 
   // ---- K/V tiles: waves 0-3 bring K row groups 4 wg .. 4 wg + 3, waves 4-7 the V ones
   const bool v_loader = wave >= 4;
   const int wg = wave & 3;
   const int row_bytes = (int)((v_loader ? p.sv : (int64_t)p.Hkv * kHeadDim) * 2);
-  const uint16_t* slab = v_loader ? p.v + (int64_t)b * T * p.sv + (int64_t)kvh * kHeadDim
-                                  : p.khat + ((int64_t)b * T * p.Hkv + kvh) * kHeadDim;
+  const uint16_t* slab = v_loader ? p.v + (int64_t)b * p.kv_rows * p.sv + (int64_t)kvh * kHeadDim
+                                  : p.khat + ((int64_t)b * p.kv_rows * p.Hkv + kvh) * kHeadDim;
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, T * row_bytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, p.n_keys * row_bytes, 0x00020000);
   const uint32_t lds_kv = (uint32_t)(uintptr_t)smem + (v_loader ? kSwaTile : 0);
   auto dma_tile = [&](int t) {  // tile t (rows 64t .. 64t + 63) into ring slot t % 3
 #pragma unroll
@@ -159,20 +164,21 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
     for (int m = 0; m < 8; ++m) gch[m] = *reinterpret_cast<const u32x4*>(g + 8 * (2 * m + hi));
   };
 
-  // ---- start of the run: the tiles before the first step and the first q rows
+  // ---- start of the run: the tiles before the first step's newest one, and the first q rows
   {
-    const int t_first = max(0, (64 * t_seg0 - W + 1) >> 6);
-    for (int t = t_first; t < t_seg0; ++t) dma_tile(t);
+    const int t_first = max(0, (qoff + 64 * t_seg0 - W + 1) >> 6);
+    for (int t = t_first; t < tq0 + t_seg0; ++t) dma_tile(t);
     dma_q(0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   for (int step = 0; step < n_steps; ++step) {
-    const int tc = t_seg0 + step;           // this step's tile
+    const int tc = t_seg0 + step;           // this step's query rows 64 tc .. 64 tc + 63
     const int qbase = 64 * tc + 32 * qb;
     const int my_q = qbase + l32;
+    const int qk = qoff + qbase;            // key row of this wave's first query
     const bool has_next = step + 1 < n_steps;
-    dma_tile(tc);
+    dma_tile(tq0 + tc);
 
     // -- q prologue (raw rows landed before the previous epilogue). Lane pair (r, half) holds dims
     // 64 half .. 64 half + 63 of row r: sum of squares for the RMS factor, and on half 0 the
@@ -274,11 +280,11 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
       for (int st = 0; st < 8; ++st)
         s = mfma32(*reinterpret_cast<const bf16x8*>(kp + ((st & 1) ? k_odd : k_even) + 128 * st), qf[st], s);
       if constexpr (!first) s = mfma32(one_op, qm, s);
-      // masks: key k0 + c_r + 4 hi is valid for query my_q when 0 <= my_q - key < W, i.e. when
-      // (unsigned)(t - c_r) < W with t = my_q - k0 - 4 hi
+      // masks: key k0 + c_r + 4 hi is valid for the query at key row qoff + my_q when
+      // 0 <= qoff + my_q - key < W, i.e. when (unsigned)(t - c_r) < W with t = qoff + my_q - k0 - 4 hi
       const int k0 = 32 * kb;
-      if (k0 + 31 > qbase || k0 < qbase + 32 - W) {
-        const uint32_t t = (uint32_t)(my_q - k0 - key_lane);
+      if (k0 + 31 > qk || k0 < qk + 32 - W) {
+        const uint32_t t = (uint32_t)(qoff + my_q - k0 - key_lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t cr = 8 * (r >> 2) + (r & 3);
@@ -358,9 +364,9 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
           o[db] = mfma32(__builtin_bit_cast(bf16x8, both), __builtin_bit_cast(bf16x8, pk[st]), o[db]);
         }
     };
-    const int kb_lo = max(0, (qbase - W + 1) >> 5);
-    const int kb_hi = qbase >> 5;
-    const int kb_new = 2 * tc;
+    const int kb_lo = max(0, (qk - W + 1) >> 5);
+    const int kb_hi = (qk + 31) >> 5;
+    const int kb_new = 2 * (tq0 + tc);  // first block of the newest tile (kb_hi >= kb_new)
     // tile tc has landed once every wave's share of it has; only the loads issued after it (next
     // q rows: 8 instructions, gate: 8) may still be in flight
     auto wait_new_tile = [&]() {
@@ -461,6 +467,14 @@ static hipError_t launch_swa_t(const PrefillParams& p, hipStream_t s) {
 
 bool prefill_uses_swa(int window, int group, int rot_half) {
   return window > 0 && window <= 128 && group == 4 && rot_half == kSwaRotHalf;
+}
+
+bool prefill_swa_offset_ok(int64_t qoff, int window) {
+  // a step's key rows [qoff + 64 tc - W + 1, qoff + 64 tc + 63] must span at most three 64-key
+  // tiles, and every wave's queries must reach the step's newest tile (qoff = 0 or 63 mod 64)
+  const int64_t r = qoff & 63;
+  return window > 0 && window <= 128 && (r == 0 || r == 63) &&
+         ((qoff - window + 1) & 63) <= 129 - window;
 }
 
 hipError_t launch_prefill_swa(const PrefillParams& p, bool gated, hipStream_t s) {

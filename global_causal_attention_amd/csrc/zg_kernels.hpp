@@ -32,6 +32,8 @@ struct KPrepParams {
   int32_t fold;
   float fold_scale;
   const float* fold_w;
+  // When non-null, the unfolded k_hat rows also go here, packed [B, T, Hkv, 128].
+  uint16_t* khat_raw;
 };
 
 struct PrefillParams {
@@ -152,6 +154,12 @@ struct RowCopyParams {
   int32_t row_elems;                 // elements copied per row (multiple of 8)
   int32_t rows;                      // rows per sequence
   int32_t B;
+  // When fold is set, element e of a row is multiplied as KPrepParams::fold does for head dim
+  // e mod 128 (fold_scale, times fold_w for dims >= rot_dim) and rounded to bf16.
+  int32_t fold;
+  int32_t rot_dim;
+  float fold_scale;
+  const float* fold_w;
 };
 hipError_t launch_row_copy(const RowCopyParams& p, hipStream_t s);
 
@@ -161,6 +169,9 @@ hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, int
 // True when launch_prefill takes the streaming kernel for short windows (which reads seg_steps and
 // expects keys prepared with KPrepParams::fold set).
 bool prefill_uses_swa(int window, int group, int rot_half);
+// True when the streaming kernel can take key rows offset by qoff from the query rows (a cached
+// context of qoff rows precedes the new ones): qoff = 0 or 63 (mod 64).
+bool prefill_swa_offset_ok(int64_t qoff, int window);
 hipError_t launch_prefill_swa(const PrefillParams& p, bool gated, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStream_t s);
 // The general tiled kernel only (any window, key rows offset from query rows, unfolded keys).

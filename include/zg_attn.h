@@ -100,7 +100,9 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
  * The result equals zg_attn_prefill over the whole sequence 0 .. pos0+T-1, rows pos0 .. pos0+T-1,
  * up to rounding; pos0 = 0 with any cache contents is the plain prefill plus the cache fill.
  *   workspace >= zg_attn_prefill_cached_workspace_bytes(cfg, B, T) (0 for linear caches: the
- *   attention reads the cache; rings stage their W-1 context rows and the new rows).
+ *   attention reads the cache; rings stage their W-1 context rows and the new rows, K and V,
+ *   plus one more copy of the new rows' normalised keys: 2 (W-1+T) + T rows of Hkv*256 bytes per
+ *   sequence, each area rounded up to 256 bytes).
  * Errors as for prefill; linear cache_stride < pos0 + T -> ZG_ERR_SHAPE; (context + T) rows of
  * more than 4 GiB per sequence -> ZG_ERR_UNSUPPORTED. */
 size_t zg_attn_prefill_cached_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T);

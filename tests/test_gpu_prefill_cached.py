@@ -5,7 +5,11 @@ fixed 128-token window, global layers the whole sequence).
 
 The oracle runs the plain definition over the whole sequence (prefill rows pos0 .. pos0+T-1 of the
 concatenated chunks, then the decode row); the expected cache rows are its normalised, rotated keys
-(one bf16 rounding: relative 2^-7) and the values bit for bit."""
+(one bf16 rounding: relative 2^-7) and the values bit for bit.
+
+Ring chunks whose context is 0 or 63 (mod 64) rows run on the banded streaming kernel (context keys
+folded as they are gathered, the ring rewritten from unfolded copies): contexts 0, 127, 64 and 63
+below; the partly filled ring of 60 rows takes the general tiled kernel."""
 import numpy as np
 import pytest
 import torch
@@ -23,6 +27,7 @@ CASES = [  # window, gated, B, T1, T2, RoPE base
     (128, True, 2, 200, 150, 1e7),   # ring full before chunk 2; chunk 2 longer than the window
     (128, True, 1, 60, 300, 1e6),    # ring partly filled before chunk 2
     (128, True, 2, 130, 64, 1e7),    # chunk 2 shorter than the window: the ring keeps chunk-1 rows
+    (128, True, 1, 64, 200, 1e6),    # 64 context rows: key rows offset by a whole tile
     (64, True, 1, 100, 37, 1e4),     # another window
     (0, False, 2, 200, 150, 1e7),    # linear caches (global layer)
     (0, False, 1, 1, 257, 1e6),      # one-token first chunk
@@ -93,3 +98,6 @@ def test_first_chunk_equals_plain_prefill():
         ref = zg.zg_attn_prefill(cfg, q, k, v, g if W else None)
         torch.cuda.synchronize()
         assert_parity(a, f64(ref), f"pos0=0 cached vs plain W={W}", max_abs=2e-2, mean_abs=2e-3)
+        if W:  # both run the banded streaming kernel on the same folded keys
+            assert torch.equal(a, ref), "pos0=0 cached vs plain: banded kernel results differ"
+
