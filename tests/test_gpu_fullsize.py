@@ -7,7 +7,10 @@ same tensors copied to the host):
     benchmark times (runs of 32 steps of 64 queries for the local layer);
   * B=64 decode step, 128-slot rings and linear caches with context lengths uniform on
     [8192, 65536], base 1e7: every ring sequence, sampled linear sequences;
-  * B=1, T=262144 gated local and full causal layers, base 1e7: sampled rows.
+  * B=1, T=262144 gated local and full causal layers, base 1e7: sampled rows;
+  * chunked prefill, B=4 sequences with 16384 cached positions continuing with 2048 new tokens,
+    base 1e6 (128-slot rings: the banded streaming kernel on a 127-row context; linear caches):
+    sampled new rows of the first and last sequence.
 Sampled rows cover the sequence edges, tile/step/run boundaries (+-1 around multiples of 64 and
 2048) and seeded uniform positions."""
 import numpy as np
@@ -122,3 +125,50 @@ def test_t262144_sampled_rows(W):
         q, k, v = (_host(x[n]) for n in ("q", "k", "v"))
         ref = oracle.prefill_rows(q, k, v, None, rows, window=0, gated=False, rope_base=base)
     assert_parity(_host(out[:, rows]), ref, f"B=1 T=262144 W={W}, {len(rows)} rows")
+
+
+@pytest.mark.parametrize("W", [128, 0])
+def test_chunked_b4_ctx16384_sampled_rows(W):
+    """zg_attn_prefill_cached with the inputs, caches and call of bench.py's chunked workload (same
+    seed and draw order). The oracle row for new token t (position P = 16384 + t) is one decode
+    step over the cache as it stands before P: the original cached rows for positions below 16384
+    and, for 16384 .. P-1, the oracle's own k_hat and v of the new tokens."""
+    Bc, ctx, Tc, base = 4, 16384, 2048, 1e6
+    print(f"[case] chunked full size W={W}", flush=True)
+    gen = si.generator(1005, device=DEV)
+    x = si.prefill_layer(gen, Bc, Tc, 32, 8, 128, gated=True, device=DEV)
+    for win in (0, 128):  # bench.py's draw order
+        rows = win if win else ctx + Tc
+        kc = si.randn_bf16(gen, (Bc, rows, 8, 128), device=DEV)
+        vc = si.randn_bf16(gen, (Bc, rows, 8, 128), device=DEV)
+        if win == W:
+            break
+    kc0, vc0 = kc.clone(), vc.clone()
+    cfg = zg.AttnConfig(window=W, gated=W > 0, rope_base=base)
+    need = zg.zg_attn_prefill_cached_workspace_bytes(cfg, Bc, Tc)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
+    out = zg.zg_attn_prefill_cached(cfg, x["q"], x["k"], x["v"], x["gate"] if W else None, kc, vc,
+                                    pos0=ctx, workspace=ws)
+    torch.cuda.synchronize()
+    picks = [0, 1, 62, 63, 64, 126, 127, 128, 1023, 1024, 2046, 2047]
+    picks += np.random.default_rng(31).integers(0, Tc, 3).tolist()
+    picks = sorted(set(picks))
+    got, ref = [], []
+    for b in (0, Bc - 1):
+        q, k, v, g = (_host(x[n][b]) for n in ("q", "k", "v", "gate"))
+        k_cache, v_cache = _host(kc0[b]), _host(vc0[b])
+        khat_new = oracle.qk_prologue(k, ctx + np.arange(Tc), None, rot_dim=42, rope_base=base,
+                                      eps=1e-6)
+        for t in picks:
+            P = ctx + t
+            kcb, vcb = k_cache.copy(), v_cache.copy()
+            for p in range(max(ctx, P - W + 1) if W else ctx, P):
+                slot = p % W if W else p
+                kcb[slot], vcb[slot] = khat_new[p - ctx], v[p - ctx]
+            o, _, _ = oracle.decode(q[t][None], k[t][None], v[t][None], g[t][None], kcb[None],
+                                    vcb[None], np.array([P + 1]), window=W, gated=W > 0,
+                                    rope_base=base)
+            ref.append(o[0])
+            got.append(_host(out[b, t]))
+    assert_parity(np.stack(got), np.stack(ref),
+                  f"chunked B=4 ctx=16384 +2048 W={W}, {len(picks)} rows x 2 sequences")
