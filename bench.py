@@ -187,7 +187,7 @@ def bench_block(torch, zg, si, dev, stream, args):
     # changed since it was taken)
     from global_causal_attention_amd.counters import lookup_traffic
     grid_prefill = ((T + 63) // 64) * B * HKV * 512     # threads: 64-query tiles x (b, kv head)
-    grid_kprep = ((B * T * HKV + 127) // 128) * 256      # threads: 128 key rows per block
+    grid_kprep = min((B * T * HKV + 31) // 32, 2048) * 256  # threads: 32 rows per block pass
     parts = [lookup_traffic("prefill_kernel<4, false>", grid_prefill),
              lookup_traffic("kprep_kernel", grid_kprep)]
     glo_traffic = None if None in parts else sum(parts)

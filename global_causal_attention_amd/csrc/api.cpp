@@ -461,6 +461,12 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
       if (swa) k_raw = vs + align256((size_t)B * (W - 1 + T) * row * 2) / 2;
       kv_rows = n_keys;
       row0 = n_ctx;
+    }
+    // copies ahead of the attention, issued as one launch: the ring's context K and V into the
+    // staging rows 0 .. n_ctx-1, the new tokens' v after them (or into the linear cache)
+    zg::RowCopyParams pre[3];
+    int n_pre = 0;
+    if (ring) {
       if (n_ctx > 0) {
         for (int which = 0; which < 2; ++which) {
           zg::RowCopyParams g{};
@@ -477,8 +483,7 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
             g.fold_scale = scale_log2(cfg);
             g.fold_w = q_norm_w;
           }
-          st = hip_status(zg::launch_row_copy(g, hs), "ring gather launch");
-          if (st != ZG_OK) return st;
+          pre[n_pre++] = g;
         }
       }
     }
@@ -510,7 +515,8 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
     vcp.src_row0 = 0; vcp.dst_row0 = row0;
     vcp.src_stride = s.v; vcp.dst_stride = row;
     vcp.row_elems = (int32_t)row; vcp.rows = T; vcp.B = B;
-    st = hip_status(zg::launch_row_copy(vcp, hs), "v copy launch");
+    pre[n_pre++] = vcp;
+    st = hip_status(zg::launch_row_copies(pre, n_pre, hs), "ring gather / v copy launch");
     if (st != ZG_OK) return st;
 
     const int mq = 256 / G;
@@ -550,8 +556,10 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
     if (ring) {
       // the ring keeps the last W positions; written after the attention has read the context
       const int64_t first = std::max<int64_t>(pos0, pos0 + T - W);
+      zg::RowCopyParams wr[2];
       for (int which = 0; which < 2; ++which) {
-        zg::RowCopyParams w{};
+        zg::RowCopyParams& w = wr[which];
+        w = zg::RowCopyParams{};
         const bool raw = swa && which == 0;  // K: the unfolded rows
         w.src = which ? vs : (raw ? k_raw : ks);
         w.dst = which ? vc : kc;
@@ -560,9 +568,9 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
         w.src_stride = row; w.dst_stride = row;
         w.src_ring = 0; w.dst_ring = W;
         w.row_elems = (int32_t)row; w.rows = (int32_t)(pos0 + T - first); w.B = B;
-        st = hip_status(zg::launch_row_copy(w, hs), "ring write launch");
-        if (st != ZG_OK) return st;
       }
+      st = hip_status(zg::launch_row_copies(wr, 2, hs), "ring write launch");
+      if (st != ZG_OK) return st;
     }
     return ZG_OK;
   } catch (...) {

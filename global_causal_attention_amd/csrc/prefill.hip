@@ -600,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 // Cache hand-off: copies of whole token rows between caches and staging buffers, 16 bytes per
 // lane (the pages' KV-cache layout: local layers a ring of the last window positions, global
 // layers one row per position; zh-TW translation page, section 2.3).
-__global__ __launch_bounds__(256) void row_copy_kernel(RowCopyParams p) {
+__device__ __forceinline__ void copy_rows(const RowCopyParams& p) {
   const int lanes_per_row = p.row_elems / 8;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_seq = (int64_t)p.rows * lanes_per_row;
@@ -626,10 +626,30 @@ __global__ __launch_bounds__(256) void row_copy_kernel(RowCopyParams p) {
   *reinterpret_cast<u32x4*>(p.dst + (b * p.dst_bstride + rd) * p.dst_stride + 8 * c) = v;
 }
 
-hipError_t launch_row_copy(const RowCopyParams& p, hipStream_t s) {
-  const int64_t n = (int64_t)p.B * p.rows * (p.row_elems / 8);
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(row_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+// Up to three independent copies in one launch: blockIdx.y picks the copy.
+struct RowCopyBatch {
+  RowCopyParams job[3];
+};
+
+__global__ __launch_bounds__(256) void row_copy_kernel(RowCopyBatch pb) {
+  switch (blockIdx.y) {
+    case 0: copy_rows(pb.job[0]); break;
+    case 1: copy_rows(pb.job[1]); break;
+    default: copy_rows(pb.job[2]); break;
+  }
+}
+
+hipError_t launch_row_copies(const RowCopyParams* jobs, int n, hipStream_t s) {
+  if (n < 1 || n > 3) return hipErrorInvalidValue;
+  RowCopyBatch pb{};
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    pb.job[i] = jobs[i];
+    const int64_t e = (int64_t)jobs[i].B * jobs[i].rows * (jobs[i].row_elems / 8);
+    blocks = std::max<int64_t>(blocks, (e + 255) / 256);
+  }
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(row_copy_kernel, dim3((unsigned)blocks, (unsigned)n), dim3(256), 0, s, pb);
   return hipGetLastError();
 }
 

@@ -161,7 +161,8 @@ struct RowCopyParams {
   float fold_scale;
   const float* fold_w;
 };
-hipError_t launch_row_copy(const RowCopyParams& p, hipStream_t s);
+// n = 1..3 independent copies (distinct destinations) in one launch.
+hipError_t launch_row_copies(const RowCopyParams* jobs, int n, hipStream_t s);
 
 hipError_t launch_kprep(const KPrepParams& p, hipStream_t s);
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t n_blocks,
