@@ -58,67 +58,113 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 }  // namespace
 
+// Prep of one decode step. For each sequence b (new token at pos = seqlens[b] - 1): the Hq query
+// rows become q_hat (fp32 holding bf16-rounded values, workspace), the Hkv key rows become k_hat,
+// written with v_new into cache row pos (ring slot pos % window). Sixteen lanes per 256-byte head
+// row, lane c holding dims 8c..8c+7; a 256-thread block takes 16 rows of the flattened
+// [B, Hq + Hkv] row list. The RMS sum is reduced over the row's lanes; RoPE pairs (i, i + h) are
+// exchanged through the wave's LDS rows, lane c rotating pairs c and c + 16.
+constexpr int kDpStage = 68;  // floats per staged row (64 used; padded)
+
 __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeParams p) {
-  __shared__ float stage[128 * 64];
-  const int b = blockIdx.x;
-  const int pos = p.seqlens[b] - 1;
-  // a length outside [1, cache rows] is a caller error: touch nothing (the output is unspecified)
-  if (pos < 0 || (p.window == 0 && pos >= p.rows)) return;
-  const int64_t row = p.window > 0 ? (int64_t)(pos % p.window) : (int64_t)pos;
-  const int pair = threadIdx.x >> 1;
-  const int half = threadIdx.x & 1;
+  __shared__ __attribute__((aligned(16))) float stage[4][4][kDpStage];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4;
+  const int c = lane & 15;
   const int n_rows = p.Hq + p.Hkv;
-  for (int r0 = 0; r0 < n_rows; r0 += 128) {
-    const int r = r0 + pair;
-    if (r < n_rows) {
-      const bool is_q = r < p.Hq;
-      const int h = is_q ? r : r - p.Hq;
-      const uint16_t* src = is_q ? p.q_new + ((int64_t)b * p.Hq + h) * kHeadDim
-                                 : p.k_new + ((int64_t)b * p.Hkv + h) * kHeadDim;
-      float x[64];
-      const u32x4* s4 = reinterpret_cast<const u32x4*>(src + 64 * half);
+  const int64_t rg = (int64_t)blockIdx.x * 16 + wave * 4 + grp;  // flattened (b, row)
+  const bool in_range = rg < (int64_t)p.B * n_rows;
+  const int b = in_range ? (int)(rg / n_rows) : 0;
+  const int r = (int)(rg - (int64_t)b * n_rows);
+  const int pos = in_range ? p.seqlens[b] - 1 : -1;
+  // a length outside [1, cache rows] is a caller error: touch nothing (the output is unspecified)
+  const bool valid = in_range && pos >= 0 && (p.window > 0 || pos < p.rows);
+  const bool is_q = r < p.Hq;
+  const int h = is_q ? r : r - p.Hq;
+  const int hr = p.rope.half;
+  const int rot = 2 * hr;
+
+  const uint16_t* src = is_q ? p.q_new + ((int64_t)b * p.Hq + h) * kHeadDim
+                             : p.k_new + ((int64_t)b * p.Hkv + h) * kHeadDim;
+  float x[8];
+  unpack8(valid ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0u, 0u, 0u, 0u}, x);
+  float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) unpack8(s4[i], x + 8 * i);
-      norm_rope_row(x, half, is_q ? p.q_norm_w : p.k_norm_w, p.eps, pos, p.rope, stage, pair,
-                    128);
-      if (is_q) {
-        f32x4* dst = reinterpret_cast<f32x4*>(p.qhat + ((int64_t)b * p.Hq + h) * kHeadDim + 64 * half);
+  for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+  ss = row16_sum(ss);
+  const float inv = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
+  const float* w = is_q ? p.q_norm_w : p.k_norm_w;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          // round to bf16 like the prefill matrix-core operand, keep as fp32
-          const uint32_t w0 = pack_bf16(x[4 * i], x[4 * i + 1]);
-          const uint32_t w1 = pack_bf16(x[4 * i + 2], x[4 * i + 3]);
-          dst[i] = f32x4{bf16lo(w0), bf16hi(w0), bf16lo(w1), bf16hi(w1)};
-        }
-      } else if (!p.fp8) {
-        const int64_t off = ((int64_t)b * p.rows + row) * p.Hkv * kHeadDim + (int64_t)h * kHeadDim;
-        u32x4* kd = reinterpret_cast<u32x4*>(p.k_cache + off + 64 * half);
+  for (int j = 0; j < 8; ++j) x[j] *= inv * (w ? w[8 * c + j] : 1.0f);
+  if (hr > 0) {
+    double rev0 = 0.0, rev1 = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kd[i] = pack8(x + 8 * i);
-        const u32x4* vs = reinterpret_cast<const u32x4*>(
-            p.v_new + ((int64_t)b * p.Hkv + h) * kHeadDim + 64 * half);
-        u32x4* vd = reinterpret_cast<u32x4*>(p.v_cache + off + 64 * half);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vd[i] = vs[i];
-      } else {
-        // E4M3 rows: one byte per element
-        const int64_t off = ((int64_t)b * p.rows + row) * p.Hkv * kHeadDim + (int64_t)h * kHeadDim;
-        u32x4* kd = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(p.k_cache) + off + 64 * half);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kd[i] = pack16_e4m3(x + 16 * i, p.k_inv);
-        const u32x4* vs = reinterpret_cast<const u32x4*>(
-            p.v_new + ((int64_t)b * p.Hkv + h) * kHeadDim + 64 * half);
-        u32x4* vd = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(p.v_cache) + off + 64 * half);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float vf[16];
-          unpack8(vs[2 * i], vf);
-          unpack8(vs[2 * i + 1], vf + 8);
-          vd[i] = pack16_e4m3(vf, p.v_inv);
-        }
+    for (int j = 0; j < 16; ++j) {
+      if (c == j) {
+        rev0 = p.rope.rev[j];
+        rev1 = p.rope.rev[j + 16];
       }
     }
-    __syncthreads();
+    float* sr = &stage[wave][grp][0];
+    const bool rotates = 8 * c < rot;
+    if (rotates) {
+      *reinterpret_cast<f32x4*>(sr + 8 * c) = f32x4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f32x4*>(sr + 8 * c + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS ops complete in order
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int pi = c + 16 * k;
+      if (pi < hr) {
+        float cs, sn;
+        rope_cs(pos, k ? rev1 : rev0, cs, sn);
+        const float a = sr[pi];
+        const float bb = sr[pi + hr];
+        sr[pi] = a * cs - bb * sn;
+        sr[pi + hr] = bb * cs + a * sn;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (rotates) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(sr + 8 * c);
+      const f32x4 hi4 = *reinterpret_cast<const f32x4*>(sr + 8 * c + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = lo[j];
+        x[4 + j] = hi4[j];
+      }
+    }
+  }
+  if (!valid) return;
+  if (is_q) {
+    // round to bf16 like the prefill matrix-core operand, keep as fp32
+    f32x4* dst = reinterpret_cast<f32x4*>(p.qhat + ((int64_t)b * p.Hq + h) * kHeadDim + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t w0 = pack_bf16(x[4 * i], x[4 * i + 1]);
+      const uint32_t w1 = pack_bf16(x[4 * i + 2], x[4 * i + 3]);
+      dst[i] = f32x4{bf16lo(w0), bf16hi(w0), bf16lo(w1), bf16hi(w1)};
+    }
+    return;
+  }
+  const int64_t row = p.window > 0 ? (int64_t)(pos % p.window) : (int64_t)pos;
+  const int64_t off = ((int64_t)b * p.rows + row) * p.Hkv * kHeadDim + (int64_t)h * kHeadDim + 8 * c;
+  const u32x4 vw = *reinterpret_cast<const u32x4*>(p.v_new + ((int64_t)b * p.Hkv + h) * kHeadDim + 8 * c);
+  if (!p.fp8) {
+    *reinterpret_cast<u32x4*>(p.k_cache + off) = pack8(x);
+    *reinterpret_cast<u32x4*>(p.v_cache + off) = vw;
+  } else {
+    // E4M3 rows: one byte per element
+    float vf[8];
+    unpack8(vw, vf);
+    const float ki = p.k_inv, vi = p.v_inv;
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.k_cache) + off) =
+        u32x2{pack4_e4m3(x[0] * ki, x[1] * ki, x[2] * ki, x[3] * ki),
+              pack4_e4m3(x[4] * ki, x[5] * ki, x[6] * ki, x[7] * ki)};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.v_cache) + off) =
+        u32x2{pack4_e4m3(vf[0] * vi, vf[1] * vi, vf[2] * vi, vf[3] * vi),
+              pack4_e4m3(vf[4] * vi, vf[5] * vi, vf[6] * vi, vf[7] * vi)};
   }
 }
 
@@ -906,7 +952,8 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(p.B), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)(((int64_t)p.B * (p.Hq + p.Hkv) + 15) / 16)),
+                     dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = p.Hq / p.Hkv;
