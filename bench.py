@@ -75,7 +75,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the attention core shards by (batch x KV head) with no exchange; see DESIGN.md)",
+              f"(the attention core shards by (batch x KV head) with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -36,7 +36,7 @@ typedef enum {
   ZG_OK = 0,
   ZG_ERR_NULL = 1,        /* a required pointer is NULL */
   ZG_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or inconsistent */
-  ZG_ERR_UNSUPPORTED = 3, /* a valid configuration this build has no kernel for */
+  ZG_ERR_UNSUPPORTED = 3, /* a valid configuration the library has no kernel for */
   ZG_ERR_WORKSPACE = 4,   /* workspace pointer NULL or smaller than the *_workspace_bytes query */
   ZG_ERR_HIP = 5          /* HIP runtime / launch error */
 } zg_status;

@@ -10,7 +10,7 @@ page, architecture paragraph):
   * the local output is multiplied elementwise by sigmoid(g_proj(h)) before o_proj; global layers
     have no gate.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * RMSNorm is per head over the 128 head dims with one shared weight vector for q and one for k;
   * RMSNorm is applied before RoPE (the order in which Fig. 3 lists them);
   * rot_dim = floor(0.33 * 128) = 42; rotate-half pairing (i, i + rot_dim/2), frequency

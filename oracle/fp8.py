@@ -9,7 +9,7 @@ bits and no infinities: exponent field e = 1..15 with mantissa m = 0..7 encodes 
 except e = 15, m = 7, which is NaN; e = 0 encodes the subnormals m/8 * 2^-6. The largest finite
 value is 448, the smallest subnormal 2^-9.
 
-Reading (listed in the design doc): values are rounded to the nearest E4M3 value, ties to the even
+Reading: values are rounded to the nearest E4M3 value, ties to the even
 mantissa, and saturate at +-448.
 
 Pins (tests/test_fp8_oracle.py): the value set has 127 non-negative members with the extremes

@@ -6,7 +6,7 @@ and projected by o_proj; global layers (6, 12, 18, 24, 30 of 32) attend over the
 gate. Hidden size 4096, 32 query heads and 8 KV heads of dim 128. Pre-LN (§3.1 "training
 efficiency").
 
-Readings (listed in the design doc): Pre-LN residual x <- x + o_proj(attn(RMSNorm(x))); input-norm weight
+Readings: Pre-LN residual x <- x + o_proj(attn(RMSNorm(x))); input-norm weight
 1, eps 1e-6; no biases; no MLP (the workload is attention-only); no final norm; weights are [out, in].
 
 Parity pins (tests/test_stack_oracle.py): W_o = 0 leaves x unchanged; T = 1 closed form (one key, so
