@@ -317,7 +317,7 @@ def bench_decode(torch, zg, si, dev, stream, reps):
     del lin_k8, lin_v8
     res["workload"] = "B=64, Hq=32 Hkv=8 D=128, ring W=128 gated; linear L~U[8192,65536] ungated; base 1e7; cold MALL"
     from global_causal_attention_amd.counters import lookup_traffic
-    parts = [lookup_traffic("decode_prep_kernel", 16384),
+    parts = [lookup_traffic("decode_prep_kernel", ((Bd * (HQ + HKV) + 15) // 16) * 256),
              lookup_traffic("decode_mfma_kernel<false>", Bd * HKV * 16 * 1024),
              lookup_traffic("decode_combine_kernel", 262144)]
     res["roofline"] = {"bound": "hbm", "achieved": res["linear"]["GBps"], "peak": HBM_PEAK / 1e9,
