@@ -223,9 +223,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int per_tile = p.B * p.Hkv;
-  const int t_idx = blockIdx.x / per_tile;
-  const int bh = blockIdx.x - t_idx * per_tile;
+  int t_idx, bh;  // the workgroups of one (sequence, KV head) together on an XCD
+  xcd_pair_major(blockIdx.x, p.B * p.Hkv, p.n_qtiles, t_idx, bh);
   const int qtile = (p.window == 0) ? (p.n_qtiles - 1 - t_idx) : t_idx;  // heavy tiles first
   const int b = bh / p.Hkv;
   const int kvh = bh - b * p.Hkv;
@@ -431,9 +430,10 @@ void bwd_kv_kernel(BwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int per_tile = p.B * p.Hkv;
-  const int ktile = blockIdx.x / per_tile;  // for full causal attention, tile 0 has the most work
-  const int bh = blockIdx.x - ktile * per_tile;
+  // for full causal attention, tile 0 has the most work; the workgroups of one (sequence, KV
+  // head) together on an XCD
+  int ktile, bh;
+  xcd_pair_major(blockIdx.x, p.B * p.Hkv, (p.T + kNk - 1) / kNk, ktile, bh);
   const int b = bh / p.Hkv;
   const int kvh = bh - b * p.Hkv;
   const int T = p.T;

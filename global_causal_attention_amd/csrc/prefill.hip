@@ -238,22 +238,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item: heavy query tiles first for full causal attention. Workgroup i runs on XCD
-  // i mod 8; when the (sequence, KV head) pairs split evenly over the 8 XCDs, each XCD walks its
-  // pairs one at a time (all query tiles of a pair, heaviest first), so the workgroups resident on
-  // an XCD stream the same K/V tiles through its L2.
-  const int per_tile = p.B * p.Hkv;
+  // ---- work item: heavy query tiles first for full causal attention, the workgroups of one
+  // (sequence, KV head) together on an XCD
   int t_idx, bh;
-  if (per_tile % 8 == 0) {
-    const int x = blockIdx.x & 7;
-    const int j = blockIdx.x >> 3;
-    const int pl = j / p.n_qtiles;
-    t_idx = j - pl * p.n_qtiles;
-    bh = x + 8 * pl;
-  } else {
-    t_idx = blockIdx.x / per_tile;
-    bh = blockIdx.x - t_idx * per_tile;
-  }
+  xcd_pair_major(blockIdx.x, p.B * p.Hkv, p.n_qtiles, t_idx, bh);
   const int qtile = (p.window == 0) ? (p.n_qtiles - 1 - t_idx) : t_idx;
   const int b = bh / p.Hkv;
   const int kvh = bh - b * p.Hkv;

@@ -23,4 +23,21 @@ __device__ __forceinline__ i16x4 lds_read_tr(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// Work item of workgroup `block` in a grid of n_tiles tiles x per_pair (sequence, KV head) pairs,
+// tile index 0 being the heaviest. Workgroup i runs on XCD i mod 8; when the pairs split evenly
+// over the 8 XCDs, each XCD walks its pairs one at a time (all tiles of a pair, heaviest first), so
+// the workgroups resident on an XCD stream the same rows through its L2. Otherwise tile-major.
+__device__ __forceinline__ void xcd_pair_major(int block, int per_pair, int n_tiles, int& tile,
+                                               int& pair) {
+  if (per_pair % 8 == 0) {
+    const int j = block >> 3;
+    const int pl = j / n_tiles;
+    tile = j - pl * n_tiles;
+    pair = (block & 7) + 8 * pl;
+  } else {
+    tile = block / per_pair;
+    pair = block - tile * per_pair;
+  }
+}
+
 }  // namespace zg
