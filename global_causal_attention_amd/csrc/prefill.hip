@@ -308,7 +308,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const uint16_t* slab = v_loader ? p.v + (int64_t)b * p.kv_rows * p.sv + (int64_t)kvh * kHeadDim
                                   : p.khat + ((int64_t)b * p.kv_rows * p.Hkv + kvh) * kHeadDim;
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, p.n_keys * row_bytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, (int)((uint32_t)p.n_keys * (uint32_t)row_bytes),
+                                        0x00020000);  // byte count < 2^32, read as unsigned
   // lane -> (row (lane >> 4) of the 4-row group i, physical chunk lane & 15)
   auto dma_voff = [&](int i) -> uint32_t {
     const int row = 4 * i + (lane >> 4);  // row within the wave's 16 (swizzle uses row & 15)

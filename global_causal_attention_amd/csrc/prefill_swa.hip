@@ -91,7 +91,8 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
   const uint16_t* slab = v_loader ? p.v + (int64_t)b * p.kv_rows * p.sv + (int64_t)kvh * kHeadDim
                                   : p.khat + ((int64_t)b * p.kv_rows * p.Hkv + kvh) * kHeadDim;
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, p.n_keys * row_bytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, (int)((uint32_t)p.n_keys * (uint32_t)row_bytes),
+                                        0x00020000);  // byte count < 2^32, read as unsigned
   const uint32_t lds_kv = (uint32_t)(uintptr_t)smem + (v_loader ? kSwaTile : 0);
   auto dma_tile = [&](int t) {  // tile t (rows 64t .. 64t + 63) into ring slot t % 3
 #pragma unroll
@@ -108,7 +109,8 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
   // ---- raw q rows of this wave: row r at r * 256, chunk c at position c ^ (r & 15)
   const int q_row_bytes = (int)(p.sq * 2);
   const __amdgpu_buffer_rsrc_t rsrc_q = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.q + (int64_t)b * T * p.sq + (int64_t)head * kHeadDim), 0, T * q_row_bytes,
+      (void*)(p.q + (int64_t)b * T * p.sq + (int64_t)head * kHeadDim), 0,
+      (int)((uint32_t)T * (uint32_t)q_row_bytes),
       0x00020000);
   unsigned char* qs = smem + kSwaRing + wave * kSwaQArea;
   const uint32_t lds_q = (uint32_t)(uintptr_t)qs;
