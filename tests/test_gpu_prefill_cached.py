@@ -9,7 +9,7 @@ concatenated chunks, then the decode row); the expected cache rows are its norma
 
 Ring chunks whose context is 0 or 63 (mod 64) rows run on the banded streaming kernel (context keys
 folded as they are gathered, the ring rewritten from unfolded copies): contexts 0, 127, 64 and 63
-below; the partly filled ring of 60 rows takes the general tiled kernel."""
+below (gated and ungated); the partly filled ring of 60 rows takes the general tiled kernel."""
 import numpy as np
 import pytest
 import torch
@@ -28,6 +28,7 @@ CASES = [  # window, gated, B, T1, T2, RoPE base
     (128, True, 1, 60, 300, 1e6),    # ring partly filled before chunk 2
     (128, True, 2, 130, 64, 1e7),    # chunk 2 shorter than the window: the ring keeps chunk-1 rows
     (128, True, 1, 64, 200, 1e6),    # 64 context rows: key rows offset by a whole tile
+    (128, False, 2, 150, 100, 1e6),  # ungated ring layer, 127 context rows
     (64, True, 1, 100, 37, 1e4),     # another window
     (0, False, 2, 200, 150, 1e7),    # linear caches (global layer)
     (0, False, 1, 1, 257, 1e6),      # one-token first chunk
