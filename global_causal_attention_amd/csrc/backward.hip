@@ -77,10 +77,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int6
   return __builtin_amdgcn_make_buffer_rsrc(ub, 0, __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
 }
 
-// One 1 KB LDS-direct load: lane l's 16 bytes at voff go to LDS address m0 + 16 l.
-__device__ __forceinline__ void lds_dma(uint32_t m0, uint32_t voff, __amdgpu_buffer_rsrc_t r) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(m0), "v"(voff), "s"(r), "s"(0) : "memory", "m0");
+// One 1 KB LDS-direct load: lane l's 16 bytes at voff go to LDS address lds + 16 l.
+__device__ __forceinline__ void lds_dma(uint32_t lds, uint32_t voff, __amdgpu_buffer_rsrc_t r) {
+  lds_dma16(lds, voff, r, 0u);
 }
 
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

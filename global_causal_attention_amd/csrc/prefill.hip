@@ -324,8 +324,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     for (int i = 0; i < 4; ++i) {
       const uint32_t m0v = base + 4 * i * kRow;
       const uint32_t soff = (row0 + 4 * i) * (uint32_t)row_bytes;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   ::"s"(m0v), "v"(dma_voff(i)), "s"(rsrc), "s"(soff) : "memory", "m0");
+      lds_dma16(m0v, dma_voff(i), rsrc, soff);
     }
   };
   auto vm_wait = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };

@@ -101,8 +101,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
       const uint32_t m0v = lds_kv + (t % 3) * kSwaSlot + g * 1024;
       const uint32_t soff = (uint32_t)(64 * t + 4 * g) * (uint32_t)row_bytes;
       const uint32_t voff = (uint32_t)((lane & 3) * row_bytes + 16 * ((lane >> 2) ^ i));
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   ::"s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+      lds_dma16(m0v, voff, rsrc, soff);
     }
   };
 
@@ -124,8 +123,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
       const uint32_t m0v = lds_q + i * 1024;
       const uint32_t soff = (uint32_t)(row0 + 4 * i) * (uint32_t)q_row_bytes;
       const uint32_t voff = (uint32_t)((lane >> 4) * q_row_bytes + 16 * ((lane & 15) ^ (r & 15)));
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   ::"s"(m0v), "v"(voff), "s"(rsrc_q), "s"(soff) : "memory", "m0");
+      lds_dma16(m0v, voff, rsrc_q, soff);
     }
   };
   // B-operand read of step st: chunk 2 st + hi of row l32, i.e. q_op0 + 32 (st ^ q_opx)

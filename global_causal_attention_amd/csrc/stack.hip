@@ -133,10 +133,8 @@ void gemm_kernel(GemmParams p) {
     for (int i = 0; i < kGDmaPerSlab; ++i) {
       const uint32_t soff = s0 + i * kGRowsPerDma * rowb;
       const uint32_t voff = (i & 1) ? voff1 : voff0;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   ::"s"(base + i * 1024), "v"(voff), "s"(ra), "s"(soff) : "memory", "m0");
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   ::"s"(base + kGTileA + i * 1024), "v"(voff), "s"(rb), "s"(soff) : "memory", "m0");
+      lds_dma16(base + i * 1024, voff, ra, soff);
+      lds_dma16(base + kGTileA + i * 1024, voff, rb, soff);
     }
   };
 

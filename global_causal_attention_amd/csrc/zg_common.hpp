@@ -50,6 +50,25 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// One LDS-direct load (buffer_load_dwordx4 ... lds): lane l's 16 bytes at buffer offset
+// voff + soff go to LDS byte address lds + 16 l, so one instruction fills 1 KB of consecutive LDS.
+// Issued in inline asm so that the compiler's wait tracking does not make later LDS reads wait
+// for it (callers wait with explicit vmcnt counts). m0, which carries the LDS address, is saved
+// and restored inside the statement, and one wait state separates its write from the load.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc,
+                                          uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
 // cos/sin of 2*pi*(pos * rev). The product is reduced modulo one revolution in fp64, so the angle
 // keeps full precision at positions up to 2^18 and beyond; v_sin_f32 / v_cos_f32 take their input
 // in revolutions (max abs error ~1.2e-7 on [-0.5, 0.5]).
