@@ -32,14 +32,61 @@ constexpr int kRow = 256;                   // LDS bytes per K or V row (unpadde
 constexpr int kTileBytes = kNk * kRow;      // 16384
 constexpr int kLdsK0 = 0;                   // two K buffers, then two V buffers
 constexpr int kLdsV0 = 2 * kTileBytes;
-constexpr int kLdsBytes = 4 * kTileBytes;
-constexpr int kQWaveBytes = 32 * kRow;      // per-wave q staging: 32 chunk-swizzled rows
-static_assert(kWaves * kQWaveBytes <= kLdsBytes, "q staging aliases the K/V buffers");
+constexpr int kQStage0 = 4 * kTileBytes;    // then per-wave q staging: 32 chunk-swizzled rows
+constexpr int kQWaveBytes = 32 * kRow;
+constexpr int kLdsBytes = kQStage0 + kWaves * kQWaveBytes;  // 128 KB
 
 // 16-byte chunk c of a staged row r lives at chunk c ^ swz(r). Sixteen consecutive rows read at
 // one logical chunk (the QK^T operand) and the four aligned rows x four adjacent chunks of a
 // transposing read (the PV operand) both land on distinct banks.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// RMSNorm + partial RoPE of one head row split over a lane pair (half 0: dims 0..63, half 1:
+// 64..127) for 21 rotary pairs (rot_dim 42, all in half 0), in registers: the two lanes compute
+// 11 and 10 of the angles, half 0 takes its partner's through one DPP exchange and rotates.
+// Same arithmetic as norm_rope_row.
+__device__ __forceinline__ void norm_rope_row_r42(float* x, int half, const float* __restrict__ w,
+                                                  float eps, int64_t pos, const RopeTable& rt) {
+  constexpr int H = 21;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
+  ss += shfl_xor_f(ss, 1);
+  const float inv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
+  if (w) {
+    const f32x4* w4 = reinterpret_cast<const f32x4*>(w + 64 * half);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      f32x4 ww = w4[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[4 * i + j] *= inv * ww[j];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] *= inv;
+  }
+  float cs[H], sn[H];
+#pragma unroll
+  for (int j = 0; j < 11; ++j) {
+    const double rev = half ? rt.rev[j + 11 < H ? j + 11 : H - 1] : rt.rev[j];
+    float c_, s_;
+    rope_cs(pos, rev, c_, s_);
+    cs[j] = c_;
+    sn[j] = s_;
+    if (j + 11 < H) {
+      cs[j + 11] = dpp_swap_pair(c_);
+      sn[j + 11] = dpp_swap_pair(s_);
+    }
+  }
+  if (half == 0) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float a = x[i], b = x[i + H];
+      x[i] = a * cs[i] - b * sn[i];
+      x[i + H] = b * cs[i] + a * sn[i];
+    }
+  }
+}
 
 
 }  // namespace
@@ -256,40 +303,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int qbase = r0 + 32 * qb;
   const float c = p.scale_log2;
 
-  // ---- q prologue: q_hat * scale * log2(e) rounded to bf16, staged through this wave's
-  // chunk-swizzled rows (aliasing the K/V buffers), read back as MFMA B operands
-  bf16x8 qf[8];
-  {
-    unsigned char* qs = smem + wave * kQWaveBytes;
-    const int r = lane >> 1;
-    const int half = lane & 1;
-    const int t = qbase + r;
-    float x[64];
-    if (t < T) {
-      const u32x4* s4 = reinterpret_cast<const u32x4*>(
-          p.q + ((int64_t)b * T + t) * p.sq + (int64_t)head * kHeadDim + 64 * half);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) unpack8(s4[i], x + 8 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = 0.f;
-    }
-    // the [dim][row] RoPE scratch (32 rows x 64 floats) overlays this wave's staging rows; every
-    // access to it precedes the bf16 row writes below in this wave's program order
-    norm_rope_row(x, half, p.q_norm_w, p.eps, p.pos0 + t, p.rope, reinterpret_cast<float*>(qs), r,
-                  32);
-#pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] *= c;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(qs + r * kRow + 16 * ((8 * half + i) ^ swz(r))) = pack8(x + 8 * i);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8*>(qs + l32 * kRow + 16 * ((2 * s + hi) ^ swz(l32)));
-    __syncthreads();
-  }
-
   // ---- key tile range of the workgroup (key rows; query row t is key row qoff + t)
   const int q_last = qoff + min(r0 + MQ, T) - 1;
   int k_begin = 0;
@@ -328,6 +341,52 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     }
   };
   auto vm_wait = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // the first two K tiles go out before the q prologue
+  if (!v_loader) {
+    dma_tile(0, false);
+    if (n_tiles > 1) dma_tile(1, false);
+  }
+
+  // ---- q prologue: q_hat * scale * log2(e) rounded to bf16, staged through this wave's own
+  // chunk-swizzled rows and read back as MFMA B operands. It runs while the first two K tiles
+  // are in flight.
+  bf16x8 qf[8];
+  {
+    unsigned char* qs = smem + kQStage0 + wave * kQWaveBytes;
+    const int r = lane >> 1;
+    const int half = lane & 1;
+    const int t = qbase + r;
+    float x[64];
+    if (t < T) {
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(
+          p.q + ((int64_t)b * T + t) * p.sq + (int64_t)head * kHeadDim + 64 * half);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) unpack8(s4[i], x + 8 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x[i] = 0.f;
+    }
+    if (p.rope.half == 21) {
+      norm_rope_row_r42(x, half, p.q_norm_w, p.eps, p.pos0 + t, p.rope);
+    } else {
+      // the [dim][row] RoPE scratch (32 rows x 64 floats) overlays this wave's staging rows;
+      // every access to it precedes the bf16 row writes below in this wave's program order
+      norm_rope_row(x, half, p.q_norm_w, p.eps, p.pos0 + t, p.rope, reinterpret_cast<float*>(qs),
+                    r, 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] *= c;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(qs + r * kRow + 16 * ((8 * half + i) ^ swz(r))) = pack8(x + 8 * i);
+    // the wave reads back only its own rows, and its LDS operations complete in order
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8*>(qs + l32 * kRow + 16 * ((2 * s + hi) ^ swz(l32)));
+  }
+
 
   // ---- MFMA operand addresses: per-lane byte offsets, everything else is an immediate
   int k_off[8];     // QK^T operand of step st: key row l32 (+32 per key block), dims 16 st + 8 hi
@@ -514,10 +573,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
 
   // ---- preamble: K_0 and K_1 in LDS, S_0 computed
-  if (!v_loader) {
-    dma_tile(0, false);
-    if (n_tiles > 1) dma_tile(1, false);
-  }
   vm_wait();
   __syncthreads();
   f32x16 sA[2], sB[2];

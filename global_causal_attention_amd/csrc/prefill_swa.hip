@@ -49,11 +49,6 @@ constexpr int kSwaQArea = 32 * 256;         // per wave: 32 q rows
 constexpr int kSwaLds = kSwaRing + kWaves * kSwaQArea;
 static_assert(kSwaLds <= 160 * 1024, "LDS budget");
 
-__device__ __forceinline__ float dpp_swap_pair(float v) {  // value of lane ^ 1
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF,
-                                                             0xF, false));
-}
-
 }  // namespace
 
 template <bool GATED>

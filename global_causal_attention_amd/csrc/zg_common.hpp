@@ -50,6 +50,12 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Value of lane ^ 1 (DPP quad permutation [1, 0, 3, 2]; VALU only).
+__device__ __forceinline__ float dpp_swap_pair(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF,
+                                                             0xF, false));
+}
+
 // One LDS-direct load (buffer_load_dwordx4 ... lds): lane l's 16 bytes at buffer offset
 // voff + soff go to LDS byte address lds + 16 l, so one instruction fills 1 KB of consecutive LDS.
 // Issued in inline asm so that the compiler's wait tracking does not make later LDS reads wait
