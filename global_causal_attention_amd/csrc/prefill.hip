@@ -621,33 +621,45 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         o[db] = mfma32(rd_v(par, st, db), __builtin_bit_cast(bf16x8, pl[st]), o[db]);
   }
 
-  // ---- epilogue: normalise, gate, round, store (one query per lane, 4 dims per store)
-  if (my_row < T) {
+  // ---- epilogue: normalise, gate, round, store. The MFMA output gives lane (query, hi) dims
+  // 4 hi .. 4 hi + 3 of every 8-dim chunk; one v_permlane32_swap per dword hands each lane whole
+  // chunks (chunk 2m + hi of the pair 2m, 2m + 1), so every store moves 16 bytes per lane.
+  {
+    const bool store = my_row < T;
     const float l_tot = l_run + shfl_xor_f(l_run, 32);
     const float inv = 1.0f / l_tot;
-    if (p.lse && hi == 0)  // scores are in log2 units relative to m_ref
+    if (p.lse && hi == 0 && store)  // scores are in log2 units relative to m_ref
       p.lse[((int64_t)b * T + my_row) * p.Hq + head] = (m_ref + __log2f(l_tot)) * 0.6931471805599453f;
-    const int64_t tok = (int64_t)b * T + my_row;
+    const int64_t tok = (int64_t)b * T + min(my_row, T - 1);
     uint16_t* dst = p.out + tok * p.so + (int64_t)head * kHeadDim;
     const uint16_t* gsrc = GATED ? p.gate + tok * p.sg + (int64_t)head * kHeadDim : nullptr;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int m = 0; m < 8; ++m) {
+      uint32_t w[4];  // output-layout words of chunks 2m (w[0..1]) and 2m + 1 (w[2..3])
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = 32 * db + 8 * rq + 4 * hi;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int cidx = 2 * m + hh, db = cidx >> 2, rq = cidx & 3;
         float y[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) y[j] = o[db][4 * rq + j] * inv;
         if (GATED) {
-          const u32x2 g = *reinterpret_cast<const u32x2*>(gsrc + d0);
+          const u32x2 g = *reinterpret_cast<const u32x2*>(gsrc + 32 * db + 8 * rq + 4 * hi);
           const float gv[4] = {bf16lo(g[0]), bf16hi(g[0]), bf16lo(g[1]), bf16hi(g[1])};
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             y[j] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[j] * 1.4426950408889634f));
         }
-        u32x2 w = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
-        *reinterpret_cast<u32x2*>(dst + d0) = w;
+        w[2 * hh] = pack_bf16(y[0], y[1]);
+        w[2 * hh + 1] = pack_bf16(y[2], y[3]);
       }
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(w[d], w[d + 2], false, false);
+        w[d] = sw[0];
+        w[d + 2] = sw[1];
+      }
+      if (store) *reinterpret_cast<u32x4*>(dst + 8 * (2 * m + hi)) = u32x4{w[0], w[1], w[2], w[3]};
+    }
   }
 }
 
