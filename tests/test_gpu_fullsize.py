@@ -6,7 +6,8 @@ same tensors copied to the host):
     block): sampled query rows of every sequence, all 32 heads, in the launch configuration the
     benchmark times (runs of 32 steps of 64 queries for the local layer);
   * B=64 decode step, 128-slot rings and linear caches with context lengths uniform on
-    [8192, 65536], base 1e7: every sequence of both;
+    [8192, 65536], base 1e7: every sequence of both, and every sequence of the same step over the
+    linear caches converted to E4M3;
   * B=1, T=262144 gated local and full causal layers, base 1e7: sampled rows (256 seeded uniform
     rows plus the edges for the local layer; a global row at this length costs the fp64 oracle
     about 4.3 GFLOP, so the global layer takes 40);
@@ -107,6 +108,33 @@ def test_b64_decode_rings_and_linear_caches():
         rel = np.abs(got_k - ref_k) / np.maximum(np.abs(ref_k), 1e-6)
         assert rel.max() <= 2.0 ** -7, f"linear K row {L - 1} of sequence {b}: rel {rel.max():.2e}"
         assert torch.equal(vc[b, L - 1].cpu(), x["v_new"][b].cpu()), "linear V write"
+
+
+def test_b64_decode_e4m3_linear_caches():
+    """The bench's E4M3 decode step: the B=64 linear caches of the decode workload (same seed and
+    draw) converted to E4M3 with zg_kv_to_fp8 (scale 1), then one ungated step through
+    zg_attn_decode_fp8; every sequence against oracle.decode_fp8_cache over the same E4M3 values."""
+    Bd, lo, hi = 64, 8192, 65536
+    print(f"[case] E4M3 decode B={Bd} L~U[{lo},{hi}]", flush=True)
+    x = si.decode_step(si.generator(1002, device=DEV), B=Bd, len_lo=lo, len_hi=hi, device=DEV)
+    seq_h = x["seqlens"].cpu().numpy()
+    kc8, vc8 = zg.zg_kv_to_fp8(x["lin_k"]), zg.zg_kv_to_fp8(x["lin_v"])
+    del x["lin_k"], x["lin_v"], x["ring_k"], x["ring_v"]
+    kc0 = {b: _host(kc8[b, :int(seq_h[b]) - 1]) for b in range(Bd)}  # rows before the new token
+    vc0 = {b: _host(vc8[b, :int(seq_h[b]) - 1]) for b in range(Bd)}
+    cfg = zg.AttnConfig(window=0, gated=False, rope_base=1e7)
+    out = zg.zg_attn_decode_fp8(cfg, x["q_new"], x["k_new"], x["v_new"], None, kc8, vc8,
+                                x["seqlens"], max_seqlen=hi)
+    torch.cuda.synchronize()
+    for b in range(Bd):
+        L = int(seq_h[b])
+        pad = np.zeros((1,) + kc0[b].shape[1:])
+        r, _, rv = oracle.decode_fp8_cache(
+            _host(x["q_new"][b:b + 1]), _host(x["k_new"][b:b + 1]), _host(x["v_new"][b:b + 1]),
+            None, np.concatenate([kc0[b], pad])[None], np.concatenate([vc0[b], pad])[None],
+            seq_h[b:b + 1], k_scale=1.0, v_scale=1.0, window=0, gated=False, rope_base=1e7)
+        assert_parity(out[b:b + 1], r, f"E4M3 decode linear sequence {b} (L={L})")
+        assert np.array_equal(_host(vc8[b, L - 1]), rv[0, L - 1]), f"E4M3 V row of sequence {b}"
 
 
 @pytest.mark.parametrize("W", [128, 0])
