@@ -23,14 +23,14 @@ Parity status per function is listed in each module's header.
 from .attention import (rms_norm, rope_inv_freq, partial_rope, qk_prologue, key_set,
                         prefill, prefill_rows, attention_probs_row, decode)
 from .kv import kv_bytes, kv_entries, is_global_layer, global_layers
-from .stack import stack_layer, stack, layer_is_global
+from .stack import stack_layer, stack_layer_rows, stack, layer_is_global
 from .fp8 import e4m3_values, round_e4m3, decode_fp8_cache
 from .backward import layer_backward, layer_backward_rows, row_lse
 
 __all__ = [
     "rms_norm", "rope_inv_freq", "partial_rope", "qk_prologue", "key_set", "prefill",
     "prefill_rows", "attention_probs_row", "decode", "kv_bytes", "kv_entries",
-    "is_global_layer", "global_layers", "stack_layer", "stack", "layer_is_global",
+    "is_global_layer", "global_layers", "stack_layer", "stack_layer_rows", "stack", "layer_is_global",
     "e4m3_values", "round_e4m3", "decode_fp8_cache", "layer_backward", "layer_backward_rows",
     "row_lse",
 ]

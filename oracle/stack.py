@@ -11,13 +11,14 @@ Readings: Pre-LN residual x <- x + o_proj(attn(RMSNorm(x))); input-norm weight
 
 Parity pins (tests/test_stack_oracle.py): W_o = 0 leaves x unchanged; T = 1 closed form (one key, so
 the attention output is v * sigmoid(g)); for T <= window a local layer with zero gate weights adds
-exactly half of what the same layer run as a global layer adds; the layer schedule.
+exactly half of what the same layer run as a global layer adds; the layer schedule; the row-restricted
+form (stack_layer_rows) equals the whole layer on every row.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import prefill
+from .attention import _attend_row, _sigmoid, key_set, prefill, qk_prologue
 from .kv import is_global_layer
 
 
@@ -47,6 +48,36 @@ def stack_layer(x, w, *, is_global, n_q_heads=32, n_kv_heads=8, head_dim=128, wi
         a = prefill(q, k, v, g, window=window, gated=True, rot_dim=rot_dim, rope_base=rope_base,
                     eps=eps, pos0=pos0)
     return x + a.reshape(B, T, n_q_heads * head_dim) @ w["wo"].T
+
+
+def stack_layer_rows(x, w, rows, *, is_global, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                     window=128, rot_dim=42, rope_base=1e7, eps=1e-6, pos0=0):
+    """Rows `rows` of stack_layer's output for one sequence, x: [T, hidden] float64. The same steps
+    as stack_layer, with the projections taken only where those rows need them: q (and the gate)
+    of the rows themselves, k and v of the union of their key sets. Returns [len(rows), hidden]."""
+    rows = [int(r) for r in rows]
+    W = 0 if is_global else window
+    keys = sorted(set().union(*(range(*key_set(t, W)) for t in rows)))
+    at = {j: i for i, j in enumerate(keys)}
+    hk = _rms_rows(x[keys], eps)
+    kk = (hk @ w["wk"].T).reshape(len(keys), n_kv_heads, head_dim)
+    vv = (hk @ w["wv"].T).reshape(len(keys), n_kv_heads, head_dim)
+    khat = qk_prologue(kk, pos0 + np.asarray(keys), None, rot_dim=rot_dim, rope_base=rope_base,
+                       eps=eps)
+    hq = _rms_rows(x[rows], eps)
+    q = (hq @ w["wq"].T).reshape(len(rows), n_q_heads, head_dim)
+    g = None if is_global else (hq @ w["wg"].T).reshape(len(rows), n_q_heads, head_dim)
+    scale = 1.0 / np.sqrt(head_dim)
+    out = np.empty((len(rows), x.shape[1]), dtype=np.float64)
+    for i, t in enumerate(rows):
+        lo, hi = key_set(t, W)
+        sel = [at[j] for j in range(lo, hi)]
+        qhat = qk_prologue(q[i], pos0 + t, None, rot_dim=rot_dim, rope_base=rope_base, eps=eps)
+        o = _attend_row(qhat, khat[sel], vv[sel], scale)
+        if not is_global:
+            o = o * _sigmoid(g[i])
+        out[i] = x[t] + o.reshape(-1) @ w["wo"].T
+    return out
 
 
 def stack(x0, layer_weights, *, global_every=6, **kw):

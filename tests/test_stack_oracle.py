@@ -62,3 +62,19 @@ def test_stack_applies_schedule():
         z = oracle.stack_layer(z, w, is_global=(l % 3 == 0), **SMALL)
     np.testing.assert_array_equal(y, z)
     assert [l for l in range(1, 33) if oracle.layer_is_global(l)] == [6, 12, 18, 24, 30]
+
+
+def test_rows_form_equals_whole_layer():
+    """stack_layer_rows (projections only where the requested rows need them) equals stack_layer on
+    every row, for both layer types, a window shorter than the sequence, a position offset and an
+    unsorted subset of rows."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((2, 11, H))
+    for is_global in (False, True):
+        w = _weights(rng, is_global)
+        full = oracle.stack_layer(x, w, is_global=is_global, pos0=5, **SMALL)
+        for b in range(2):
+            got = oracle.stack_layer_rows(x[b], w, range(11), is_global=is_global, pos0=5, **SMALL)
+            np.testing.assert_allclose(got, full[b], rtol=0, atol=1e-12)
+        got = oracle.stack_layer_rows(x[1], w, [10, 0, 6], is_global=is_global, pos0=5, **SMALL)
+        np.testing.assert_allclose(got, full[1][[10, 0, 6]], rtol=0, atol=1e-12)
