@@ -93,6 +93,64 @@ def _token_stride(t, name, row):
     raise ValueError(f"{name} must be 4-D [B, T, H, D]")
 
 
+def _shape(t, name, shape):
+    """Raise ValueError unless tensor t has exactly `shape` (checked before any launch: the
+    library addresses caches and rows from cfg and the sizes it is given, not from the tensors)."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+
+
+def _norm_weights(q_norm_w, k_norm_w, head_dim):
+    import torch
+    for w, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _shape(w, n, (head_dim,))
+            _need(w, n, torch.float32)
+            if not w.is_contiguous():
+                raise ValueError(f"{n} must be contiguous")
+
+
+def _layer_shapes(cfg, q, k, v, gate):
+    """[B, T, Hq, D] q (and gate), [B, T, Hkv, D] k and v, against cfg; returns (B, T)."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be 4-D [B, T, Hq, D], got shape {tuple(q.shape)}")
+    B, T = q.shape[:2]
+    _shape(q, "q", (B, T, cfg.n_q_heads, cfg.head_dim))
+    _shape(k, "k", (B, T, cfg.n_kv_heads, cfg.head_dim))
+    _shape(v, "v", (B, T, cfg.n_kv_heads, cfg.head_dim))
+    if cfg.gated:
+        if gate is None:
+            raise ValueError("gate is required when cfg.gated")
+        _shape(gate, "gate", (B, T, cfg.n_q_heads, cfg.head_dim))
+    return B, T
+
+
+def _decode_shapes(cfg, q_new, k_new, v_new, gate, k_cache, v_cache, seqlens, max_seqlen):
+    """One new token per sequence: q_new/gate [B, Hq, D], k_new/v_new [B, Hkv, D]; ring caches
+    [B, W, Hkv, D] (the library writes slot pos % W), linear caches [B, rows, Hkv, D] with
+    rows >= max_seqlen; seqlens [B]."""
+    if q_new.dim() != 3:
+        raise ValueError(f"q_new must be 3-D [B, Hq, D], got shape {tuple(q_new.shape)}")
+    B = q_new.shape[0]
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    _shape(q_new, "q_new", (B, Hq, D))
+    _shape(k_new, "k_new", (B, Hkv, D))
+    _shape(v_new, "v_new", (B, Hkv, D))
+    if cfg.gated:
+        if gate is None:
+            raise ValueError("gate is required when cfg.gated")
+        _shape(gate, "gate", (B, Hq, D))
+    rows = cfg.window if cfg.window > 0 else k_cache.shape[1]
+    _shape(k_cache, "k_cache", (B, rows, Hkv, D))
+    _shape(v_cache, "v_cache", (B, rows, Hkv, D))
+    if cfg.window == 0 and rows < max_seqlen:
+        raise ValueError(f"linear caches hold {rows} rows < max_seqlen={max_seqlen}")
+    if seqlens.dim() != 1 or seqlens.numel() != B:
+        raise ValueError(f"seqlens must hold one length per sequence ({B}), got shape "
+                         f"{tuple(seqlens.shape)}")
+    return B
+
+
 def zg_attn_prefill_workspace_bytes(cfg: AttnConfig, B: int, T: int) -> int:
     c = cfg.c()
     return load_library().zg_attn_prefill_workspace_bytes(ctypes.byref(c), B, T)
@@ -104,23 +162,21 @@ def zg_attn_prefill(cfg: AttnConfig, q, k, v, gate=None, *, q_norm_w=None, k_nor
     [B, T, Hkv, 128] bf16 (token-strided views allowed). Returns out [B, T, Hq, 128] bf16."""
     import torch
     bf = torch.bfloat16
+    B, T = _layer_shapes(cfg, q, k, v, gate)
+    Hq, D = cfg.n_q_heads, cfg.head_dim
+    _shape(out, "out", (B, T, Hq, D))
+    _norm_weights(q_norm_w, k_norm_w, D)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, bf)
     if cfg.gated:
         _need(gate, "gate", bf)
-    B, T, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, T, Hq, D), dtype=bf, device=q.device)
     _need(out, "out", bf)
-    for w, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
-        if w is not None:
-            _need(w, n, torch.float32)
     strides = ZgTokenStrides(_token_stride(q, "q", Hq * D), _token_stride(k, "k", 0),
                              _token_stride(v, "v", 0),
                              _token_stride(gate, "gate", 0) if cfg.gated else Hq * D,
                              _token_stride(out, "out", 0))
-    if k.shape[:2] != (B, T) or v.shape[:2] != (B, T) or out.shape != (B, T, Hq, D):
-        raise ValueError("q/k/v/out shapes disagree")
     need = zg_attn_prefill_workspace_bytes(cfg, B, T)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -144,8 +200,10 @@ def zg_attn_forward_train(cfg: AttnConfig, q, k, v, gate=None, *, out=None, lse=
     [B, T, Hq] fp32 natural-log log-sum-exp of each query row's scaled scores."""
     import torch
     bf = torch.bfloat16
-    B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
+    B, T = _layer_shapes(cfg, q, k, v, gate)
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    _shape(out, "out", (B, T, Hq, D))
+    _shape(lse, "lse", (B, T, Hq))
     for t, n, shp in ((q, "q", (B, T, Hq, D)), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D))):
         _need(t, n, bf)
         _packed(t, n, shp)
@@ -182,8 +240,11 @@ def zg_attn_backward(cfg: AttnConfig, q, k, v, gate, out, dout, lse, *, workspac
     output gradient dout. Returns (dq, dk, dv, dgate); dgate is None when not gated."""
     import torch
     bf = torch.bfloat16
-    B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
+    B, T = _layer_shapes(cfg, q, k, v, gate)
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    _shape(out, "out", (B, T, Hq, D))
+    _shape(dout, "dout", (B, T, Hq, D))
+    _shape(lse, "lse", (B, T, Hq))
     for t, n, shp in ((q, "q", (B, T, Hq, D)), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D)),
                       (out, "out", (B, T, Hq, D)), (dout, "dout", (B, T, Hq, D))):
         _need(t, n, bf)
@@ -221,6 +282,15 @@ def zg_attn_prefill_cached(cfg: AttnConfig, q, k, v, gate, k_cache, v_cache, *, 
     the new tokens. Returns out [B, T, Hq, 128] bf16."""
     import torch
     bf = torch.bfloat16
+    B, T = _layer_shapes(cfg, q, k, v, gate)
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    _shape(out, "out", (B, T, Hq, D))
+    rows = cfg.window if cfg.window > 0 else k_cache.shape[1]
+    _shape(k_cache, "k_cache", (B, rows, Hkv, D))
+    _shape(v_cache, "v_cache", (B, rows, Hkv, D))
+    if cfg.window == 0 and rows < pos0 + T:
+        raise ValueError(f"linear caches hold {rows} rows < pos0 + T = {pos0 + T}")
+    _norm_weights(q_norm_w, k_norm_w, D)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, bf)
     if cfg.gated:
@@ -229,21 +299,13 @@ def zg_attn_prefill_cached(cfg: AttnConfig, q, k, v, gate, k_cache, v_cache, *, 
         _need(t, n, bf)
         if not t.is_contiguous():
             raise ValueError(f"{n} must be contiguous")
-    B, T, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, T, Hq, D), dtype=bf, device=q.device)
     _need(out, "out", bf)
-    for w, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
-        if w is not None:
-            _need(w, n, torch.float32)
     strides = ZgTokenStrides(_token_stride(q, "q", Hq * D), _token_stride(k, "k", 0),
                              _token_stride(v, "v", 0),
                              _token_stride(gate, "gate", 0) if cfg.gated else Hq * D,
                              _token_stride(out, "out", 0))
-    if k.shape[:2] != (B, T) or v.shape[:2] != (B, T) or out.shape != (B, T, Hq, D):
-        raise ValueError("q/k/v/out shapes disagree")
-    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B:
-        raise ValueError("k_cache/v_cache shapes disagree")
     need = zg_attn_prefill_cached_workspace_bytes(cfg, B, T)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -268,6 +330,8 @@ def zg_attn_decode(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_cache,
     out [B, Hq, 128] bf16."""
     import torch
     bf = torch.bfloat16
+    B = _decode_shapes(cfg, q_new, k_new, v_new, gate, k_cache, v_cache, seqlens, max_seqlen)
+    _shape(out, "out", q_new.shape)
     for t, n in ((q_new, "q_new"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
                  (v_cache, "v_cache")):
         _need(t, n, bf)
@@ -276,9 +340,14 @@ def zg_attn_decode(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_cache,
     _need(seqlens, "seqlens", torch.int32)
     if cfg.gated:
         _need(gate, "gate", bf)
-    B = q_new.shape[0]
+        if not gate.is_contiguous():
+            raise ValueError("gate must be contiguous")
+    _norm_weights(q_norm_w, k_norm_w, cfg.head_dim)
     if out is None:
         out = torch.empty_like(q_new)
+    _need(out, "out", bf)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
     need = zg_attn_decode_workspace_bytes(cfg, B, max_seqlen)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_new.device)
@@ -299,6 +368,8 @@ def zg_attn_decode_fp8(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_ca
     shape; see include/zg_attn.h). Updates the caches in place, returns out [B, Hq, 128] bf16."""
     import torch
     bf = torch.bfloat16
+    B = _decode_shapes(cfg, q_new, k_new, v_new, gate, k_cache, v_cache, seqlens, max_seqlen)
+    _shape(out, "out", q_new.shape)
     for t, n in ((q_new, "q_new"), (k_new, "k_new"), (v_new, "v_new")):
         _need(t, n, bf)
         if not t.is_contiguous():
@@ -309,9 +380,14 @@ def zg_attn_decode_fp8(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_ca
     _need(seqlens, "seqlens", torch.int32)
     if cfg.gated:
         _need(gate, "gate", bf)
-    B = q_new.shape[0]
+        if not gate.is_contiguous():
+            raise ValueError("gate must be contiguous")
+    _norm_weights(q_norm_w, k_norm_w, cfg.head_dim)
     if out is None:
         out = torch.empty_like(q_new)
+    _need(out, "out", bf)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
     need = zg_attn_decode_workspace_bytes(cfg, B, max_seqlen)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_new.device)
@@ -363,7 +439,13 @@ def zg_hbm_read_probe(src, sink=None, n_blocks=2048, stream=None):
 
 def zg_rmsnorm(x, eps=1e-6, w=None, out=None, stream=None):
     import torch
+    _shape(w, "w", (x.shape[-1],))
+    _shape(out, "out", x.shape)
     _need(x, "x", torch.float32)
+    if not x.is_contiguous() or (w is not None and not w.is_contiguous()):
+        raise ValueError("x and w must be contiguous")
+    if w is not None:
+        _need(w, "w", torch.float32)
     rows = x.numel() // x.shape[-1]
     if out is None:
         out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
@@ -375,10 +457,20 @@ def zg_rmsnorm(x, eps=1e-6, w=None, out=None, stream=None):
 def zg_gemm_bf16(x, w, residual=None, y=None, want_y=True, stream=None):
     """Y = X W^T (fp32 accumulate); residual (fp32) += Y if given; y = bf16(Y) if want_y."""
     import torch
-    _need(x, "x", torch.bfloat16)
-    _need(w, "w", torch.bfloat16)
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError(f"x [M, K] and w [N, K] must be 2-D, got {tuple(x.shape)} and {tuple(w.shape)}")
     M, K = x.shape
     N = w.shape[0]
+    _shape(w, "w", (N, K))
+    _shape(residual, "residual", (M, N))
+    _shape(y, "y", (M, N))
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16)
+    for t, n in ((x, "x"), (w, "w"), (residual, "residual"), (y, "y")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if residual is not None:
+        _need(residual, "residual", torch.float32)
     if want_y and y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _check(load_library().zg_gemm_bf16(M, N, K, _ptr(x), _ptr(w), _ptr(residual),
@@ -395,8 +487,20 @@ def zg_attn_layer(cfg: AttnConfig, x, w_qkvg, w_o, *, q_norm_w=None, k_norm_w=No
                   workspace=None, stream=None):
     """x (fp32 [B, T, hidden]) <- x + o_proj(attn(RMSNorm(x))), in place."""
     import torch
+    if x.dim() != 3:
+        raise ValueError(f"x must be 3-D [B, T, hidden], got shape {tuple(x.shape)}")
+    B, T, hidden = x.shape
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    _shape(x, "x", (B, T, Hq * D))
+    _shape(w_qkvg, "w_qkvg", ((Hq + 2 * Hkv + (Hq if cfg.gated else 0)) * D, hidden))
+    _shape(w_o, "w_o", (hidden, Hq * D))
     _need(x, "x", torch.float32)
-    B, T, _ = x.shape
+    _need(w_qkvg, "w_qkvg", torch.bfloat16)
+    _need(w_o, "w_o", torch.bfloat16)
+    for t, n in ((x, "x"), (w_qkvg, "w_qkvg"), (w_o, "w_o")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    _norm_weights(q_norm_w, k_norm_w, D)
     need = zg_attn_layer_workspace_bytes(cfg, B, T)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)

@@ -166,7 +166,7 @@ zg_status zg_attn_backward(const zg_attn_cfg* cfg, int32_t B, int32_t T, const v
  * applies the gate if cfg->gated. The result equals prefill row pos over the same keys.
  *   workspace >= zg_attn_decode_workspace_bytes(cfg, B, max_seqlen) (split-KV partials).
  * Errors as for prefill; max_seqlen < 1 or cache_stride < max_seqlen (linear) -> ZG_ERR_SHAPE;
- * more than 2^20 keys to attend over (linear max_seqlen > 1048576) -> ZG_ERR_UNSUPPORTED.
+ * more than 2^21 keys to attend over (linear max_seqlen > 2097152) -> ZG_ERR_UNSUPPORTED.
  * seqlens values are device data and are not validated by the host; the kernels skip a sequence
  * whose seqlens[b] is < 1, or > cache_stride for a linear cache (no cache write, its out rows
  * unspecified), so no access leaves the caches; values above max_seqlen are otherwise a caller

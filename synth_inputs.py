@@ -84,3 +84,36 @@ def stack_layer_weights(gen, hidden=4096, Hq=32, Hkv=8, D=128, is_global=False, 
 def stack_input(gen, B, T, hidden=4096, device="cpu") -> torch.Tensor:
     """Residual-stream input x0 ~ N(0,1), kept in float32 (drawn as bf16 values)."""
     return randn_bf16(gen, (B, T, hidden), device=device).float()
+
+
+def ramped_logits_layer(gen, T, Hq=32, Hkv=8, D=128, window=0, noise=0.05, period=96,
+                        device="cpu"):
+    """Inputs whose attention scores sweep a wide range smoothly along the key axis (for the
+    running-reference rescale path of the kernels; used with a q norm weight of a few units).
+
+    Two fixed directions u and w, nonzero only on dims >= 42 (the unrotated ones) and of unit RMS
+    over D, with w orthogonal to u. q rows are u + noise; key j is cos(th_j) u + sin(th_j) w + noise
+    with th_j falling from pi to 0 over the sequence (window 0) or over every `period` keys (a
+    sawtooth, window > 0); v is a smooth function of the position, sin(2 pi j / 200 + d / 7 + kv
+    head); gate logits are N(0, 1). Draw order: u, w, q noise, k noise, gate."""
+    u = torch.zeros(D)
+    u[42:] = torch.randn(D - 42, generator=gen)
+    w = torch.zeros(D)
+    w[42:] = torch.randn(D - 42, generator=gen)
+    u = u.double()
+    w = w.double()
+    w = w - (w @ u) / (u @ u) * u
+    u = u / torch.sqrt(torch.mean(u * u))
+    w = w / torch.sqrt(torch.mean(w * w))
+    j = torch.arange(T, dtype=torch.float64)
+    frac = j / max(T - 1, 1) if window == 0 else (j % period) / (period - 1)
+    th = torch.pi * (1.0 - frac)
+    q = u + noise * torch.randn((T, Hq, D), generator=gen).double()
+    k = (torch.cos(th)[:, None, None] * u + torch.sin(th)[:, None, None] * w
+         + noise * torch.randn((T, Hkv, D), generator=gen).double())
+    d = torch.arange(D, dtype=torch.float64)
+    h = torch.arange(Hkv, dtype=torch.float64)
+    v = torch.sin(2 * torch.pi * j[:, None, None] / 200.0 + d / 7.0 + h[:, None])
+    g = torch.randn((T, Hq, D), generator=gen).double()
+    to = lambda a: a.float().to(torch.bfloat16)[None].to(device)
+    return {"q": to(q), "k": to(k), "v": to(v), "gate": to(g)}

@@ -155,3 +155,25 @@ def test_read_probe_rejects_bad_arguments():
     assert lib.zg_hbm_read_probe(16, 1000, 16, 4, None) == zg.ZG_ERR_SHAPE
     assert lib.zg_hbm_read_probe(16, 1024, 16, 0, None) == zg.ZG_ERR_SHAPE
     assert lib.zg_hbm_read_probe(8, 1024, 16, 4, None) == zg.ZG_ERR_SHAPE
+
+
+def test_decode_key_limit_matches_header():
+    """The header allows at most 2^21 = 2,097,152 keys per sequence (linear max_seqlen); one more
+    is UNSUPPORTED. At the limit the call gets past that check and stops at the (too small)
+    workspace, before any launch."""
+    lib = zg.load_library()
+    limit = 1 << 21
+    assert "2^21" in open(HEADER).read()
+    for fp8 in (False, True):
+        cfg = zg.AttnConfig(window=0, gated=False)
+        c = cfg.c()
+        need = zg.zg_attn_decode_workspace_bytes(cfg, 1, limit)
+
+        def call(max_len):
+            args = (ctypes.byref(c), 1, max_len, max_len, 16, 16, 16, None, None, None, 16, 16)
+            tail = (16, 16, 256, need - 16, None)
+            if fp8:
+                return lib.zg_attn_decode_fp8(*args, ctypes.c_float(1.0), ctypes.c_float(1.0), *tail)
+            return lib.zg_attn_decode(*args, *tail)
+        assert call(limit + 1) == zg.ZG_ERR_UNSUPPORTED, zg.zg_last_error()
+        assert call(limit) == zg.ZG_ERR_WORKSPACE, zg.zg_last_error()

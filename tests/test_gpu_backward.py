@@ -10,7 +10,8 @@ matrix-core inputs and accumulates in fp32, so each gradient carries a relative 
 size of each gradient: relative RMS error <= 1e-2 and max-abs error <= 3e-2 * max |ref|
 (about 15 ulp of bf16 at the largest element); measured: relative RMS <= 4.8e-3, max <= 8.7e-3.
 With one token dq and dk are exactly 0 while the GPU's D = sum(dy * y) uses the bf16-rounded y,
-so there they are held to the absolute bar 2e-2. The row log-sum-exp is compared absolutely:
+so there they are held to the absolute bar 2e-2. The forward's bf16 output is held to the bf16
+output bar (max-abs 2e-2, mean-abs 2e-3), as prefill's is. The row log-sum-exp is compared absolutely:
 <= 2e-2, the bf16 rounding of q_hat and k_hat moving a score of size |s| by about |s| 2^-8.
 """
 import numpy as np
@@ -20,7 +21,7 @@ import torch
 import global_causal_attention_amd as zg
 import oracle
 import synth_inputs as si
-from helpers import f64
+from helpers import assert_parity, f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -75,8 +76,9 @@ def test_backward_matches_oracle(W, gated, B, T, Hq, Hkv):
     ref_lse = oracle.row_lse(qh, kh, window=W)
     rdq, rdk, rdv, rdg = oracle.layer_backward(qh, kh, vh, gh, dyh, window=W, gated=gated)
 
+    # the forward output is a bf16 output like prefill's: the standard bar
+    assert_parity(out, ref_out, f"forward_train out W={W} T={T}")
     res = {}
-    res["out"] = _check(out, ref_out, "out")
     lse_err = float(np.abs(f64(lse) - ref_lse).max())
     print(f"[parity] lse: max_abs={lse_err:.3e}", flush=True)
     res["dq"] = _check(dq, rdq, "dq")

@@ -208,17 +208,18 @@ def test_chunked_b4_ctx16384_sampled_rows(W):
 
 def test_stack_t65536_teacher_forced_layers():
     """The 32-layer stack's inputs as the benchmark draws them (seed 1004: x0, then each layer's
-    weights in order) at T=65536, hidden 4096. Layer 1 (gated local) and layer 6 (global) run on the
-    GPU from the GPU's own input to that layer (layers 2-5 run in between), and sampled output rows
-    are compared, as the layer's increment over its input, with oracle.stack_layer_rows applied to
-    that same input (teacher forcing). Global rows are sampled below 2048, so the oracle projects at
-    most 2048 key rows."""
+    weights in order) at T=65536, hidden 4096. All 32 layers run on the GPU in order; at layers 1
+    and 32 (gated local) and 6 and 30 (global) the layer's sampled output rows are compared, as the
+    layer's increment over its input, with oracle.stack_layer_rows applied to that same GPU input
+    (teacher forcing). Global rows are sampled over the whole length (the oracle projects every key
+    row below the last sampled one, about 1.1e12 fp64 FLOP per global layer), so the heaviest
+    causal query tiles are among the compared rows."""
     Ts, hidden = 65536, 4096
-    print(f"[case] stack layers 1 and 6, T={Ts}", flush=True)
+    print(f"[case] stack layers 1, 6, 30 and 32, T={Ts}", flush=True)
     gen = si.generator(1004, device=DEV)
     x = si.stack_input(gen, 1, Ts, hidden, device=DEV)
     weights = [si.stack_layer_weights(gen, hidden, 32, 8, 128, is_global=(l % 6 == 0), device=DEV)
-               for l in range(1, 7)]
+               for l in range(1, 33)]
     cfgs = {False: zg.AttnConfig(window=128, gated=True, rope_base=1e7),
             True: zg.AttnConfig(window=0, gated=False, rope_base=1e7)}
     ws = torch.empty(max(zg.zg_attn_layer_workspace_bytes(c, 1, Ts) for c in cfgs.values()),
@@ -230,21 +231,20 @@ def test_stack_t65536_teacher_forced_layers():
         zg.zg_attn_layer(cfgs[g], x, torch.cat(parts, 0).contiguous(), w["wo"], workspace=ws)
 
     rng = np.random.default_rng(41)
-    for l in range(1, 7):
-        if l not in (1, 6):
+    for l in range(1, 33):
+        if l not in (1, 6, 30, 32):
             run(l)
             continue
         g = l % 6 == 0
         x_in = f64(x[0])
         run(l)
         torch.cuda.synchronize()
-        if g:
-            rows = sorted({0, 1, 2, 63, 64, 127, 128, 129, 1023, 1024, 2047} |
-                          set(rng.integers(0, 2048, 13).tolist()))
-        else:
-            rows = sorted({0, 1, 127, 128, 129, 4095, 32768, Ts - 2, Ts - 1} |
-                          set(rng.integers(0, Ts, 39).tolist()))
+        edges = {0, 1, 2, 63, 64, 127, 128, 129, 1023, 1024, 2047, 4095, 32767, 32768, Ts - 65,
+                 Ts - 64, Ts - 2, Ts - 1}
+        rows = sorted(edges | set(rng.integers(0, Ts, 14 if g else 40).tolist()))
         w_h = {k: f64(v) for k, v in weights[l - 1].items()}
         ref = oracle.stack_layer_rows(x_in, w_h, rows, is_global=g, rope_base=1e7)
         got = f64(x[0, rows])
-        assert_parity(got - x_in[rows], ref - x_in[rows], f"stack layer {l} at T={Ts}, {len(rows)} rows")
+        assert_parity(got - x_in[rows], ref - x_in[rows],
+                      f"stack layer {l} at T={Ts}, {len(rows)} rows")
+        del x_in, w_h, ref

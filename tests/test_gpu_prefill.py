@@ -95,6 +95,11 @@ def test_prefill_token_strided_views(W):
 
 
 def test_prefill_norm_weights_scale_and_rot_dims():
+    # rot 42 with non-unit weights runs the banded kernel's folded path (local layer) and the
+    # general kernel (causal layer) at normal logit scale
+    for W, rot, scale in ((128, 42, 0.0), (0, 42, 0.0), (100, 42, 0.07)):
+        out, ref = _run(1, 333, 32, 8, W, W > 0, 1e4, 13 + W, rot=rot, norm_w=True, scale=scale)
+        assert_parity(out, ref, f"W={W} rot={rot} scale={scale} with norm weights")
     for rot, scale in ((0, 0.0), (64, 0.05), (16, 0.0)):
         out, ref = _run(1, 200, 32, 8, 128, True, 1e4, 11, rot=rot, norm_w=True, scale=scale)
         assert_parity(out, ref, f"rot={rot} scale={scale} with norm weights")
@@ -163,3 +168,29 @@ def test_prefill_peaky_logits(W):
     kw = (torch.rand(128, generator=gen) * 1.5 + 0.25).double().numpy()
     model = _rounded_operand_reference(x, W, gated, qw, kw, folded=W > 0)
     assert_parity(out, model, f"peaky logits W={W} vs bf16-operand model", max_abs=4e-2)
+
+
+@pytest.mark.parametrize("W", [0, 128])
+def test_prefill_rescale_path_standard_bar(W):
+    """The running softmax reference raised many times, held to the bf16 output bar (2e-2 max,
+    2e-3 mean) against the fp64 oracle. synth_inputs.ramped_logits_layer sweeps each query's scores
+    over about +-90 log2 units (q norm weight 4): in the causal layer every row's first key tile
+    has its maximum outside [-32, 32], so the reference is set from it, and about half the rows
+    later see scores more than 64 above it; in the banded layer the sawtooth makes the newest
+    keys of a window exceed the first block's maximum by more than 60 on about a third of the
+    rows. The score differences that decide the weights come from the smooth ramp and v is
+    smooth along the keys, so the bf16 rounding of the matrix-core operands moves the output
+    little (a CPU model of exactly those rounding points stays within 1.0e-2 / 6.8e-4), while a
+    wrong rescale of the running sum or output moves it by O(1)."""
+    T = 600
+    print(f"[case] rescale path W={W} T={T}", flush=True)
+    x = si.ramped_logits_layer(si.generator(4100 + W), T, window=W)
+    qw = torch.full((128,), 4.0)
+    cfg = zg.AttnConfig(window=W, gated=W > 0, rope_base=1e4)
+    dev = {k: v.to(DEV) for k, v in x.items()}
+    out = zg.zg_attn_prefill(cfg, dev["q"], dev["k"], dev["v"], dev["gate"] if W else None,
+                             q_norm_w=qw.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.prefill(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["gate"]), window=W,
+                         gated=W > 0, rope_base=1e4, q_norm_w=qw.double().numpy())
+    assert_parity(out, ref, f"rescale path W={W}")

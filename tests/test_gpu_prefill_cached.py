@@ -102,3 +102,49 @@ def test_first_chunk_equals_plain_prefill():
         if W:  # both run the banded streaming kernel on the same folded keys
             assert torch.equal(a, ref), "pos0=0 cached vs plain: banded kernel results differ"
 
+
+
+@pytest.mark.parametrize("T1,T2", [(127, 150), (64, 200)])
+def test_ring_chunks_with_norm_weights(T1, T2):
+    """Ring chunks on the banded streaming kernel (context 127 = 63 mod 64, or 64 = 0 mod 64) with
+    non-unit q and k norm weights: the context keys are gathered from the ring with the q weights
+    of dims >= 42 folded in, against the whole-sequence oracle with the same weights; the ring
+    then holds the unfolded normalised keys, and decode continues with the same weights."""
+    W, B, base = 128, 2, 1e6
+    L = T1 + T2
+    print(f"[case] cached ring with norm weights T1={T1} T2={T2}", flush=True)
+    gen = si.generator(2200 + T1)
+    x = si.prefill_layer(gen, B, L + 1, HQ, HKV, D, gated=True)
+    qw = torch.rand(D, generator=gen) * 1.5 + 0.25
+    kw = torch.rand(D, generator=gen) * 1.5 + 0.25
+    q, k, v, g = (x[n].to(DEV) for n in ("q", "k", "v", "gate"))
+    qwd, kwd = qw.to(DEV), kw.to(DEV)
+    cfg = zg.AttnConfig(window=W, gated=True, rope_base=base)
+    kc = torch.zeros(B, W, HKV, D, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    outs = []
+    for lo, hi in ((0, T1), (T1, L)):
+        c = lambda t: t[:, lo:hi].contiguous()
+        outs.append(zg.zg_attn_prefill_cached(cfg, c(q), c(k), c(v), c(g), kc, vc, pos0=lo,
+                                              q_norm_w=qwd, k_norm_w=kwd))
+    torch.cuda.synchronize()
+    qh, kh, vh, gh = (f64(x[n]) for n in ("q", "k", "v", "gate"))
+    qwh, kwh = qw.double().numpy(), kw.double().numpy()
+    ref = oracle.prefill(qh[:, :L], kh[:, :L], vh[:, :L], gh[:, :L], window=W, gated=True,
+                         rope_base=base, q_norm_w=qwh, k_norm_w=kwh)
+    assert_parity(torch.cat(outs, 1), ref, f"ring chunks with norm weights T1={T1} T2={T2}")
+    kc_h = kc.float().cpu().numpy()
+    for b in range(B):
+        khat = oracle.qk_prologue(kh[b, :L], np.arange(L), kwh, rot_dim=42, rope_base=base,
+                                  eps=1e-6)
+        for p in range(L - W, L):
+            rel = np.abs(kc_h[b, p % W] - khat[p]) / np.maximum(np.abs(khat[p]), 1e-6)
+            assert rel.max() <= 2.0 ** -7, f"k cache, sequence {b}, position {p}: rel {rel.max():.2e}"
+    seq = torch.full((B,), L + 1, dtype=torch.int32, device=DEV)
+    out_d = zg.zg_attn_decode(cfg, q[:, L].contiguous(), k[:, L].contiguous(), v[:, L].contiguous(),
+                              g[:, L].contiguous(), kc, vc, seq, max_seqlen=L + 1, q_norm_w=qwd,
+                              k_norm_w=kwd)
+    torch.cuda.synchronize()
+    ref_d = oracle.prefill_rows(qh, kh, vh, gh, [L], window=W, gated=True, rope_base=base,
+                                q_norm_w=qwh, k_norm_w=kwh)
+    assert_parity(out_d, ref_d[:, 0], f"decode after ring chunks with norm weights L={L}")

@@ -12,7 +12,8 @@ import torch
 import global_causal_attention_amd as zg
 import oracle
 import synth_inputs as si
-from helpers import assert_parity, f64
+import stack_model
+from helpers import assert_parity, err_stats, f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -86,29 +87,52 @@ def test_attn_layer_teacher_forced(is_global, B, T):
 
 
 def test_stack_32_layers_end_to_end():
-    """All 32 layers (globals at 6, 12, 18, 24, 30) at T=96, GPU and oracle each carrying their
-    own residual stream; weights are drawn layer by layer so only one layer is resident.
+    """All 32 layers (globals at 6, 12, 18, 24, 30) at T=96 through zg_attn_layer, weights drawn
+    layer by layer so only one layer is resident.
 
-    Bar: the output is the fp32 residual after 32 layers (RMS ~5 here), not a bf16 tensor, so the
-    bf16 output bar does not apply to it directly. Each layer contributes with a relative error of
-    ~5e-3 (its bf16 operands: the teacher-forced test above holds it to the bf16 bar), and the
-    errors compound through the later layers' norms; the check is relative RMS error <= 1e-2 and
-    max-abs error <= 2e-2 of the output's largest magnitude. Any wiring mistake (layer schedule,
-    residual, gate) moves the output by O(1) relative to itself."""
+    Three checks, with bars fixed before the run from a CPU simulation (an fp32 implementation with
+    the GPU's bf16 rounding points, against tests/stack_model.py):
+      1. Every layer on the GPU's own input (teacher forcing): its increment against the rounding
+         model's increment, at the bf16 output bar (2e-2 max, 2e-3 mean). Against the fp64 oracle
+         the increment may differ by what the rounding points themselves cause: the bar there is
+         the model's own distance from fp64 (max x 1.5, mean x 1.25), since the deep global layers'
+         increments (RMS ~1.4) carry a mean rounding error of ~2.0e-3 by themselves.
+      2. Free running, layers 1-4: the GPU's residual stream against the rounding model run on its
+         own, at the bf16 output bar. (Beyond ~4 layers no implementation tracks the model
+         element by element: the bf16 rounding of h = RMSNorm(x) turns fp32-level differences in x
+         into whole-ulp differences in h; the simulation drifts from the model by 0.11 max / 0.016
+         mean at layer 32.)
+      3. Free running, layer 32: the GPU's distance from the fp64 oracle is no more than the
+         rounding model's own (max x 1.5, mean x 1.25). A wiring mistake (schedule, residual,
+         gate) moves the output by O(1) relative to itself."""
     B, T = 1, 96
     print(f"[case] 32-layer stack B={B} T={T}", flush=True)
     gen = si.generator(1004, device=DEV)
     x = si.stack_input(gen, B, T, H, device=DEV)
-    xr = f64(x)
+    xr = f64(x)[0]          # fp64 oracle, free running
+    xm = xr.copy()          # rounding model, free running
     for l in range(1, 33):
         is_global = oracle.layer_is_global(l)
         w, wqkvg = _layer_weights(gen, is_global)
+        wh = _oracle_weights(w)
         cfg = zg.AttnConfig(window=0 if is_global else 128, gated=not is_global, rope_base=1e7)
+        x_in = f64(x)[0]
         zg.zg_attn_layer(cfg, x, wqkvg, w["wo"])
-        xr = oracle.stack_layer(xr, _oracle_weights(w), is_global=is_global, rope_base=1e7)
-        del w, wqkvg
-    torch.cuda.synchronize()
-    scale = float(np.abs(xr).max())
-    mx, mean, rel = assert_parity(x, xr, "32-layer stack output", max_abs=2e-2 * scale,
-                                  mean_abs=np.inf)
-    assert rel <= 1e-2, f"32-layer stack: relative RMS error {rel:.3e} > 1e-2"
+        torch.cuda.synchronize()
+        d_gpu = f64(x)[0] - x_in
+        d_mod = stack_model.layer(x_in, wh, is_global=is_global) - x_in
+        d_ref = oracle.stack_layer(x_in[None], wh, is_global=is_global, rope_base=1e7)[0] - x_in
+        assert_parity(d_gpu, d_mod, f"layer {l} increment vs rounding model (teacher-forced)")
+        m_max, m_mean, _ = err_stats(d_mod, d_ref)
+        assert_parity(d_gpu, d_ref, f"layer {l} increment vs fp64 (teacher-forced)",
+                      max_abs=1.5 * m_max, mean_abs=1.25 * m_mean)
+        xr = oracle.stack_layer(xr[None], wh, is_global=is_global, rope_base=1e7)[0]
+        xm = stack_model.layer(xm, wh, is_global=is_global)
+        if l <= 4:
+            assert_parity(f64(x)[0], xm, f"free-running layers 1..{l} vs rounding model")
+        del w, wqkvg, wh
+    m_max, m_mean, m_rel = err_stats(xm, xr)
+    print(f"[parity] rounding model vs fp64 after 32 layers: max_abs={m_max:.3e} "
+          f"mean_abs={m_mean:.3e} rel_rms={m_rel:.3e}", flush=True)
+    assert_parity(x[0], xr, "32-layer stack output vs fp64", max_abs=1.5 * m_max,
+                  mean_abs=1.25 * m_mean)

@@ -1,5 +1,6 @@
 """Pins of the stack oracle (Pre-LN attention-only layers with projections)."""
 import numpy as np
+import pytest
 
 import oracle
 
@@ -78,3 +79,22 @@ def test_rows_form_equals_whole_layer():
             np.testing.assert_allclose(got, full[b], rtol=0, atol=1e-12)
         got = oracle.stack_layer_rows(x[1], w, [10, 0, 6], is_global=is_global, pos0=5, **SMALL)
         np.testing.assert_allclose(got, full[1][[10, 0, 6]], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("is_global", [False, True])
+def test_rounding_model_without_rounding_is_the_oracle(is_global, monkeypatch):
+    """tests/stack_model.py (the GPU's bf16 rounding points inserted into the oracle's arithmetic)
+    reduces to oracle.stack_layer when its rounding is switched off: the folded score form of the
+    local layer (RMS factor applied to the scores, reference subtracted) is exact in real
+    arithmetic, so a wiring mistake in the model shows here."""
+    import stack_model
+    monkeypatch.setattr(stack_model, "bf16", lambda a: np.asarray(a, dtype=np.float64))
+    rng = np.random.default_rng(5 + is_global)
+    T, hidden = 150, 4096
+    x = rng.standard_normal((T, hidden))
+    w = {n: rng.standard_normal(s) * 0.02 for n, s in
+         (("wq", (4096, hidden)), ("wk", (1024, hidden)), ("wv", (1024, hidden)),
+          ("wg", (4096, hidden)), ("wo", (hidden, 4096)))}
+    got = stack_model.layer(x, w, is_global=is_global, rope_base=1e7)
+    ref = oracle.stack_layer(x[None], w, is_global=is_global, rope_base=1e7)[0]
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10)
