@@ -11,10 +11,13 @@ Rounding points (ZGCM-1 zh-TW translation page, section 2.1 and Fig. 3 for the l
 for Pre-LN):
   * h = bf16(RMSNorm(x)) (the residual x itself is fp32 and is not rounded);
   * the q, k, v and gate projections h W^T, each rounded to bf16;
-  * global layers (full causal, ungated): the matrix cores see bf16(q_hat * c) and bf16(k_hat),
-    c = log2(e) / sqrt(128); scores are in log2 units and the softmax weights are bf16(exp2(s))
-    (with weight-1 norms |s| <= 128 c < 32, so the running reference of the causal kernel stays 0);
-  * local layers (window 128, gated, 4 query heads per KV head, 42 rotary dims): the matrix cores see
+  * global layers (full causal, ungated), and local layers whose window covers the whole sequence
+    (T <= 128: the library runs them as causal, gated): the matrix cores see bf16(q_hat * c) and
+    bf16(k_hat), c = log2(e) / sqrt(128); scores are in log2 units and the softmax weights are
+    bf16(exp2(s)) (with weight-1 norms |s| <= 128 c < 32, so the running reference of the causal
+    kernel stays 0);
+  * local layers with T > 128 (window 128, gated, 4 query heads per KV head, 42 rotary dims,
+    the banded kernel): the matrix cores see
     q with its first 42 dims replaced by bf16(RoPE(q)) and bf16(k_hat * c); the RMS factor r_q of
     the query multiplies the scores; the weights are bf16(exp2(r_q (s - mu))) with mu the bf16
     rounding of the largest score of the first 32-key block the banded kernel visits for that query
@@ -48,8 +51,9 @@ def _first_block(t):
     return (64 * tc - 32, 64 * tc) if tc >= 1 else (0, 32)
 
 
-def attention_global(q, k, v, rope_base, eps=1e-6):
-    """q: [T, 32, 128] (bf16 values), k, v: [T, 8, 128]; full causal, ungated."""
+def attention_causal(q, k, v, rope_base, g=None, eps=1e-6):
+    """q: [T, 32, 128] (bf16 values), k, v: [T, 8, 128]; full causal; gated when g is given (a
+    local layer whose window covers the whole sequence runs this form)."""
     T = q.shape[0]
     pos = np.arange(T)
     qs = bf16(C_LOG2 * oracle.qk_prologue(q, pos, None, rot_dim=42, rope_base=rope_base, eps=eps))
@@ -61,6 +65,8 @@ def attention_global(q, k, v, rope_base, eps=1e-6):
         s = np.where(np.tril(np.ones((T, T), dtype=bool)), s, -np.inf)
         p = bf16(np.exp2(s))
         out[:, h] = (p @ v[:, c]) / p.sum(-1, keepdims=True)
+    if g is not None:
+        out = out / (1.0 + np.exp(-g))
     return bf16(out)
 
 
@@ -86,7 +92,7 @@ def attention_local(q, k, v, g, rope_base, window=128, eps=1e-6):
     return bf16(out)
 
 
-def layer(x, w, *, is_global, rope_base=1e7, eps=1e-6):
+def layer(x, w, *, is_global, rope_base=1e7, window=128, eps=1e-6):
     """One Pre-LN layer on one sequence. x: [T, 4096] float64 residual; w: dict of [out, in]
     float64 weights (bf16 values) 'wq', 'wk', 'wv', 'wo' and, for local layers, 'wg'."""
     T = x.shape[0]
@@ -95,8 +101,11 @@ def layer(x, w, *, is_global, rope_base=1e7, eps=1e-6):
     k = bf16(h @ w["wk"].T).reshape(T, 8, 128)
     v = bf16(h @ w["wv"].T).reshape(T, 8, 128)
     if is_global:
-        a = attention_global(q, k, v, rope_base, eps)
+        a = attention_causal(q, k, v, rope_base, eps=eps)
     else:
         g = bf16(h @ w["wg"].T).reshape(T, 32, 128)
-        a = attention_local(q, k, v, g, rope_base, eps=eps)
+        if T <= window:   # the window covers every key: the causal form, gated
+            a = attention_causal(q, k, v, rope_base, g=g, eps=eps)
+        else:
+            a = attention_local(q, k, v, g, rope_base, window=window, eps=eps)
     return x + a.reshape(T, 4096) @ w["wo"].T

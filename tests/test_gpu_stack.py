@@ -87,25 +87,27 @@ def test_attn_layer_teacher_forced(is_global, B, T):
 
 
 def test_stack_32_layers_end_to_end():
-    """All 32 layers (globals at 6, 12, 18, 24, 30) at T=96 through zg_attn_layer, weights drawn
-    layer by layer so only one layer is resident.
+    """All 32 layers (globals at 6, 12, 18, 24, 30) at T=160 through zg_attn_layer (T > 128, so the
+    local layers run the banded kernel on a ragged last step), weights drawn layer by layer so only
+    one layer is resident.
 
     Three checks, with bars fixed before the run from a CPU simulation (an fp32 implementation with
-    the GPU's bf16 rounding points, against tests/stack_model.py):
+    the GPU's bf16 rounding points, against tests/stack_model.py, at this T):
       1. Every layer on the GPU's own input (teacher forcing): its increment against the rounding
-         model's increment, at the bf16 output bar (2e-2 max, 2e-3 mean). Against the fp64 oracle
-         the increment may differ by what the rounding points themselves cause: the bar there is
-         the model's own distance from fp64 (max x 1.5, mean x 1.25), since the deep global layers'
-         increments (RMS ~1.4) carry a mean rounding error of ~2.0e-3 by themselves.
-      2. Free running, layers 1-4: the GPU's residual stream against the rounding model run on its
-         own, at the bf16 output bar. (Beyond ~4 layers no implementation tracks the model
-         element by element: the bf16 rounding of h = RMSNorm(x) turns fp32-level differences in x
-         into whole-ulp differences in h; the simulation drifts from the model by 0.11 max / 0.016
-         mean at layer 32.)
+         model's increment, at the bf16 output bar (2e-2 max, 2e-3 mean; the simulation differs
+         from the model by 1.0e-3 / 1.4e-5 there). Against the fp64 oracle the increment may
+         differ by what the rounding points themselves cause: the bar there is the model's own
+         distance from fp64 (max x 1.5, mean x 1.25), since the deep global layers' increments
+         (RMS ~1.4) carry a mean rounding error of ~2.0e-3 by themselves.
+      2. Free running, layers 1-2: the GPU's residual stream against the rounding model run on its
+         own, at the bf16 output bar (simulation: 5.7e-3 / 4.2e-4 at layer 2). Beyond a few layers
+         no implementation tracks the model element by element: the bf16 rounding of
+         h = RMSNorm(x) turns fp32-level differences in x into whole-ulp differences in h, and the
+         simulation drifts from the model by 0.11 max / 0.015 mean at layer 32.
       3. Free running, layer 32: the GPU's distance from the fp64 oracle is no more than the
-         rounding model's own (max x 1.5, mean x 1.25). A wiring mistake (schedule, residual,
-         gate) moves the output by O(1) relative to itself."""
-    B, T = 1, 96
+         rounding model's own (max x 1.5, mean x 1.25; the simulation's ratios are 0.99 and 0.98).
+         A wiring mistake (schedule, residual, gate) moves the output by O(1) relative to itself."""
+    B, T = 1, 160
     print(f"[case] 32-layer stack B={B} T={T}", flush=True)
     gen = si.generator(1004, device=DEV)
     x = si.stack_input(gen, B, T, H, device=DEV)
@@ -128,7 +130,7 @@ def test_stack_32_layers_end_to_end():
                       max_abs=1.5 * m_max, mean_abs=1.25 * m_mean)
         xr = oracle.stack_layer(xr[None], wh, is_global=is_global, rope_base=1e7)[0]
         xm = stack_model.layer(xm, wh, is_global=is_global)
-        if l <= 4:
+        if l <= 2:
             assert_parity(f64(x)[0], xm, f"free-running layers 1..{l} vs rounding model")
         del w, wqkvg, wh
     m_max, m_mean, m_rel = err_stats(xm, xr)
