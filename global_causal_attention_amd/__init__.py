@@ -17,7 +17,8 @@ from ._abi import (LIB_PATH, ZgAttnCfg, ZgTokenStrides, load_library, ZG_OK, ZG_
 
 __all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached",
            "zg_attn_forward_train", "zg_attn_backward", "zg_attn_backward_workspace_bytes",
-           "zg_hbm_read_probe", "zg_attn_decode", "zg_attn_decode_fp8", "zg_kv_to_fp8", "zg_kv_bytes",
+           "zg_hbm_read_probe", "zg_attn_decode", "zg_attn_decode_noalloc", "zg_attn_decode_fp8",
+           "zg_kv_to_fp8", "zg_kv_bytes",
            "zg_attn_prefill_workspace_bytes", "zg_attn_decode_workspace_bytes", "zg_rmsnorm",
            "zg_gemm_bf16", "zg_attn_layer", "zg_attn_layer_workspace_bytes", "zg_last_error",
            "load_library", "LIB_PATH", "EXPORTS"]
@@ -358,6 +359,40 @@ def zg_attn_decode(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_cache,
         _ptr(gate if cfg.gated else None), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(k_cache),
         _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def zg_attn_decode_noalloc(cfg: AttnConfig, q_new, k_new, v_new, gate, k_cache, v_cache, seqlens,
+                           *, max_seqlen: int, q_norm_w=None, k_norm_w=None, out=None,
+                           stream=None):
+    """zg_attn_decode with the library's static per-device scratch instead of a workspace (see
+    include/zg_attn.h): the library call allocates nothing (`out` is allocated here when not
+    given). Calls that overlap on one GPU race on the shared scratch."""
+    import torch
+    bf = torch.bfloat16
+    _decode_shapes(cfg, q_new, k_new, v_new, gate, k_cache, v_cache, seqlens, max_seqlen)
+    _shape(out, "out", q_new.shape)
+    for t, n in ((q_new, "q_new"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _need(t, n, bf)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    _need(seqlens, "seqlens", torch.int32)
+    if cfg.gated:
+        _need(gate, "gate", bf)
+        if not gate.is_contiguous():
+            raise ValueError("gate must be contiguous")
+    _norm_weights(q_norm_w, k_norm_w, cfg.head_dim)
+    if out is None:
+        out = torch.empty_like(q_new)
+    _need(out, "out", bf)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    c = cfg.c()
+    _check(load_library().zg_attn_decode_noalloc(
+        ctypes.byref(c), q_new.shape[0], k_cache.shape[1], max_seqlen, _ptr(q_new), _ptr(k_new),
+        _ptr(v_new), _ptr(gate if cfg.gated else None), _ptr(q_norm_w), _ptr(k_norm_w),
+        _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), _stream(stream)))
     return out
 
 

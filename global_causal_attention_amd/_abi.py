@@ -38,6 +38,8 @@ EXPORTS = {
     "zg_attn_decode_workspace_bytes": (_SZ, [_CFG, _I32, _I64]),
     "zg_attn_decode": (ctypes.c_int, [_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _SZ, _P]),
+    "zg_attn_decode_noalloc": (ctypes.c_int, [_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P,
+                                              _P, _P, _P, _P, _P]),
     "zg_attn_decode_fp8": (ctypes.c_int, [_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _F32, _F32, _P, _P, _P, _SZ, _P]),
     "zg_kv_to_fp8": (ctypes.c_int, [_P, _P, _I64, _F32, _P]),

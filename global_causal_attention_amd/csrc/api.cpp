@@ -587,6 +587,37 @@ size_t zg_attn_decode_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int64_t
   return bytes;
 }
 
+// Every decode argument check except the workspace's.
+static zg_status decode_check(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                              int64_t max_seqlen, const void* q_new, const void* k_new,
+                              const void* v_new, const void* gate, const float* q_norm_w,
+                              const float* k_norm_w, const void* k_cache, const void* v_cache,
+                              bool fp8, float k_scale, float v_scale, const int32_t* seqlens,
+                              const void* out) {
+  zg_status st = check_cfg(cfg);
+  if (st != ZG_OK) return st;
+  if (!q_new || !k_new || !v_new || !k_cache || !v_cache || !seqlens || !out)
+    return fail(ZG_ERR_NULL, "q_new, k_new, v_new, caches, seqlens and out must be non-NULL");
+  if (cfg->gated && !gate) return fail(ZG_ERR_NULL, "gate must be non-NULL when gated=1");
+  if (B < 1) return fail(ZG_ERR_SHAPE, "B=%d must be >= 1", B);
+  if (max_seqlen < 1 || max_seqlen >= (int64_t(1) << 31))
+    return fail(ZG_ERR_SHAPE, "max_seqlen=%lld out of range", (long long)max_seqlen);
+  const int64_t keys = cfg->window > 0 ? std::min<int64_t>(cfg->window, max_seqlen) : max_seqlen;
+  if ((keys + kDecodeChunk - 1) / kDecodeChunk > zg::kDecodeMaxChunks)
+    return fail(ZG_ERR_UNSUPPORTED, "max_seqlen=%lld: at most %lld keys per sequence",
+                (long long)max_seqlen, (long long)(kDecodeChunk * zg::kDecodeMaxChunks));
+  if (cfg->window == 0 && cache_stride < max_seqlen)
+    return fail(ZG_ERR_SHAPE, "linear cache: cache_stride=%lld < max_seqlen=%lld",
+                (long long)cache_stride, (long long)max_seqlen);
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(ZG_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
+  if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || (q_norm_w && !aligned16(q_norm_w)) ||
+      (k_norm_w && !aligned16(k_norm_w)))
+    return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+  return ZG_OK;
+}
+
 static zg_status decode_impl(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
                              int64_t max_seqlen, const void* q_new, const void* k_new,
                              const void* v_new, const void* gate, const float* q_norm_w,
@@ -594,27 +625,10 @@ static zg_status decode_impl(const zg_attn_cfg* cfg, int32_t B, int64_t cache_st
                              float k_scale, float v_scale, const int32_t* seqlens, void* out,
                              void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    zg_status st = check_cfg(cfg);
+    zg_status st = decode_check(cfg, B, cache_stride, max_seqlen, q_new, k_new, v_new, gate,
+                                q_norm_w, k_norm_w, k_cache, v_cache, fp8, k_scale, v_scale,
+                                seqlens, out);
     if (st != ZG_OK) return st;
-    if (!q_new || !k_new || !v_new || !k_cache || !v_cache || !seqlens || !out)
-      return fail(ZG_ERR_NULL, "q_new, k_new, v_new, caches, seqlens and out must be non-NULL");
-    if (cfg->gated && !gate) return fail(ZG_ERR_NULL, "gate must be non-NULL when gated=1");
-    if (B < 1) return fail(ZG_ERR_SHAPE, "B=%d must be >= 1", B);
-    if (max_seqlen < 1 || max_seqlen >= (int64_t(1) << 31))
-      return fail(ZG_ERR_SHAPE, "max_seqlen=%lld out of range", (long long)max_seqlen);
-    const int64_t keys = cfg->window > 0 ? std::min<int64_t>(cfg->window, max_seqlen) : max_seqlen;
-    if ((keys + kDecodeChunk - 1) / kDecodeChunk > zg::kDecodeMaxChunks)
-      return fail(ZG_ERR_UNSUPPORTED, "max_seqlen=%lld: at most %lld keys per sequence",
-                  (long long)max_seqlen, (long long)(kDecodeChunk * zg::kDecodeMaxChunks));
-    if (cfg->window == 0 && cache_stride < max_seqlen)
-      return fail(ZG_ERR_SHAPE, "linear cache: cache_stride=%lld < max_seqlen=%lld",
-                  (long long)cache_stride, (long long)max_seqlen);
-    if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
-      return fail(ZG_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
-    if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
-        !aligned16(v_cache) || (q_norm_w && !aligned16(q_norm_w)) ||
-        (k_norm_w && !aligned16(k_norm_w)))
-      return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
     const size_t need = zg_attn_decode_workspace_bytes(cfg, B, max_seqlen);
     if (!workspace || workspace_bytes < need)
       return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
@@ -622,6 +636,7 @@ static zg_status decode_impl(const zg_attn_cfg* cfg, int32_t B, int64_t cache_st
     if (!aligned16(workspace)) return fail(ZG_ERR_SHAPE, "workspace must be 16-byte aligned");
 
     const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+    const int64_t keys = cfg->window > 0 ? std::min<int64_t>(cfg->window, max_seqlen) : max_seqlen;
     zg::DecodeParams p{};
     p.q_new = static_cast<const uint16_t*>(q_new);
     p.k_new = static_cast<const uint16_t*>(k_new);
@@ -677,6 +692,34 @@ zg_status zg_attn_decode_fp8(const zg_attn_cfg* cfg, int32_t B, int64_t cache_st
   return decode_impl(cfg, B, cache_stride, max_seqlen, q_new, k_new, v_new, gate, q_norm_w,
                      k_norm_w, k_cache, v_cache, true, k_scale, v_scale, seqlens, out, workspace,
                      workspace_bytes, stream);
+}
+
+zg_status zg_attn_decode_noalloc(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                                 int64_t max_seqlen, const void* q_new, const void* k_new,
+                                 const void* v_new, const void* gate, const float* q_norm_w,
+                                 const float* k_norm_w, void* k_cache, void* v_cache,
+                                 const int32_t* seqlens, void* out, void* stream) {
+  try {
+    // every argument and the scratch limit are checked before anything touches the device
+    zg_status st = decode_check(cfg, B, cache_stride, max_seqlen, q_new, k_new, v_new, gate,
+                                q_norm_w, k_norm_w, k_cache, v_cache, false, 1.f, 1.f, seqlens,
+                                out);
+    if (st != ZG_OK) return st;
+    const size_t need = zg_attn_decode_workspace_bytes(cfg, B, max_seqlen);
+    if (need > zg::kDecodeScratchBytes)
+      return fail(ZG_ERR_UNSUPPORTED,
+                  "zg_attn_decode_noalloc: %zu bytes of scratch needed, the static scratch holds %zu "
+                  "(B * n_q_heads * (128 + chunks * 132) * 4 bytes, chunks = keys / 1024 rounded up)",
+                  need, zg::kDecodeScratchBytes);
+    void* scratch = nullptr;
+    st = hip_status(zg::decode_scratch_ptr(&scratch), "decode scratch address");
+    if (st != ZG_OK) return st;
+    return decode_impl(cfg, B, cache_stride, max_seqlen, q_new, k_new, v_new, gate, q_norm_w,
+                       k_norm_w, k_cache, v_cache, false, 1.f, 1.f, seqlens, out, scratch,
+                       zg::kDecodeScratchBytes, stream);
+  } catch (...) {
+    return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_decode_noalloc");
+  }
 }
 
 zg_status zg_kv_to_fp8(const void* src_bf16, void* dst_e4m3, int64_t n, float scale, void* stream) {

@@ -14,6 +14,8 @@
 //     A sequence with one chunk writes its output directly; otherwise the chunk writes (max, sum,
 //     unnormalised o) partials.
 //  3. decode_combine: log-sum-exp merge of the partials, gate, bf16 store.
+#include <mutex>
+
 #include "zg_mfma.hpp"
 
 namespace zg {
@@ -949,6 +951,33 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
     y *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
   }
   p.out[((int64_t)b * p.Hq + head) * kHeadDim + d] = (uint16_t)(pack_bf16(y, 0.f) & 0xffffu);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Device-resident scratch for callers that cannot allocate (zg_attn_decode_noalloc): the decode
+// workspace (fp32 q_hat and the split-KV partials) lives in this array, one copy per GPU, for the
+// life of the process. Host code never passes the array's name to a kernel: on the host it is a
+// stand-in symbol, not a device address. The device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept per device.
+static __device__ __attribute__((aligned(256))) unsigned char decode_scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch_ptr(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void* ptr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev]() {
+    void* a = nullptr;
+    err[dev] = hipGetSymbolAddress(&a, HIP_SYMBOL(decode_scratch));
+    ptr[dev] = a;
+  });
+  if (err[dev] != hipSuccess) return err[dev];
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {

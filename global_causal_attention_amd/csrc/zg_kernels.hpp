@@ -178,6 +178,10 @@ hipError_t launch_prefill(const PrefillParams& p, int group, bool gated, hipStre
 // The general tiled kernel only (any window, key rows offset from query rows, unfolded keys).
 hipError_t launch_prefill_general(const PrefillParams& p, int group, bool gated, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+// Size of the per-device static decode scratch, and its device address on the current device
+// (looked up once per device; never the host-side symbol).
+constexpr size_t kDecodeScratchBytes = size_t(96) << 20;
+hipError_t decode_scratch_ptr(void** out);
 hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 

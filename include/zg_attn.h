@@ -19,8 +19,9 @@
  *  - ZG_ERR_HIP: a HIP call or kernel launch reported an error. Faults inside a kernel surface at the
  *    caller's next synchronisation, as with any asynchronous launch.
  *  - NaN/Inf in inputs propagate; the hot path does no value checks.
- *  - No mutable global state: calls from several host threads are safe; calls that share output
- *    buffers or a workspace must be ordered by the caller.
+ *  - No mutable global state except the static scratch of zg_attn_decode_noalloc (see there):
+ *    calls from several host threads are safe; calls that share output buffers or a workspace
+ *    must be ordered by the caller.
  */
 #ifndef ZG_ATTN_H
 #define ZG_ATTN_H
@@ -179,6 +180,24 @@ zg_status zg_attn_decode(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride
                          const float* k_norm_w, void* k_cache, void* v_cache,
                          const int32_t* seqlens, void* out, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* zg_attn_decode without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
+ * workspace lives in a static device array of 96 MiB (100,663,296 bytes) that the library holds on
+ * each GPU it runs on until the process ends; its address is looked up once per device, on the
+ * first call with that device current. The call allocates and frees nothing.
+ *   Arguments, layouts, numerics and errors as zg_attn_decode; in addition, when
+ *   zg_attn_decode_workspace_bytes(cfg, B, max_seqlen) exceeds 96 MiB -> ZG_ERR_UNSUPPORTED
+ *   (e.g. B = 64 with 32 query heads fits up to 94,208 keys per sequence: 92 chunks of 1024).
+ *   Nothing in the scratch needs to start at zero: every value a call reads there it has written
+ *   earlier on its own stream.
+ *   All calls on one GPU share its array: calls that may overlap in time on one GPU (different
+ *   streams, or host threads without ordering) race on it and give undefined results; order them. */
+zg_status zg_attn_decode_noalloc(const zg_attn_cfg* cfg, int32_t B, int64_t cache_stride,
+                                 int64_t max_seqlen, const void* q_new, const void* k_new,
+                                 const void* v_new, const void* gate, const float* q_norm_w,
+                                 const float* k_norm_w, void* k_cache, void* v_cache,
+                                 const int32_t* seqlens, void* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Decode over E4M3 KV caches: the FP8 format of the pages' forward pass (zh-TW translation,

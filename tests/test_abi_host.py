@@ -177,3 +177,25 @@ def test_decode_key_limit_matches_header():
             return lib.zg_attn_decode(*args, *tail)
         assert call(limit + 1) == zg.ZG_ERR_UNSUPPORTED, zg.zg_last_error()
         assert call(limit) == zg.ZG_ERR_WORKSPACE, zg.zg_last_error()
+
+
+def test_decode_noalloc_rejects_before_touching_the_device():
+    """zg_attn_decode_noalloc checks every argument and its 96 MiB scratch limit before it looks
+    up the scratch address or launches anything (these calls run without a GPU)."""
+    lib = zg.load_library()
+    c = zg.AttnConfig(window=0, gated=False).c()
+
+    def call(B=64, stride=200000, max_len=200000, seq=16, q=16):
+        return lib.zg_attn_decode_noalloc(ctypes.byref(c), B, stride, max_len, q, 16, 16, None,
+                                          None, None, 16, 16, seq, 16, None)
+    assert call(q=None) == zg.ZG_ERR_NULL
+    assert call(seq=None) == zg.ZG_ERR_NULL
+    assert call(B=0) == zg.ZG_ERR_SHAPE
+    assert call(stride=10) == zg.ZG_ERR_SHAPE
+    # B = 64 sequences of up to 200,000 keys need ~213 MB of partials: beyond the static scratch
+    assert call() == zg.ZG_ERR_UNSUPPORTED
+    assert "96" in zg.zg_last_error() or "scratch" in zg.zg_last_error()
+    assert zg.zg_attn_decode_workspace_bytes(zg.AttnConfig(window=0, gated=False), 64, 94208) \
+        <= 96 << 20
+    assert zg.zg_attn_decode_workspace_bytes(zg.AttnConfig(window=0, gated=False), 64, 94209) \
+        > 96 << 20
