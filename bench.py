@@ -21,7 +21,9 @@ Also measured in the same run (reported beside the headline):
   * a context sweep at 262,144 tokens per step (T = 4K .. 256K, B = 256K / T): one local and one
     global layer timed per T, and the 32-layer attention time of the all-global, 1:1, 3:1 and
     ZGCM-1's 5:1 schedules (global at every 1st, 2nd, 4th, 6th layer);
-  * the oracle (fp64 NumPy on the host cores) on a bounded sample of the same workload.
+  * the B=1, T=1024 gated local layer (cold MALL);
+  * the oracle (fp64 NumPy on the host cores) on a bounded sample of the same workload, and on
+    samples of the other workloads (per-config rates, scaled-up figures labelled extrapolated).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long]
                        [--no-stack] [--no-chunked] [--no-sweep] [--no-block]
@@ -101,6 +103,7 @@ def main():
 
     if not args.no_decode:
         result["decode"] = bench_decode(torch, zg, si, dev, stream, args.decode_reps)
+        result["t1024_local"] = bench_t1024(torch, zg, si, dev, stream)
     if not args.no_long:
         result["long_context"] = bench_long(torch, zg, si, dev, stream)
     if not args.no_stack:
@@ -119,6 +122,7 @@ def main():
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, si)
+        result["cpu_baseline_configs"] = cpu_baseline_configs(torch, si)
 
     print(json.dumps(result), flush=True)
 
@@ -216,6 +220,39 @@ def bench_block(torch, zg, si, dev, stream, args):
     log(f"[bench] step {ms_step:.3f} ms; swa {swa_ms:.3f} ms; global {glo_ms:.3f} ms")
     del swa, glo, out_swa, out_glo, ws
     return result
+
+
+def bench_t1024(torch, zg, si, dev, stream, reps=20):
+    """The small check workload timed: one gated local layer, B=1, T=1024 (W=128, base 1e4, seed
+    1000). Its 29.4 MB of inputs and outputs fit the MALL, so each rep starts after a 1 GiB fill
+    that evicts them (cold); median of `reps`."""
+    x = si.prefill_layer(si.generator(1000, device="cuda"), 1, 1024, HQ, HKV, D, gated=True,
+                         device="cuda")
+    cfg = zg.AttnConfig(window=W, gated=True, rope_base=1e4)
+    out = torch.empty_like(x["q"])
+    ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, 1, 1024), dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    fn = lambda: zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"], out=out, workspace=ws)
+    for _ in range(3):
+        fn()
+    ts = []
+    for _ in range(reps):
+        flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    ms = ts[len(ts) // 2]
+    nbytes = 1024 * (HQ * D * 2 * 3 + HKV * D * 2 * 2)
+    log(f"[bench] T=1024 local layer: {ms * 1e3:.1f} us")
+    del x, out, ws, flush
+    return {"workload": "B=1, T=1024, Hq=32 Hkv=8 D=128, gated W=128, rot 42, base 1e4, cold MALL",
+            "ms_median": round(ms, 4), "tokens_per_s": round(1024 / (ms * 1e-3), 1),
+            "min_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
 
 
 def bench_decode(torch, zg, si, dev, stream, reps):
@@ -360,7 +397,7 @@ def bench_long(torch, zg, si, dev, stream):
         ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, 1, Tl), dtype=torch.uint8, device=dev)
         fn = lambda: zg.zg_attn_prefill(cfg, x["q"], x["k"], x["v"], x["gate"] if win else None,
                                         out=out, workspace=ws)
-        ms = _time(torch, stream, fn, 5 if win else 2)
+        ms = _time(torch, stream, fn, 5)
         flop = HQ * n_pairs(Tl, win) * 4 * D
         r = {"ms_median": round(ms, 3), "tokens_per_s": round(Tl / (ms * 1e-3), 1),
              "TFLOPs_useful": round(flop / (ms * 1e-3) / 1e12, 2)}
@@ -379,7 +416,8 @@ def bench_long(torch, zg, si, dev, stream):
 def bench_stack(torch, zg, si, dev, stream, n_layers=32, Ts=65536, hidden=4096):
     """The attention-only stack with projections: x <- x + o_proj(attn(RMSNorm(x))) for 32 layers,
     global at layers 6, 12, 18, 24, 30 (ungated, full causal), gated W=128 elsewhere; base 1e7.
-    One untimed pass, then the median of two timed passes; per-layer events give the breakdown."""
+    One untimed pass, then five timed passes (the fastest is reported; the median beside it);
+    per-layer events give the breakdown."""
     log(f"[bench] stack: {n_layers} layers, T={Ts}, hidden {hidden}")
     gen = si.generator(1004, device="cuda")
     x = si.stack_input(gen, 1, Ts, hidden, device="cuda")
@@ -404,7 +442,7 @@ def bench_stack(torch, zg, si, dev, stream, n_layers=32, Ts=65536, hidden=4096):
     one_pass()
     torch.cuda.synchronize()
     runs = []
-    for _ in range(2):
+    for _ in range(5):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
         evs[0].record(stream)
         one_pass(evs)
@@ -413,6 +451,7 @@ def bench_stack(torch, zg, si, dev, stream, n_layers=32, Ts=65536, hidden=4096):
         runs.append((sum(per), per))
     runs.sort(key=lambda r: r[0])
     total, per = runs[0]
+    median_ms = runs[len(runs) // 2][0]
     n_glob = sum(1 for g, _, _ in layers if g)
     t_glob = sum(p for p, (g, _, _) in zip(per, layers) if g)
     t_loc = total - t_glob
@@ -422,7 +461,8 @@ def bench_stack(torch, zg, si, dev, stream, n_layers=32, Ts=65536, hidden=4096):
     del layers, ws, x
     return {"workload": f"B=1, T={Ts}, hidden {hidden}, {n_layers} layers ({n_glob} global), "
                         f"N(0, 0.02) bf16 weights, fp32 residual, base 1e7",
-            "ms": round(total, 2), "tokens_per_s": round(Ts / (total * 1e-3), 1),
+            "ms": round(total, 2), "ms_median_of_5": round(median_ms, 2),
+            "tokens_per_s": round(Ts / (total * 1e-3), 1),
             "useful_flop": proj + att,
             "TFLOPs_useful": round((proj + att) / (total * 1e-3) / 1e12, 1),
             "mfma_frac": round((proj + att) / (total * 1e-3) / MFMA_BF16_PEAK, 4),
@@ -575,6 +615,141 @@ def bench_sweep(torch, zg, si, dev, stream, tokens=262144, n_layers=32):
     return res
 
 
+def _oracle_threads():
+    """BLAS threads for the oracle: every core this process may run on."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(n)
+    except Exception:
+        pass
+    return n
+
+
+def cpu_baseline_configs(torch, si, budget_s=8.0):
+    """The oracle (fp64 NumPy on the host cores) on the other workloads, each on a bounded sample
+    with the shapes of the GPU workload (inputs drawn on the host; the oracle's time does not depend
+    on the values). Rates are in the unit of the GPU figure they sit beside; every figure that is
+    scaled up from a sample says so."""
+    import numpy as np
+    import oracle
+    cores = _oracle_threads()
+    f = lambda t: t.float().numpy().astype(np.float64)
+    res = {}
+
+    # B=1, T=1024 gated local layer (the small check workload), in full
+    x = si.prefill_layer(si.generator(1000), 1, 1024, HQ, HKV, D, gated=True)
+    t0 = time.perf_counter()
+    oracle.prefill(f(x["q"]), f(x["k"]), f(x["v"]), f(x["gate"]), window=W, gated=True,
+                   rope_base=1e4)
+    dt = time.perf_counter() - t0
+    res["t1024_local"] = {"value": round(1024 / dt, 1), "unit": "tokens/s", "cores": cores,
+                          "kind": "oracle", "sample": "the whole layer (B=1, T=1024, W=128, gated)",
+                          "seconds": round(dt, 2)}
+    log(f"[bench] oracle T=1024 local layer: {dt:.2f} s")
+
+    # B=64 decode step: the ring (local) step in full; the linear (global) step on sequences drawn
+    # from the same length distribution until about budget_s seconds, scaled to the 64
+    rng = np.random.default_rng(1002)
+    Bd, lo, hi = 64, 8192, 65536
+    lens = rng.integers(lo, hi + 1, Bd)
+    qn, kn, vn, g = (rng.standard_normal(s_) for s_ in
+                     ((Bd, HQ, D), (Bd, HKV, D), (Bd, HKV, D), (Bd, HQ, D)))
+    kr, vr = rng.standard_normal((Bd, W, HKV, D)), rng.standard_normal((Bd, W, HKV, D))
+    t0 = time.perf_counter()
+    oracle.decode(qn, kn, vn, g, kr, vr, lens, window=W, gated=True, rope_base=1e7)
+    t_ring = time.perf_counter() - t0
+    done, t_lin = 0, 0.0
+    while done < Bd and t_lin < budget_s:
+        L = int(lens[done])
+        kc = rng.standard_normal((1, L, HKV, D))
+        vc = rng.standard_normal((1, L, HKV, D))
+        t0 = time.perf_counter()
+        oracle.decode(qn[done:done + 1], kn[done:done + 1], vn[done:done + 1], None, kc, vc,
+                      lens[done:done + 1], window=0, gated=False, rope_base=1e7)
+        t_lin += time.perf_counter() - t0
+        done += 1
+        del kc, vc
+    t_lin_step = t_lin / float(lens[:done].sum()) * float(lens.sum())
+    res["decode_b64"] = {
+        "ring": {"value": round(Bd / t_ring, 1), "unit": "tokens/s", "cores": cores,
+                 "kind": "oracle", "sample": "the whole B=64 ring step", "seconds": round(t_ring, 3)},
+        "linear": {"value": round(Bd / t_lin_step, 2), "unit": "tokens/s", "cores": cores,
+                   "kind": "oracle",
+                   "sample": f"{done} of the 64 sequences ({int(lens[:done].sum())} keys), step time "
+                             f"scaled by total keys (extrapolated)",
+                   "seconds_sampled": round(t_lin, 2), "step_seconds_extrapolated": round(t_lin_step, 1)}}
+    log(f"[bench] oracle decode: ring step {t_ring:.3f} s, linear step {t_lin_step:.1f} s (extrapolated)")
+
+    # B=1, T=262144 layer pair: local rows at uniform positions; global rows near the middle in
+    # one call (the prologue over the keys is shared by the rows of a call)
+    Tl = 262144
+    q = rng.standard_normal((1, Tl, HQ, D), dtype=np.float32)
+    k = rng.standard_normal((1, Tl, HKV, D), dtype=np.float32)
+    v = rng.standard_normal((1, Tl, HKV, D), dtype=np.float32)
+    rows_l = np.sort(rng.integers(W, Tl, 128))
+    t0 = time.perf_counter()
+    for r_ in rows_l:  # one call per row: a call normalises every key between its first and last row
+        oracle.prefill_rows(q, k, v, q, [r_], window=W, gated=True, rope_base=1e7)
+    t_l = (time.perf_counter() - t0) / len(rows_l)
+    mid = Tl // 2
+    rows_g = [mid - 3, mid - 2, mid - 1, mid]
+    t0 = time.perf_counter()
+    oracle.prefill_rows(q, k, v, None, rows_g, window=0, gated=False, rope_base=1e7)
+    t_call = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.prefill_rows(q, k, v, None, rows_g[-1:], window=0, gated=False, rope_base=1e7)
+    t_one = time.perf_counter() - t0
+    t_row_mid = max((t_call - t_one) / 3.0, 1e-9)       # one more row at the mean position
+    t_shared = max(t_one - t_row_mid, 0.0)               # key prologue of half the sequence
+    t_glob = 2 * t_shared + Tl * t_row_mid               # whole layer, extrapolated
+    del q, k, v
+    res["t262144"] = {
+        "local": {"value": round(1.0 / t_l, 1), "unit": "tokens/s", "cores": cores,
+                  "kind": "oracle", "sample": f"{len(rows_l)} rows at uniform positions, one call each",
+                  "layer_seconds_extrapolated": round(Tl * t_l, 1)},
+        "global": {"value": round(Tl / t_glob, 3), "unit": "tokens/s", "cores": cores,
+                   "kind": "oracle",
+                   "sample": "rows at T/2 (the mean causal row): one row, then four in one call; "
+                             "layer time = key prologue + T x per-row time (extrapolated)",
+                   "layer_seconds_extrapolated": round(t_glob, 1)}}
+    log(f"[bench] oracle T=262144: local {t_l * 1e3:.2f} ms/row, global layer ~{t_glob:.0f} s")
+
+    # one teacher-forced layer of the 32-layer stack (T=65536, hidden 4096): sampled rows; the k/v
+    # projections of the rows' keys are shared by the rows of a call
+    Ts, hidden = 65536, 4096
+    xs = rng.standard_normal((Ts, hidden))
+    wts = {n_: rng.standard_normal(s_) * 0.02 for n_, s_ in
+           (("wq", (HQ * D, hidden)), ("wk", (HKV * D, hidden)), ("wv", (HKV * D, hidden)),
+            ("wg", (HQ * D, hidden)), ("wo", (hidden, HQ * D)))}
+    rows = np.sort(rng.integers(W, Ts, 32))
+    t0 = time.perf_counter()
+    oracle.stack_layer_rows(xs, wts, rows, is_global=False, rope_base=1e7)
+    t_loc = (time.perf_counter() - t0) / len(rows)
+    mid = Ts // 2
+    t0 = time.perf_counter()
+    oracle.stack_layer_rows(xs, wts, [mid], is_global=True, rope_base=1e7)
+    t_g1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.stack_layer_rows(xs, wts, [mid - 3, mid - 2, mid - 1, mid], is_global=True, rope_base=1e7)
+    t_g4 = time.perf_counter() - t0
+    t_grow = max((t_g4 - t_g1) / 3.0, 1e-9)
+    t_gshared = max(t_g1 - t_grow, 0.0)                  # k/v projections of half the keys
+    t_glayer = 2 * t_gshared + Ts * t_grow
+    t_stack = 27 * Ts * t_loc + 5 * t_glayer
+    del xs, wts
+    res["stack_t65536"] = {
+        "value": round(Ts / t_stack, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": f"teacher-forced layers on host-drawn inputs: {len(rows)} local rows; global rows at "
+                  f"T/2 (one, then four in one call); 32-layer time = 27 local layers at the per-row "
+                  f"time + 5 global layers at (shared k/v projection + T x per-row time) "
+                  f"(extrapolated)",
+        "local_ms_per_row": round(t_loc * 1e3, 2), "global_layer_seconds_extrapolated": round(t_glayer, 1),
+        "stack_seconds_extrapolated": round(t_stack, 1)}
+    log(f"[bench] oracle stack: local {t_loc * 1e3:.1f} ms/row, global layer ~{t_glayer:.0f} s")
+    return res
+
+
 def cpu_baseline(torch, si, budget_s=12.0):
     """The fp64 oracle on the host cores, on a bounded sample of the same 5:1 block: query rows of
     sequence 0 (all 32 heads) of a gated local layer and of the global layer, drawn at uniform
@@ -583,11 +758,7 @@ def cpu_baseline(torch, si, budget_s=12.0):
     with the global row time scaled to the mean position of a full sequence."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _oracle_threads()
     gen = si.generator(SEED)
     Ts = 16384
     x = si.prefill_layer(gen, 1, Ts, HQ, HKV, D, gated=True)

@@ -886,6 +886,320 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(DecodeParams p
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Ring decode in one launch, for 4 query heads per KV head and rings of at most 128 slots (the
+// local layers: zh-TW translation page, section 2.3, a fixed 128-token window per sequence). One
+// workgroup per (KV head, sequence); wave w owns slots 32 w .. 32 w + 31.
+//  1. Every wave issues the loads of its K and V slots at once, beside the new token's rows.
+//  2. Wave 0 normalises and rotates the group's 4 q rows, wave 1 the new key row (16 lanes per
+//     row, as the prep kernel does); the new k_hat and v go to the cache slot pos % W, and the
+//     workgroup keeps the same rows (as the cache holds them) in LDS.
+//  3. Scores and output on the matrix cores as in decode_mfma_kernel, the new slot's row taken
+//     from LDS instead of the cache (the same workgroup writes that cache row, so reading it back
+//     would race); exact softmax over the <= 128 slots, sigmoid gate, bf16 store.
+// Results equal the prep + decode_mfma_kernel pair bit for bit (same operand rounding, same
+// reduction order).
+namespace {
+// RMSNorm + RoPE of one 128-dim row held by 16 lanes (lane c: dims 8c .. 8c + 7), rotated pairs
+// exchanged through the row's 68-float LDS stage. Result in x (fp32).
+__device__ __forceinline__ void norm_rope16(float* x, int c, int pos, const float* w, float eps,
+                                            const RopeTable& rt, float* sr) {
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+  ss = row16_sum(ss);
+  const float inv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] *= inv * (w ? w[8 * c + j] : 1.0f);
+  const int hr = rt.half;
+  if (hr > 0) {
+    double rev0 = 0.0, rev1 = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (c == j) {
+        rev0 = rt.rev[j];
+        rev1 = rt.rev[j + 16];
+      }
+    }
+    const bool rotates = 8 * c < 2 * hr;
+    if (rotates) {
+      *reinterpret_cast<f32x4*>(sr + 8 * c) = f32x4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f32x4*>(sr + 8 * c + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS ops complete in order
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int pi = c + 16 * k;
+      if (pi < hr) {
+        float cs, sn;
+        rope_cs(pos, k ? rev1 : rev0, cs, sn);
+        const float a = sr[pi];
+        const float bb = sr[pi + hr];
+        sr[pi] = a * cs - bb * sn;
+        sr[pi + hr] = bb * cs + a * sn;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (rotates) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(sr + 8 * c);
+      const f32x4 hi4 = *reinterpret_cast<const f32x4*>(sr + 8 * c + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = lo[j];
+        x[4 + j] = hi4[j];
+      }
+    }
+  }
+}
+}  // namespace
+
+template <bool FP8>
+__global__ __launch_bounds__(kDecThreads) void decode_ring_kernel(DecodeParams p) {
+  constexpr int G = 4;
+  constexpr int kSlots = 128;
+  __shared__ float s_s[G * kSlots];
+  __shared__ float ml[G][2];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[4 * kMfWaveLds];
+  __shared__ __attribute__((aligned(16))) uint32_t qhs[G][64];   // bf16 q_hat rows
+  __shared__ __attribute__((aligned(16))) uint32_t newk[64];     // new slot's K row (bf16)
+  __shared__ __attribute__((aligned(16))) uint32_t newv[64];     // new slot's V row (bf16)
+  __shared__ __attribute__((aligned(16))) float stage[G + 1][kDpStage];
+
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int pos = p.seqlens[b] - 1;
+  if (pos < 0) return;  // a length below 1 is a caller error: touch nothing
+  const int W = p.window;
+  const int n = min(pos + 1, W);   // valid slots 0 .. n-1 (positions max(0, pos-W+1) .. pos)
+  const int slot = pos % W;        // the new token's slot
+  const int n_blk = (n + 31) >> 5;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  constexpr int EB = FP8 ? 1 : 2;
+  const int64_t row_bytes = (int64_t)p.Hkv * kHeadDim * EB;
+  const unsigned char* kc = reinterpret_cast<const unsigned char*>(p.k_cache) +
+                            (int64_t)b * W * row_bytes + (int64_t)kvh * kHeadDim * EB;
+  const unsigned char* vc = reinterpret_cast<const unsigned char*>(p.v_cache) +
+                            (int64_t)b * W * row_bytes + (int64_t)kvh * kHeadDim * EB;
+  const bf16x8 zero8 = bf16x8{};
+  unsigned char* wtile = vt + wave * kMfWaveLds;
+
+  constexpr int NV = FP8 ? 4 : 8;
+  auto load_rows = [&](u32x4 (&vraw)[NV], const unsigned char* base, int blk) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = 64 * i + lane;
+      const int row = FP8 ? (idx >> 3) : (idx >> 4), pc = FP8 ? (idx & 7) : (idx & 15);
+      const int key = 32 * blk + row;
+      vraw[i] = key < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)key * row_bytes) + pc)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage_rows = [&](const u32x4 (&vraw)[NV], unsigned char* tile) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = 64 * i + lane;
+      if (FP8) {
+        const int row = idx >> 3, pc = idx & 7;
+        const u32x4 w = vraw[i];
+        const u32x4 lo = {e4m3x2_bf16<false>(w[0]), e4m3x2_bf16<true>(w[0]),
+                          e4m3x2_bf16<false>(w[1]), e4m3x2_bf16<true>(w[1])};
+        const u32x4 up = {e4m3x2_bf16<false>(w[2]), e4m3x2_bf16<true>(w[2]),
+                          e4m3x2_bf16<false>(w[3]), e4m3x2_bf16<true>(w[3])};
+        *reinterpret_cast<u32x4*>(tile + row * kMfRow + 16 * ((2 * pc) ^ mf_swz(row))) = lo;
+        *reinterpret_cast<u32x4*>(tile + row * kMfRow + 16 * ((2 * pc + 1) ^ mf_swz(row))) = up;
+      } else {
+        const int row = idx >> 4, ch = idx & 15;
+        *reinterpret_cast<u32x4*>(tile + row * kMfRow + 16 * (ch ^ mf_swz(row))) = vraw[i];
+      }
+    }
+  };
+  // the new slot's row (bf16 words in LDS) over its row of this wave's tile, if the slot is here
+  auto put_new_row = [&](const uint32_t* src, unsigned char* tile) {
+    const int r = slot - 32 * wave;
+    if (r >= 0 && r < 32 && lane < 16) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(src + 4 * lane);
+      *reinterpret_cast<u32x4*>(tile + r * kMfRow + 16 * (lane ^ mf_swz(r))) = w;
+    }
+  };
+
+  // ---- 1. cache loads of this wave's slots (the new slot's stale row is replaced below)
+  u32x4 kraw[NV], vraw[NV];
+  if (wave < n_blk) {
+    load_rows(kraw, kc, wave);
+    load_rows(vraw, vc, wave);
+  }
+
+  // ---- 2. the new token: q rows (wave 0), k row (wave 1, lanes 0..15), v row (wave 1, 16..31)
+  {
+    const int grp = lane >> 4, c = lane & 15;
+    if (wave == 0 || (wave == 1 && grp == 0)) {
+      const bool is_q = wave == 0;
+      const int h = is_q ? kvh * G + grp : kvh;
+      const uint16_t* src = is_q ? p.q_new + ((int64_t)b * p.Hq + h) * kHeadDim
+                                 : p.k_new + ((int64_t)b * p.Hkv + h) * kHeadDim;
+      float x[8];
+      unpack8(*reinterpret_cast<const u32x4*>(src + 8 * c), x);
+      norm_rope16(x, c, pos, is_q ? p.q_norm_w : p.k_norm_w, p.eps, p.rope,
+                  &stage[is_q ? grp : G][0]);
+      if (is_q) {
+        *reinterpret_cast<u32x4*>(&qhs[grp][4 * c]) = pack8(x);
+      } else {
+        const int64_t off = ((int64_t)b * W + slot) * p.Hkv * kHeadDim + (int64_t)kvh * kHeadDim + 8 * c;
+        if (!FP8) {
+          const u32x4 w = pack8(x);
+          *reinterpret_cast<u32x4*>(p.k_cache + off) = w;
+          *reinterpret_cast<u32x4*>(&newk[4 * c]) = w;
+        } else {
+          const float ki = p.k_inv;
+          const u32x2 w = {pack4_e4m3(x[0] * ki, x[1] * ki, x[2] * ki, x[3] * ki),
+                           pack4_e4m3(x[4] * ki, x[5] * ki, x[6] * ki, x[7] * ki)};
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.k_cache) + off) = w;
+          *reinterpret_cast<u32x4*>(&newk[4 * c]) =
+              u32x4{e4m3x2_bf16<false>(w[0]), e4m3x2_bf16<true>(w[0]), e4m3x2_bf16<false>(w[1]),
+                    e4m3x2_bf16<true>(w[1])};
+        }
+      }
+    } else if (wave == 1 && grp == 1) {
+      const u32x4 vw = *reinterpret_cast<const u32x4*>(p.v_new + ((int64_t)b * p.Hkv + kvh) * kHeadDim + 8 * c);
+      const int64_t off = ((int64_t)b * W + slot) * p.Hkv * kHeadDim + (int64_t)kvh * kHeadDim + 8 * c;
+      if (!FP8) {
+        *reinterpret_cast<u32x4*>(p.v_cache + off) = vw;
+        *reinterpret_cast<u32x4*>(&newv[4 * c]) = vw;
+      } else {
+        float vf[8];
+        unpack8(vw, vf);
+        const float vi = p.v_inv;
+        const u32x2 w = {pack4_e4m3(vf[0] * vi, vf[1] * vi, vf[2] * vi, vf[3] * vi),
+                         pack4_e4m3(vf[4] * vi, vf[5] * vi, vf[6] * vi, vf[7] * vi)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.v_cache) + off) = w;
+        *reinterpret_cast<u32x4*>(&newv[4 * c]) =
+            u32x4{e4m3x2_bf16<false>(w[0]), e4m3x2_bf16<true>(w[0]), e4m3x2_bf16<false>(w[1]),
+                  e4m3x2_bf16<true>(w[1])};
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3a. scores of this wave's 32 slots
+  if (wave < n_blk) {
+    bf16x8 qa[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      qa[st] = l32 < G ? *reinterpret_cast<const bf16x8*>(&qhs[l32][32 * hi + 4 * st]) : zero8;
+    stage_rows(kraw, wtile);
+    put_new_row(newk, wtile);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are in LDS
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      sacc = mfma32(qa[st], *reinterpret_cast<const bf16x8*>(wtile + l32 * kMfRow + 16 * ((8 * hi + st) ^ mf_swz(l32))), sacc);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the tile is rewritten
+    const int key = 32 * wave + l32;
+    if (hi == 0 && key < n) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) s_s[h * kSlots + key] = sacc[h];
+    }
+  }
+  __syncthreads();
+
+  // ---- 3b. exact softmax over the slots, one wave per head; bf16 P in the permuted key order
+  // over the head's score row (a single pass: n / 2 <= 64 words)
+  {
+    const int h = wave;
+    float* sh = s_s + h * kSlots;
+    float mx = -INFINITY;
+    for (int j = lane; j < n; j += 64) mx = fmaxf(mx, sh[j]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+    const float c = p.scale_log2;
+    const float nmc = -mx * c;
+    const int n_pad = (n + 31) & ~31;
+    float sum = 0.f;
+    const int q = lane;
+    uint32_t w = 0;
+    if (q < n_pad / 2) {
+      const int ja = 16 * (q >> 3) + mf_key(2 * (q & 7));
+      const int jb = ja + 1;
+      const float ea = ja < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(sh[ja], c, nmc)) : 0.f;
+      const float eb = jb < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(sh[jb], c, nmc)) : 0.f;
+      w = pack_bf16(ea, eb);
+      sum = bf16lo(w) + bf16hi(w);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every lane's reads precede the writes
+    if (q < n_pad / 2) sh[q] = __uint_as_float(w);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += shfl_xor_f(sum, o);
+    if (lane == 0) {
+      ml[h][0] = mx * c;
+      ml[h][1] = sum;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3c. output of this wave's 32 slots: two 16-key steps x 4 dim blocks
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  if (wave < n_blk) {
+    int tr_off[2][4];
+    const int tr_row = 4 * hi + ((lane & 15) >> 2);
+    const int tr_dch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int row = 8 * x + tr_row;
+        tr_off[x][db] = row * kMfRow + 16 * ((4 * db + tr_dch) ^ mf_swz(row)) + 8 * (lane & 1);
+      }
+    stage_rows(vraw, wtile);
+    put_new_row(newv, wtile);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2) {
+      const int pstep = 2 * wave + st2;
+      bf16x8 pa = zero8;
+      if (l32 < G) pa = *reinterpret_cast<const bf16x8*>(s_s + l32 * kSlots + 8 * pstep + 4 * hi);
+      const unsigned char* base = wtile + st2 * 16 * kMfRow;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const i16x4 a = lds_read_tr(base + tr_off[0][db]);
+        const i16x4 cc = lds_read_tr(base + tr_off[1][db]);
+        const i16x4 both[2] = {a, cc};
+        o[db] = mfma32(pa, __builtin_bit_cast(bf16x8, both), o[db]);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with its tile and with P
+  float* red = reinterpret_cast<float*>(vt);  // [4 waves][G][128]
+  if (hi == 0) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int h = 0; h < G; ++h) red[(wave * G + h) * kHeadDim + 32 * db + l32] = o[db][h];
+  }
+  __syncthreads();
+
+  const float vs = FP8 ? p.v_scale : 1.0f;
+  for (int i = tid; i < G * kHeadDim; i += kDecThreads) {
+    const int h = i / kHeadDim;
+    const int d = i - h * kHeadDim;
+    const float ov = vs * (red[(0 * G + h) * kHeadDim + d] + red[(1 * G + h) * kHeadDim + d] +
+                           red[(2 * G + h) * kHeadDim + d] + red[(3 * G + h) * kHeadDim + d]);
+    const int head = kvh * G + h;
+    float y = ov / ml[h][1];
+    if (p.gated) {
+      const float g = bf16lo(p.gate[((int64_t)b * p.Hq + head) * kHeadDim + d]);
+      y *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+    }
+    p.out[((int64_t)b * p.Hq + head) * kHeadDim + d] = (uint16_t)(pack_bf16(y, 0.f) & 0xffffu);
+  }
+}
+
 // bf16 -> E4M3 of value * inv_scale, 16 elements per lane.
 __global__ __launch_bounds__(256) void to_fp8_kernel(ToFp8Params p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -981,6 +1295,11 @@ hipError_t decode_scratch_ptr(void** out) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
+  if (p.window > 0 && p.window <= 128 && p.Hq == 4 * p.Hkv) {
+    if (p.fp8) hipLaunchKernelGGL(decode_ring_kernel<true>, dim3(p.Hkv, p.B), dim3(kDecThreads), 0, s, p);
+    else hipLaunchKernelGGL(decode_ring_kernel<false>, dim3(p.Hkv, p.B), dim3(kDecThreads), 0, s, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)(((int64_t)p.B * (p.Hq + p.Hkv) + 15) / 16)),
                      dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();

@@ -35,6 +35,7 @@ def _spacing(v):
 
 CASES = [  # Hq, Hkv, window, lens, k_scale, v_scale
     (32, 8, 128, [200, 128, 5, 1000], 1.0, 1.0),
+    (32, 8, 64, [64, 65, 300, 1], 0.5, 2.0),      # another ring width, scaled E4M3 entries
     (32, 8, 0, [1, 2048, 3000], 0.5, 2.0),
     (32, 8, 0, [777, 1024, 1025], 1.0, 0.25),
     (32, 4, 0, [1500, 60], 1.0, 1.0),       # 8 query heads per KV head
