@@ -137,8 +137,8 @@ def bench_block(torch, zg, si, dev, stream, args):
     cfg_glo = zg.AttnConfig(window=0, gated=False, rope_base=ROPE_BASE)
     out_swa = torch.empty_like(swa["q"])
     out_glo = torch.empty_like(glo["q"])
-    ws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg_swa, B, T), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(max(zg.zg_attn_prefill_workspace_bytes(c, B, T) for c in (cfg_swa, cfg_glo)),
+                     dtype=torch.uint8, device=dev)
 
     def run_swa():
         zg.zg_attn_prefill(cfg_swa, swa["q"], swa["k"], swa["v"], swa["gate"], out=out_swa,
@@ -527,7 +527,8 @@ def bench_backward(torch, zg, si, dev, stream, Bb=B, Tb=T):
         cfg = zg.AttnConfig(window=win, gated=win > 0, rope_base=ROPE_BASE)
         g = x["gate"] if win else None
         out, lse = zg.zg_attn_forward_train(cfg, x["q"], x["k"], x["v"], g)
-        fws = torch.empty(zg.zg_attn_prefill_workspace_bytes(cfg, Bb, Tb), dtype=torch.uint8, device=dev)
+        fws = torch.empty(zg.zg_attn_forward_train_workspace_bytes(cfg, Bb, Tb), dtype=torch.uint8,
+                          device=dev)
         bws = torch.empty(zg.zg_attn_backward_workspace_bytes(cfg, Bb, Tb), dtype=torch.uint8, device=dev)
         f_ms = _time(torch, stream, lambda: zg.zg_attn_forward_train(
             cfg, x["q"], x["k"], x["v"], g, out=out, lse=lse, workspace=fws), 5)

@@ -16,7 +16,8 @@ from ._abi import (LIB_PATH, ZgAttnCfg, ZgTokenStrides, load_library, ZG_OK, ZG_
                    ZG_ERR_SHAPE, ZG_ERR_UNSUPPORTED, ZG_ERR_WORKSPACE, ZG_ERR_HIP, EXPORTS)
 
 __all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached",
-           "zg_attn_forward_train", "zg_attn_backward", "zg_attn_backward_workspace_bytes",
+           "zg_attn_forward_train", "zg_attn_forward_train_workspace_bytes", "zg_attn_backward",
+           "zg_attn_backward_workspace_bytes",
            "zg_hbm_read_probe", "zg_attn_decode", "zg_attn_decode_noalloc", "zg_attn_decode_fp8",
            "zg_kv_to_fp8", "zg_kv_bytes",
            "zg_attn_prefill_workspace_bytes", "zg_attn_decode_workspace_bytes", "zg_rmsnorm",
@@ -194,6 +195,11 @@ def _packed(t, name, shape):
         raise ValueError(f"{name} must be a contiguous tensor of shape {tuple(shape)}")
 
 
+def zg_attn_forward_train_workspace_bytes(cfg: AttnConfig, B: int, T: int) -> int:
+    c = cfg.c()
+    return load_library().zg_attn_forward_train_workspace_bytes(ctypes.byref(c), B, T)
+
+
 def zg_attn_forward_train(cfg: AttnConfig, q, k, v, gate=None, *, out=None, lse=None,
                           workspace=None, stream=None):
     """Forward for training (see include/zg_attn.h): packed q, gate [B, T, Hq, 128] and k, v
@@ -219,7 +225,7 @@ def zg_attn_forward_train(cfg: AttnConfig, q, k, v, gate=None, *, out=None, lse=
     _packed(out, "out", (B, T, Hq, D))
     _need(lse, "lse", torch.float32)
     _packed(lse, "lse", (B, T, Hq))
-    need = zg_attn_prefill_workspace_bytes(cfg, B, T)
+    need = zg_attn_forward_train_workspace_bytes(cfg, B, T)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     c = cfg.c()

@@ -234,6 +234,11 @@ static zg_status check_train(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
   return ZG_OK;
 }
 
+size_t zg_attn_forward_train_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
+  if (!cfg || B < 1 || T < 1 || cfg->n_kv_heads < 1) return 0;
+  return align256((size_t)B * T * cfg->n_kv_heads * kD * 2);  // k_hat for the tiled kernel
+}
+
 zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, const void* q,
                                 const void* k, const void* v, const void* gate, void* out,
                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
@@ -245,7 +250,7 @@ zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, co
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) ||
         (cfg->gated && !aligned16(gate)))
       return fail(ZG_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
-    const size_t need = zg_attn_prefill_workspace_bytes(cfg, B, T);
+    const size_t need = zg_attn_forward_train_workspace_bytes(cfg, B, T);
     if (!workspace || workspace_bytes < need)
       return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                   workspace ? workspace_bytes : (size_t)0, need);

@@ -125,7 +125,8 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
  *
  * zg_attn_forward_train: out as zg_attn_prefill, plus lse [B, T, Hq] fp32, the natural-log
  * log-sum-exp of each query row's scaled scores over its key set (what the backward recomputes the
- * softmax from). workspace >= zg_attn_prefill_workspace_bytes(cfg, B, T).
+ * softmax from). workspace >= zg_attn_forward_train_workspace_bytes(cfg, B, T) (the normalised,
+ * rotated keys: B T Hkv 256 bytes, rounded up to 256).
  *
  * zg_attn_backward: gradients of L = sum(dout * out) with respect to q, k, v and the gate logits
  * (dgate, written only when cfg->gated), given the forward's inputs, its out and lse:
@@ -140,6 +141,8 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
  * Errors: NULL -> ZG_ERR_NULL; B < 1, T < 1 -> ZG_ERR_SHAPE; unsupported head ratio, head_dim,
  * rot_dim, or T * Hq * 256 bytes >= 4 GiB -> ZG_ERR_UNSUPPORTED; small workspace ->
  * ZG_ERR_WORKSPACE. */
+size_t zg_attn_forward_train_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T);
+
 zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, const void* q,
                                 const void* k, const void* v, const void* gate, void* out,
                                 float* lse, void* workspace, size_t workspace_bytes, void* stream);

@@ -199,3 +199,16 @@ def test_decode_noalloc_rejects_before_touching_the_device():
         <= 96 << 20
     assert zg.zg_attn_decode_workspace_bytes(zg.AttnConfig(window=0, gated=False), 64, 94209) \
         > 96 << 20
+
+
+def test_forward_train_workspace_query():
+    """The training forward runs the tiled kernel on keys normalised and rotated into its
+    workspace: B T Hkv 256 bytes; a smaller workspace is rejected before any launch."""
+    band = zg.AttnConfig(window=128, gated=True)
+    assert zg.zg_attn_forward_train_workspace_bytes(band, 2, 1000) == 2 * 1000 * 8 * 256
+    lib = zg.load_library()
+    c = band.c()
+    need = zg.zg_attn_forward_train_workspace_bytes(band, 1, 1000)
+    st = lib.zg_attn_forward_train(ctypes.byref(c), 1, 1000, 16, 16, 16, 16, 16, 16, 16, need - 16,
+                                   None)
+    assert st == zg.ZG_ERR_WORKSPACE
