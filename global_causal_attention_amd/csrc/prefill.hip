@@ -281,48 +281,70 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int lane = tid & 63;
+
+  // ---- work items: heavy query tiles first for full causal attention, the workgroups of one
+  // (sequence, KV head) together on an XCD. One item per workgroup, or (p.persist) one workgroup
+  // per CU walking the items the hardware order would give its XCD, 8 * round + the CU's place in
+  // the XCD, the places snaking from round to round so that every CU sees heavy and light items.
+  // A persistent workgroup brings the next item's q rows into its staging rows during iteration 1
+  // of the current item, and the next item's first two K tiles once the current item's last
+  // iteration has read its K buffers, so neither waits on memory at the next item's start.
+  int item_k = 0;
+  int vb = p.persist ? -1 : (int)blockIdx.x;   // -1: the schedule's first item, looked up below
+  bool q_ready = false;   // this item's raw q rows are already in the staging rows
+  bool k_ready = false;   // this item's first K tiles were issued during the previous item
+  while (true) {
+  // The kernel arguments are read through a pointer the compiler must treat as new on every item,
+  // so it loads them where the item needs them instead of keeping all of them live across the
+  // loop (which would spill).
+  typedef __attribute__((address_space(4))) const PrefillParams* karg_prefill_ptr;
+  karg_prefill_ptr kpp = (karg_prefill_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kpp));
+  const __attribute__((address_space(4))) PrefillParams& p = *kpp;
+  // likewise the lane index, so the per-lane offsets derived from it are recomputed per item
+  // rather than held in registers through the q prologue
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-
-  // ---- work item: heavy query tiles first for full causal attention, the workgroups of one
-  // (sequence, KV head) together on an XCD
-  int t_idx, bh;
-  xcd_pair_major(blockIdx.x, p.B * p.Hkv, p.n_qtiles, t_idx, bh);
-  const int qtile = (p.window == 0) ? (p.n_qtiles - 1 - t_idx) : t_idx;
-  const int b = bh / p.Hkv;
-  const int kvh = bh - b * p.Hkv;
-  const int r0 = qtile * MQ;
+  const int n_items = p.n_qtiles * p.B * p.Hkv;
+  auto item_at = [&](int k) -> int {
+    if (!p.persist) return k == 0 ? (int)blockIdx.x : n_items;
+    const int cx = (int)(gridDim.x >> 3), x = (int)(blockIdx.x & 7), cw = (int)(blockIdx.x >> 3);
+    const int cc = (k & 1) ? (cx - 1 - cw) : cw;
+    const int64_t vb_ = x + 8 * ((int64_t)k * cx + cc);
+    return vb_ < n_items ? (int)vb_ : n_items;
+  };
   const int T = p.T;
   const int W = p.window;
   const int qoff = p.qoff;
-
-  const int hg = wave % G;
-  const int qb = wave / G;
-  const int head = kvh * G + hg;
-  const int qbase = r0 + 32 * qb;
-  const float c = p.scale_log2;
-
-  // ---- key tile range of the workgroup (key rows; query row t is key row qoff + t)
-  const int q_last = qoff + min(r0 + MQ, T) - 1;
-  int k_begin = 0;
-  if (W > 0) k_begin = max(0, qoff + r0 - W + 1) & ~(kNk - 1);
-  const int n_tiles = (q_last + 1 - k_begin + kNk - 1) / kNk;
-
-  // ---- tile streaming: waves 0-3 bring K rows, waves 4-7 V rows, straight into chunk-swizzled
-  // LDS rows (buffer_load ... lds, 4 rows = 1 KB per instruction, 4 per wave per tile). The
-  // buffer's range check returns zeros for rows at or past T. Iteration j reads K_{j+1} and V_{j-1}
-  // and streams K_{j+2} and V_j into the buffers those tiles' predecessors left; the loads are
-  // inline asm (so later LDS reads do not wait for them) and are awaited before the barrier that
-  // ends the iteration.
   const bool v_loader = wave >= 4;
   const int wg = wave & 3;
   const int row_bytes = (int)((v_loader ? p.sv : (int64_t)p.Hkv * kHeadDim) * 2);
-  const uint16_t* slab = v_loader ? p.v + (int64_t)b * p.kv_rows * p.sv + (int64_t)kvh * kHeadDim
-                                  : p.khat + ((int64_t)b * p.kv_rows * p.Hkv + kvh) * kHeadDim;
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, (int)((uint32_t)p.n_keys * (uint32_t)row_bytes),
-                                        0x00020000);  // byte count < 2^32, read as unsigned
+  const int q_row_bytes = (int)(p.sq * 2);
+  unsigned char* qs = smem + kQStage0 + wave * kQWaveBytes;
+  // key tile range of an item (key rows; query row t is key row qoff + t)
+  auto item_k_begin = [&](int r0_) -> int {
+    return W > 0 ? (max(0, qoff + r0_ - W + 1) & ~(kNk - 1)) : 0;
+  };
+  auto item_n_tiles = [&](int r0_) -> int {
+    const int q_last_ = qoff + min(r0_ + MQ, T) - 1;
+    return (q_last_ + 1 - item_k_begin(r0_) + kNk - 1) / kNk;
+  };
+  auto item_coords = [&](int vb_, int& qtile_, int& b_, int& kvh_) {
+    int t_, bh_;
+    xcd_pair_major(vb_, p.B * p.Hkv, p.n_qtiles, t_, bh_);
+    qtile_ = (W == 0) ? (p.n_qtiles - 1 - t_) : t_;
+    b_ = bh_ / p.Hkv;
+    kvh_ = bh_ - b_ * p.Hkv;
+  };
+  auto kv_rsrc = [&](int b_, int kvh_) {
+    const uint16_t* slab_ = v_loader ? p.v + (int64_t)b_ * p.kv_rows * p.sv + (int64_t)kvh_ * kHeadDim
+                                     : p.khat + ((int64_t)b_ * p.kv_rows * p.Hkv + kvh_) * kHeadDim;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)slab_, 0,
+                                             (int)((uint32_t)p.n_keys * (uint32_t)row_bytes),
+                                             0x00020000);  // byte count < 2^32, read as unsigned
+  };
   // lane -> (row (lane >> 4) of the 4-row group i, physical chunk lane & 15)
   auto dma_voff = [&](int i) -> uint32_t {
     const int row = 4 * i + (lane >> 4);  // row within the wave's 16 (swizzle uses row & 15)
@@ -330,20 +352,64 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
   const uint32_t lds_k = (uint32_t)(uintptr_t)smem + kLdsK0;
   const uint32_t lds_v = (uint32_t)(uintptr_t)smem + kLdsV0;
-  auto dma_tile = [&](int t, bool is_v) {  // tile t into buffer t & 1
+  // tile t of the keys starting at key row kb0 into buffer t & 1
+  auto dma_tile_at = [&](__amdgpu_buffer_rsrc_t rs_, int kb0, int t, bool is_v) {
     const uint32_t base = (is_v ? lds_v : lds_k) + (t & 1) * kTileBytes + 16 * wg * kRow;
-    const uint32_t row0 = (uint32_t)(k_begin + t * kNk + 16 * wg);
+    const uint32_t row0 = (uint32_t)(kb0 + t * kNk + 16 * wg);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t m0v = base + 4 * i * kRow;
       const uint32_t soff = (row0 + 4 * i) * (uint32_t)row_bytes;
-      lds_dma16(m0v, dma_voff(i), rsrc, soff);
+      lds_dma16(m0v, dma_voff(i), rs_, soff);
+    }
+  };
+  // this wave's 32 raw q rows of an item into its staging rows (row r at r * kRow, chunk c at
+  // c ^ swz(r)): 8 instructions of 4 rows; rows at or past T read as zeros
+  auto dma_q_rows = [&](int b_, int head_, int row0_) {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.q + (int64_t)b_ * T * p.sq + (int64_t)head_ * kHeadDim), 0,
+        (int)((uint32_t)T * (uint32_t)q_row_bytes), 0x00020000);
+    const uint32_t lq = (uint32_t)(uintptr_t)qs;
+    // the rows' previous contents (the current item's operands) have been read out
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const uint32_t voff = (uint32_t)((lane >> 4) * q_row_bytes + 16 * ((lane & 15) ^ swz(r)));
+      lds_dma16(lq + i * 1024, voff, rq, (uint32_t)(row0_ + 4 * i) * (uint32_t)q_row_bytes);
     }
   };
   auto vm_wait = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  const int hg = wave % G;
+  const int qb = wave / G;
+  const float c = p.scale_log2;
 
-  // the first two K tiles go out before the q prologue
-  if (!v_loader) {
+  if (vb < 0) vb = item_at(0);
+  if (vb >= n_items) break;
+  const int vb_next = item_at(item_k + 1);
+  const bool has_next = vb_next < n_items;
+  int qtile, b, kvh;
+  item_coords(vb, qtile, b, kvh);
+  const int r0 = qtile * MQ;
+  const int head = kvh * G + hg;
+  const int qbase = r0 + 32 * qb;
+  const int k_begin = item_k_begin(r0);
+  const int n_tiles = item_n_tiles(r0);
+  // the next item's q rows are brought in during iteration 1 (the register RoPE of 42 dims keeps
+  // the staging rows free of scratch)
+  const bool prefetch_q = p.persist && has_next && n_tiles >= 3 && p.rope.half == 21;
+
+  // ---- tile streaming: waves 0-3 bring K rows, waves 4-7 V rows, straight into chunk-swizzled
+  // LDS rows (buffer_load ... lds, 4 rows = 1 KB per instruction, 4 per wave per tile). The
+  // buffer's range check returns zeros for rows at or past T. Iteration j reads K_{j+1} and V_{j-1}
+  // and streams K_{j+2} and V_j into the buffers those tiles' predecessors left; the loads are
+  // inline asm (so later LDS reads do not wait for them) and are awaited before the barrier that
+  // ends the iteration.
+  const __amdgpu_buffer_rsrc_t rsrc = kv_rsrc(b, kvh);
+  auto dma_tile = [&](int t, bool is_v) { dma_tile_at(rsrc, k_begin, t, is_v); };
+
+  // the first two K tiles go out before the q prologue (unless the previous item issued them)
+  if (!v_loader && !k_ready) {
     dma_tile(0, false);
     if (n_tiles > 1) dma_tile(1, false);
   }
@@ -353,12 +419,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // are in flight.
   bf16x8 qf[8];
   {
-    unsigned char* qs = smem + kQStage0 + wave * kQWaveBytes;
     const int r = lane >> 1;
     const int half = lane & 1;
     const int t = qbase + r;
     float x[64];
-    if (t < T) {
+    if (q_ready) {
+      // prefetched raw rows (landed: iteration 2 of the previous item waited for them)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        unpack8(*reinterpret_cast<const u32x4*>(qs + r * kRow + 16 * ((8 * half + i) ^ swz(r))),
+                x + 8 * i);
+      // every lane has read its half row before any lane of the wave writes q_hat over it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else if (t < T) {
       const u32x4* s4 = reinterpret_cast<const u32x4*>(
           p.q + ((int64_t)b * T + t) * p.sq + (int64_t)head * kHeadDim + 64 * half);
 #pragma unroll
@@ -368,11 +441,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       for (int i = 0; i < 64; ++i) x[i] = 0.f;
     }
     if (p.rope.half == 21) {
-      norm_rope_row_r42(x, half, p.q_norm_w, p.eps, p.pos0 + t, p.rope);
+      norm_rope_row_r42(x, half, p.q_norm_w, p.eps, p.pos0 + t, *(const RopeTableH*)&p.rope);
     } else {
       // the [dim][row] RoPE scratch (32 rows x 64 floats) overlays this wave's staging rows;
       // every access to it precedes the bf16 row writes below in this wave's program order
-      norm_rope_row(x, half, p.q_norm_w, p.eps, p.pos0 + t, p.rope, reinterpret_cast<float*>(qs),
+      norm_rope_row(x, half, p.q_norm_w, p.eps, p.pos0 + t, *(const RopeTableH*)&p.rope,
+                    reinterpret_cast<float*>(qs),
                     r, 32);
     }
 #pragma unroll
@@ -515,6 +589,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const bool more = j + 1 < n_tiles;
     if (v_loader) dma_tile(j, true);
     else if (j + 2 < n_tiles) dma_tile(j + 2, false);
+    const bool pf = prefetch_q && j == 1;  // n_tiles >= 3: iteration 2 waits for these rows
+    if (pf) {
+      int qt_n, b_n, kvh_n;
+      item_coords(vb_next, qt_n, b_n, kvh_n);
+      dma_q_rows(b_n, kvh_n * G + hg, qt_n * MQ + 32 * qb);
+    }
     mask_tile(j, sc);
     float e[32];
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -568,7 +648,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     if (__builtin_amdgcn_ballot_w64(!m_valid || !(rs <= 0x1p64f))) slow_path(sc, sn, pk_cur, rs);
     l_run += rs;
     (void)more;
-    vm_wait();
+    // this iteration's tiles have landed (the q rows issued after them may still be in flight)
+    if (pf) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else vm_wait();
     __syncthreads();
   };
 
@@ -609,6 +691,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   if (j < n_tiles) {
     iter(j, std::integral_constant<int, 1>{}, sB, sA, pB, pA);
     ++j;
+  }
+  // every wave has passed the last iteration's barrier, so no K buffer is read any more: the next
+  // item's first K tiles go out now
+  const bool next_k = p.persist && has_next;
+  if (next_k && !v_loader) {
+    int qt_n, b_n, kvh_n;
+    item_coords(vb_next, qt_n, b_n, kvh_n);
+    const __amdgpu_buffer_rsrc_t rs_n = kv_rsrc(b_n, kvh_n);
+    const int kb_n = item_k_begin(qt_n * MQ);
+    dma_tile_at(rs_n, kb_n, 0, false);
+    if (item_n_tiles(qt_n * MQ) > 1) dma_tile_at(rs_n, kb_n, 1, false);
   }
   // PV of the last tile (its weights are in the set written last)
   {
@@ -661,6 +754,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       if (store) *reinterpret_cast<u32x4*>(dst + 8 * (2 * m + hi)) = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
+  q_ready = prefetch_q;
+  k_ready = next_k;
+  vb = vb_next;
+  ++item_k;
+  }  // items
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -731,14 +829,29 @@ hipError_t launch_kprep(const KPrepParams& p, hipStream_t s) {
 }
 
 template <int G, bool GATED>
-static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
+static hipError_t launch_prefill_t(const PrefillParams& p_in, hipStream_t s) {
   constexpr int lds = kLdsBytes;
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = prefill_kernel<G, GATED>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  const int64_t grid = (int64_t)p.n_qtiles * p.B * p.Hkv;
+  PrefillParams p = p_in;
+  int64_t grid = (int64_t)p.n_qtiles * p.B * p.Hkv;
+  // Full causal layers with many items run persistent: one workgroup per CU (the LDS allows one),
+  // the CUs of an XCD sharing its (sequence, KV head) pairs as the item order expects. The q rows
+  // prefetched for the next item are read through one buffer resource per sequence, whose byte
+  // range must stay below 2^32.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      p.window == 0 && p.rope.half == 21 && (p.B * p.Hkv) % 8 == 0 && cus > 0 && cus % 8 == 0 &&
+      grid >= 2 * (int64_t)cus && (int64_t)p.T * p.sq * 2 < (int64_t)1 << 32) {
+    p.persist = 1;
+    grid = cus;
+  } else {
+    p.persist = 0;
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }

@@ -49,6 +49,7 @@ struct PrefillParams {
   int32_t window;
   int32_t n_qtiles;
   int32_t seg_steps;  // banded kernel: 64-query steps per workgroup
+  int32_t persist;    // tiled kernel: one workgroup per CU walks the items (set by the launcher)
   // Keys: sequence b's k_hat and v rows start kv_rows rows apart; n_keys of them are valid, and
   // query row t is key row qoff + t (rows before qoff are earlier positions from a cache).
   // Plain prefill: kv_rows = n_keys = T, qoff = 0.

@@ -75,6 +75,19 @@ def test_prefill_edges(B, T, Hq, Hkv, W, gated, base, pos0):
     assert_parity(out, ref, f"B={B} T={T} Hq={Hq}/{Hkv} W={W}")
 
 
+@pytest.mark.parametrize("B,T,gated,base,pos0,norm_w", [
+    # full causal layers with at least two query tiles per compute unit: one workgroup per CU
+    # walks the tiles, heavy ones first, bringing the next tile's q rows and first key tiles in
+    # while the current one runs (tiles of 1, 2 and >= 3 key tiles mixed, ragged tails)
+    (8, 601, True, 1e6, 0, False),
+    (16, 300, False, 1e4, 0, True),
+    (4, 1030, True, 1e6, 3, False),
+])
+def test_prefill_persistent_causal(B, T, gated, base, pos0, norm_w):
+    out, ref = _run(B, T, 32, 8, 0, gated, base, 17 + T, pos0=pos0, norm_w=norm_w)
+    assert_parity(out, ref, f"persistent causal B={B} T={T} gated={gated} norm_w={norm_w}")
+
+
 @pytest.mark.parametrize("W", [128, 0])
 def test_prefill_token_strided_views(W):
     # q, k, v and gate as column slices of one fused [B, T, (2 Hq + 2 Hkv) * 128] projection buffer,
