@@ -117,7 +117,12 @@ constexpr int kStageRow = 132;  // floats per staged fp32 row: 528 bytes, rows 4
 // dx = (dxn - xn mean(dxn . xn)) / r with r = sqrt(mean(x^2) + eps). Two adjacent lanes per row
 // (half = lane & 1 holds dims 64 half .. +63; the rotated dims all lie in half 0); x and dx are bf16
 // rows in global memory.
-__device__ __forceinline__ void dx_from_staged(float* srow, const uint16_t* xrow, uint16_t* drow,
+__device__ __forceinline__ void load_row_half(const uint16_t* xrow, int half, u32x4 (&xr)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xr[i] = reinterpret_cast<const u32x4*>(xrow + 64 * half)[i];
+}
+
+__device__ __forceinline__ void dx_from_staged(float* srow, const u32x4 (&xr)[8], uint16_t* drow,
                                                int half, int64_t pos, const RopeTableH& rt,
                                                float eps) {
   const int h = rt.half;
@@ -142,7 +147,7 @@ __device__ __forceinline__ void dx_from_staged(float* srow, const uint16_t* xrow
     for (int j = 0; j < 4; ++j) g[4 * i + j] = v[j];
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) unpack8(reinterpret_cast<const u32x4*>(xrow + 64 * half)[i], x + 8 * i);
+  for (int i = 0; i < 8; ++i) unpack8(xr[i], x + 8 * i);
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
@@ -300,15 +305,13 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = f32x16{};
 
-  // the operands above are loaded: pinning them here keeps the loop free of waits on them (which
-  // would also wait for the tile loads in flight)
+  // tile 0 goes out behind the operand loads and one wait covers both; pinning the operands after
+  // it keeps the loop free of waits on them (which would also wait for the tile loads in flight)
+  dma_tile(0);
   vm_wait();
 #pragma unroll
   for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(qf[st]), "+v"(dof[st]));
   asm volatile("" : "+v"(auxb));
-
-  dma_tile(0);
-  vm_wait();
   __syncthreads();
   for (int j = 0; j < n_tiles; ++j) {
     if (j + 1 < n_tiles) dma_tile(j + 1);
@@ -392,7 +395,14 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
   }
 
   // epilogue: dq_hat rows (one query per lane, 4 dims per register group) staged in the freed
-  // tile buffers, then dq with two lanes per row
+  // tile buffers (the loop ended on a barrier, so no wave reads them any more; each wave reads back
+  // only its own rows, in order behind its writes), then dq with two lanes per row. The raw q rows
+  // the RMSNorm derivative needs are loaded first, so their latency hides behind the staging.
+  const int er = lane >> 1, ehalf = lane & 1;
+  const int et = qbase + er;
+  const int64_t erow = (((int64_t)b * T + min(et, T - 1)) * p.Hq + head) * kHeadDim;
+  u32x4 xr[8];
+  load_row_half(p.q + erow, ehalf, xr);
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * kStageRow;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -402,15 +412,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
                        dq[db][4 * rq + 2] * p.scale, dq[db][4 * rq + 3] * p.scale};
       *reinterpret_cast<f32x4*>(stage + l32 * kStageRow + 32 * db + 8 * rq + 4 * hi) = v;
     }
-  __syncthreads();
-  {
-    const int r = lane >> 1, half = lane & 1;
-    const int t = qbase + r;
-    if (t < T) {  // both lanes of a row agree
-      const int64_t row = (((int64_t)b * T + t) * p.Hq + head) * kHeadDim;
-      dx_from_staged(stage + r * kStageRow, p.q + row, p.dq + row, half, p.pos0 + t, p.rope, p.eps);
-    }
-  }
+  if (et < T)  // both lanes of a row agree
+    dx_from_staged(stage + er * kStageRow, xr, p.dq + erow, ehalf, p.pos0 + et, p.rope, p.eps);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -473,11 +476,6 @@ void bwd_kv_kernel(BwdParams p) {
       for (int st = 0; st < 8; ++st) kB[kb][st] = bf16x8{};
     }
   }
-  vm_wait();
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(kB[kb][st]));  // loaded: no waits in the loop
   const bf16x8 one_l = ones3(hi == 0);
   const bf16x8 one_d = ones3(hi == 1);
 
@@ -520,8 +518,14 @@ void bwd_kv_kernel(BwdParams p) {
     }
 
   const unsigned char* vtile = smem + kKvVTile;
+  // the first step's rows go out behind the V rows and the K operands, one wait for all of them;
+  // the K operands are pinned after it, so the loop holds no waits on them
   dma_step(0);
   vm_wait();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(kB[kb][st]));
   __syncthreads();  // every wave's V rows are in LDS
   for (int i = 0; i < n_steps; ++i) {
     vm_wait();  // this step's rows are in LDS (the wave's own loads)
@@ -642,6 +646,13 @@ void bwd_kv_kernel(BwdParams p) {
   // (dim block `wave` of both key blocks): dv straight to memory, dk_hat staged as rows
   f32x4* red = reinterpret_cast<f32x4*>(smem);
   f32x4 dks[8];
+  // the raw k rows of the epilogue's RMSNorm derivative (waves 0 and 1, two lanes per key row)
+  // are loaded now, so their latency hides behind the reduction
+  const int er = 32 * (wave & 1) + (lane >> 1), ehalf = lane & 1;
+  const int ekey = k0 + er;
+  const int64_t erow = (((int64_t)b * T + min(ekey, T - 1)) * p.Hkv + kvh) * kHeadDim;
+  u32x4 xr[8];
+  if (wave < 2) load_row_half(p.k + erow, ehalf, xr);
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     __syncthreads();  // the buffers (or the previous round's sums) are free
@@ -683,14 +694,8 @@ void bwd_kv_kernel(BwdParams p) {
     *reinterpret_cast<f32x4*>(stage + (32 * kb + l32) * kStageRow + 32 * wave + 8 * rq + 4 * hi) = dks[u];
   }
   __syncthreads();
-  if (wave < 2) {  // dk: two lanes per key row, 32 rows per wave
-    const int r = 32 * wave + (lane >> 1), half = lane & 1;
-    const int key = k0 + r;
-    if (key < T) {
-      const int64_t row = (((int64_t)b * T + key) * p.Hkv + kvh) * kHeadDim;
-      dx_from_staged(stage + r * kStageRow, p.k + row, p.dk + row, half, p.pos0 + key, p.rope, p.eps);
-    }
-  }
+  if (wave < 2 && ekey < T)  // dk: two lanes per key row, 32 rows per wave
+    dx_from_staged(stage + er * kStageRow, xr, p.dk + erow, ehalf, p.pos0 + ekey, p.rope, p.eps);
 }
 
 // ---------------------------------------------------------------------------------------------

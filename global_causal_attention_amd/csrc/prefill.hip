@@ -579,75 +579,89 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     need_ref = __builtin_amdgcn_ballot_w64(m_ref != 0.f) != 0;
   };
 
-  // One iteration j >= 1 (buffer parity PAR = j & 1): the 32 (34 with the 9th step) MFMAs (PV of
-  // tile j-1 with its weights, then QK^T of tile j+1) are issued one by one, each followed by a slice of this tile's
-  // softmax (an exponential, plus a pack and a row-sum step every other slot), which runs in the
-  // MFMA shadow.
+  // One iteration j >= 1 (buffer parity PAR = j & 1): 32 MFMAs (34 with the 9th step) issued one
+  // by one, each followed by a slice of tile j's softmax (an exponential, plus a pack and a
+  // row-sum step every other slot), which runs in the MFMA shadow. The slots:
+  //   0-1    the last key-dimension step of S_j (K_j, read before the previous barrier)
+  //   2-17   PV of tile j-1 with its weights
+  //   18-31  QK^T of tile j+1, key-dimension steps 0-6 (step 7 opens the next iteration)
+  // The A operands stream through a two-deep ring that runs on across iterations: the last two
+  // reads of an iteration fetch the next one's slots 0-1 from K_{j+1}, which every wave can
+  // already see, so after the barrier the matrix work resumes without waiting on LDS. Masking
+  // S_j before its last step is exact (a -inf partial sum stays -inf), and so is the slow path's
+  // shift of the partial S_{j+1} (the remaining step adds on top of it).
+  constexpr int kAhead = 2;
+  bf16x8 ring[kAhead];
   auto iter = [&](int j, auto par_c, f32x16 (&sc)[2], f32x16 (&sn)[2], u32x4 (&pk_prev)[4],
                   u32x4 (&pk_cur)[4]) {
     constexpr int PAR = decltype(par_c)::value;
-    const bool more = j + 1 < n_tiles;
-    if (v_loader) dma_tile(j, true);
-    else if (j + 2 < n_tiles) dma_tile(j + 2, false);
     const bool pf = prefetch_q && j == 1;  // n_tiles >= 3: iteration 2 waits for these rows
-    if (pf) {
-      int qt_n, b_n, kvh_n;
-      item_coords(vb_next, qt_n, b_n, kvh_n);
-      dma_q_rows(b_n, kvh_n * G + hg, qt_n * MQ + 32 * qb);
-    }
     mask_tile(j, sc);
     float e[32];
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) sn[kb] = f32x16{};
-    // A operand of slot i (slots 32 and 33 use the constant one_op)
+    // A operand of slot i; slots 32 and 33 are the next iteration's slots 0 and 1
     auto opnd = [&](int i) -> bf16x8 {
-      if (i < 16) return rd_v(PAR ^ 1, i >> 2, i & 3);
-      return rd_k(PAR ^ 1, (i - 16) >> 1, (i - 16) & 1);
+      if (i < 2) return rd_k(PAR, 7, i);
+      if (i < 18) return rd_v(PAR ^ 1, (i - 2) >> 2, (i - 2) & 3);
+      if (i < 32) return rd_k(PAR ^ 1, (i - 18) >> 1, (i - 18) & 1);
+      return rd_k(PAR ^ 1, 7, i - 32);
     };
-    constexpr int kAhead = 2;
-    bf16x8 ring[kAhead];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) ring[i] = opnd(i);
+    // one exponential of tile j's scores, and the pack and row-sum step of each completed pair
+    auto soft = [&](int k) {
+      e[k] = __builtin_amdgcn_exp2f(sc[k >> 4][k & 15]);
+      if (k & 1) {
+        const int pr = k >> 1;
+        uint32_t w = pack_bf16(e[k - 1], e[k]);
+        float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
+                                                   part[pr & 3], false);
+        // pins the pair's work to this slot: the compiler would otherwise sink it past the
+        // branch around the 9th step, out of the MFMA shadow
+        asm volatile("" : "+v"(w), "+v"(ps));
+        pk_cur[pr >> 2][pr & 3] = w;
+        part[pr & 3] = ps;
+      }
+    };
 #pragma unroll
     for (int i = 0; i < 34; ++i) {
       // matrix work
       if (i < 32) {
         const bf16x8 a = ring[i % kAhead];
-        if (i + kAhead < 32) ring[i % kAhead] = opnd(i + kAhead);
-        if (i < 16) {
-          const int st = i >> 2, db = i & 3;
+        ring[i % kAhead] = opnd(i + kAhead);
+        if (i < 2) {
+          sc[i] = mfma32(a, qf[7], sc[i]);
+        } else if (i < 18) {
+          const int st = (i - 2) >> 2, db = (i - 2) & 3;
           o[db] = mfma32(a, __builtin_bit_cast(bf16x8, pk_prev[st]), o[db]);
         } else {
-          const int st = (i - 16) >> 1, kb = (i - 16) & 1;
+          const int st = (i - 18) >> 1, kb = (i - 18) & 1;
           sn[kb] = mfma32(a, qf[st], sn[kb]);
         }
       } else {
         const int kb = i - 32;
         if (need_ref) sn[kb] = mfma32(one_op, qm, sn[kb]);
       }
-      // vector work on this tile's scores: one exponential per slot, the pack and row-sum step of
-      // a pair in the slot of its second score
-      if (i < 32) {
-        e[i] = __builtin_amdgcn_exp2f(sc[i >> 4][i & 15]);
-        if (i & 1) {
-          const int k = i >> 1;  // pair of scores
-          uint32_t w = pack_bf16(e[i - 1], e[i]);
-          float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
-                                                     part[k & 3], false);
-          // pins the pair's work to this slot: the compiler would otherwise sink it past the
-          // branch around the 9th step, out of the MFMA shadow
-          asm volatile("" : "+v"(w), "+v"(ps));
-          pk_cur[k >> 2][k & 3] = w;
-          part[k & 3] = ps;
+      if (i == 1) {
+        // the buffers these tiles go to were last read before the barrier that opened this
+        // iteration
+        if (v_loader) dma_tile(j, true);
+        else if (j + 2 < n_tiles) dma_tile(j + 2, false);
+        if (pf) {
+          int qt_n, b_n, kvh_n;
+          item_coords(vb_next, qt_n, b_n, kvh_n);
+          dma_q_rows(b_n, kvh_n * G + hg, qt_n * MQ + 32 * qb);
         }
       }
+      // vector work on tile j's scores, from slot 2 on (S_j is complete after slots 0-1)
+      if (i >= 2 && i < 32) soft(i - 2);
       __builtin_amdgcn_sched_barrier(0);
     }
+    soft(30);
+    soft(31);
     float rs = (part[0] + part[1]) + (part[2] + part[3]);
     if (__builtin_amdgcn_ballot_w64(!m_valid || !(rs <= 0x1p64f))) slow_path(sc, sn, pk_cur, rs);
     l_run += rs;
-    (void)more;
     // this iteration's tiles have landed (the q rows issued after them may still be in flight)
     if (pf) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else vm_wait();
@@ -661,12 +675,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   u32x4 pA[4], pB[4];
   qk_all(0, sA);
   __syncthreads();  // K_0's buffer is refilled during iteration 0
-  // iteration 0: no PV yet; QK^T of tile 1 while this tile's weights are formed
+  // iteration 0: no PV yet; QK^T of tile 1 (steps 0-6, step 7 opens iteration 1) while this
+  // tile's weights are formed
   {
     if (v_loader) dma_tile(0, true);
     else if (2 < n_tiles) dma_tile(2, false);
     mask_tile(0, sA);
-    qk_all(1, sB);  // stale keys if n_tiles == 1: discarded
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sB[kb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 7; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sB[kb] = mfma32(rd_k(1, st, kb), qf[st], sB[kb]);
+    if (need_ref) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sB[kb] = mfma32(one_op, qm, sB[kb]);
+    }
+    // stale keys if n_tiles == 1: discarded
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) ring[i] = rd_k(1, 7, i);
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
