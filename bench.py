@@ -190,7 +190,11 @@ def bench_block(torch, zg, si, dev, stream, args):
     # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record (null if the kernels
     # changed since it was taken)
     from global_causal_attention_amd.counters import lookup_traffic
-    grid_prefill = ((T + 63) // 64) * B * HKV * 512     # threads: 64-query tiles x (b, kv head)
+    # threads: 64-query tiles x (b, kv head) workgroups of 512, or one workgroup per CU walking
+    # them when the layer has at least two tiles per CU (the library's persistent launch)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    tiles = ((T + 63) // 64) * B * HKV
+    grid_prefill = (cus if (tiles >= 2 * cus and cus % 8 == 0) else tiles) * 512
     grid_kprep = min((B * T * HKV + 31) // 32, 2048) * 256  # threads: 32 rows per block pass
     parts = [lookup_traffic("prefill_kernel<4, false>", grid_prefill),
              lookup_traffic("kprep_kernel", grid_kprep)]

@@ -239,7 +239,8 @@ uint64_t zg_kv_bytes(int32_t n_layers, int32_t global_every, int32_t n_kv_heads,
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* zg_last_error(void);
 
-/* Measurement helper (not part of the attention path): reads `bytes` (a positive multiple of 16)
+/* Benchmark infrastructure, not part of the attention path (the benchmark uses it for the
+ * streaming-read reference it reports beside the decode and local-layer rates): reads `bytes` (a positive multiple of 16)
  * from the device buffer `src` with streaming non-temporal 16-byte loads over `n_blocks`
  * workgroups of 256 lanes and writes one word per wave to `sink` (device, >= 4 * n_blocks words;
  * its values are meaningless). Timing it gives the device's streaming-read bandwidth, the
