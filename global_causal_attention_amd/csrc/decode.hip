@@ -900,9 +900,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(DecodeParams p
 // Results equal the prep + decode_mfma_kernel pair bit for bit (same operand rounding, same
 // reduction order).
 namespace {
-// RMSNorm + RoPE of one 128-dim row held by 16 lanes (lane c: dims 8c .. 8c + 7), rotated pairs
-// exchanged through the row's 68-float LDS stage. Result in x (fp32).
-__device__ __forceinline__ void norm_rope16(float* x, int c, int pos, const float* w, float eps,
+// RMSNorm + RoPE of one 128-dim row held by 16 lanes (lane c: dims 8c .. 8c + 7, w: the norm
+// weights of those dims), rotated pairs exchanged through the row's 68-float LDS stage. Result in
+// x (fp32).
+__device__ __forceinline__ void norm_rope16(float* x, int c, int pos, const float (&w)[8], float eps,
                                             const RopeTable& rt, float* sr) {
   float ss = 0.f;
 #pragma unroll
@@ -910,7 +911,7 @@ __device__ __forceinline__ void norm_rope16(float* x, int c, int pos, const floa
   ss = row16_sum(ss);
   const float inv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] *= inv * (w ? w[8 * c + j] : 1.0f);
+  for (int j = 0; j < 8; ++j) x[j] *= inv * w[j];
   const int hr = rt.half;
   if (hr > 0) {
     double rev0 = 0.0, rev1 = 0.0;
@@ -967,13 +968,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_ring_kernel(DecodeParams p
 
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
-  const int pos = p.seqlens[b] - 1;
-  if (pos < 0) return;  // a length below 1 is a caller error: touch nothing
   const int W = p.window;
-  const int n = min(pos + 1, W);   // valid slots 0 .. n-1 (positions max(0, pos-W+1) .. pos)
-  const int slot = pos % W;        // the new token's slot
-  const int n_blk = (n + 31) >> 5;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -989,14 +984,30 @@ __global__ __launch_bounds__(kDecThreads) void decode_ring_kernel(DecodeParams p
   unsigned char* wtile = vt + wave * kMfWaveLds;
 
   constexpr int NV = FP8 ? 4 : 8;
+  // every slot below W is read (the ring holds W rows whatever the position), so the loads need
+  // not wait for the sequence length; rows at or past the valid count are zeroed once it is known
+  // The ring holds W rows whatever the position, so the loads need not wait for the sequence
+  // length: a buffer resource spanning slots 0 .. W-1 of this (sequence, KV head) returns zeros
+  // for slots at or past W without a per-lane branch; rows at or past the valid count are zeroed
+  // once the length is known.
   auto load_rows = [&](u32x4 (&vraw)[NV], const unsigned char* base, int blk) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)base, 0, (int)((int64_t)(W - 1) * row_bytes + kHeadDim * EB), 0x00020000);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = 64 * i + lane;
       const int row = FP8 ? (idx >> 3) : (idx >> 4), pc = FP8 ? (idx & 7) : (idx & 15);
       const int key = 32 * blk + row;
-      vraw[i] = key < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)key * row_bytes) + pc)
-                        : u32x4{0u, 0u, 0u, 0u};
+      vraw[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, key * (int)row_bytes + 16 * pc, 0, 2));
+    }
+  };
+  auto zero_past = [&](u32x4 (&vraw)[NV], int blk, int n_valid) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = 64 * i + lane;
+      const int row = FP8 ? (idx >> 3) : (idx >> 4);
+      if (32 * blk + row >= n_valid) vraw[i] = u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto stage_rows = [&](const u32x4 (&vraw)[NV], unsigned char* tile) {
@@ -1019,56 +1030,90 @@ __global__ __launch_bounds__(kDecThreads) void decode_ring_kernel(DecodeParams p
     }
   };
   // the new slot's row (bf16 words in LDS) over its row of this wave's tile, if the slot is here
-  auto put_new_row = [&](const uint32_t* src, unsigned char* tile) {
-    const int r = slot - 32 * wave;
+  auto put_new_row = [&](const uint32_t* src, unsigned char* tile, int new_slot) {
+    const int r = new_slot - 32 * wave;
     if (r >= 0 && r < 32 && lane < 16) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(src + 4 * lane);
       *reinterpret_cast<u32x4*>(tile + r * kMfRow + 16 * (lane ^ mf_swz(r))) = w;
     }
   };
 
-  // ---- 1. cache loads of this wave's slots (the new slot's stale row is replaced below)
-  u32x4 kraw[NV], vraw[NV];
-  if (wave < n_blk) {
-    load_rows(kraw, kc, wave);
-    load_rows(vraw, vc, wave);
+  // ---- 1. every load the workgroup needs goes out first, none waiting on another: the new
+  // token's rows (q: wave 0, k: wave 1 lanes 0..15, v: wave 1 lanes 16..31) and the gate logits of
+  // the output elements this thread writes, then this wave's cache slots (the new slot's stale row
+  // is replaced below), then the sequence length. Loads complete in issue order, so the new rows,
+  // issued first, are normalised while the cache rows are still in flight.
+  const int grp = lane >> 4, c = lane & 15;
+  const bool is_q = wave == 0;
+  u32x4 xnew = u32x4{0u, 0u, 0u, 0u};
+  if (wave == 0 || (wave == 1 && grp < 2)) {
+    const uint16_t* src = is_q ? p.q_new + ((int64_t)b * p.Hq + kvh * G + grp) * kHeadDim
+                        : grp == 0 ? p.k_new + ((int64_t)b * p.Hkv + kvh) * kHeadDim
+                                   : p.v_new + ((int64_t)b * p.Hkv + kvh) * kHeadDim;
+    xnew = *reinterpret_cast<const u32x4*>(src + 8 * c);
   }
+  float wv[8];  // norm weights of this lane's 8 dims of the new q or k row
+  {
+    const float* w = is_q ? p.q_norm_w : p.k_norm_w;
+    if (w) {
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + 8 * c);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + 8 * c + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wv[j] = w0[j];
+        wv[4 + j] = w1[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wv[j] = 1.0f;
+    }
+  }
+  // this thread writes output elements 2 tid and 2 tid + 1 of the group's 4 x 128; their gate
+  // logits come as one word (read from the q rows, of the same shape, when ungated, and unused)
+  static_assert(G * kHeadDim == 2 * kDecThreads, "two output elements per thread");
+  const int64_t out_base = ((int64_t)b * p.Hq + kvh * G) * kHeadDim + 2 * tid;
+  const uint32_t graw = *reinterpret_cast<const uint32_t*>((p.gated ? p.gate : p.q_new) + out_base);
+  u32x4 kraw[NV], vraw[NV];  // waves past the ring's W slots read zeros
+  load_rows(kraw, kc, wave);
+  load_rows(vraw, vc, wave);
+  // A length below 1 is a caller error: the workgroup then computes on position 0 and writes
+  // nothing (no early exit, which would let the compiler sink the loads above behind this read).
+  const int pos_raw = p.seqlens[b] - 1;
+  const bool valid = pos_raw >= 0;
+  const int pos = valid ? pos_raw : 0;
+  const int n = min(pos + 1, W);   // valid slots 0 .. n-1 (positions max(0, pos-W+1) .. pos)
+  const int slot = pos % W;        // the new token's slot
+  const int n_blk = (n + 31) >> 5;
 
   // ---- 2. the new token: q rows (wave 0), k row (wave 1, lanes 0..15), v row (wave 1, 16..31)
   {
-    const int grp = lane >> 4, c = lane & 15;
     if (wave == 0 || (wave == 1 && grp == 0)) {
-      const bool is_q = wave == 0;
-      const int h = is_q ? kvh * G + grp : kvh;
-      const uint16_t* src = is_q ? p.q_new + ((int64_t)b * p.Hq + h) * kHeadDim
-                                 : p.k_new + ((int64_t)b * p.Hkv + h) * kHeadDim;
       float x[8];
-      unpack8(*reinterpret_cast<const u32x4*>(src + 8 * c), x);
-      norm_rope16(x, c, pos, is_q ? p.q_norm_w : p.k_norm_w, p.eps, p.rope,
-                  &stage[is_q ? grp : G][0]);
+      unpack8(xnew, x);
+      norm_rope16(x, c, pos, wv, p.eps, p.rope, &stage[is_q ? grp : G][0]);
       if (is_q) {
         *reinterpret_cast<u32x4*>(&qhs[grp][4 * c]) = pack8(x);
       } else {
         const int64_t off = ((int64_t)b * W + slot) * p.Hkv * kHeadDim + (int64_t)kvh * kHeadDim + 8 * c;
         if (!FP8) {
           const u32x4 w = pack8(x);
-          *reinterpret_cast<u32x4*>(p.k_cache + off) = w;
+          if (valid) *reinterpret_cast<u32x4*>(p.k_cache + off) = w;
           *reinterpret_cast<u32x4*>(&newk[4 * c]) = w;
         } else {
           const float ki = p.k_inv;
           const u32x2 w = {pack4_e4m3(x[0] * ki, x[1] * ki, x[2] * ki, x[3] * ki),
                            pack4_e4m3(x[4] * ki, x[5] * ki, x[6] * ki, x[7] * ki)};
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.k_cache) + off) = w;
+          if (valid) *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.k_cache) + off) = w;
           *reinterpret_cast<u32x4*>(&newk[4 * c]) =
               u32x4{e4m3x2_bf16<false>(w[0]), e4m3x2_bf16<true>(w[0]), e4m3x2_bf16<false>(w[1]),
                     e4m3x2_bf16<true>(w[1])};
         }
       }
     } else if (wave == 1 && grp == 1) {
-      const u32x4 vw = *reinterpret_cast<const u32x4*>(p.v_new + ((int64_t)b * p.Hkv + kvh) * kHeadDim + 8 * c);
+      const u32x4 vw = xnew;
       const int64_t off = ((int64_t)b * W + slot) * p.Hkv * kHeadDim + (int64_t)kvh * kHeadDim + 8 * c;
       if (!FP8) {
-        *reinterpret_cast<u32x4*>(p.v_cache + off) = vw;
+        if (valid) *reinterpret_cast<u32x4*>(p.v_cache + off) = vw;
         *reinterpret_cast<u32x4*>(&newv[4 * c]) = vw;
       } else {
         float vf[8];
@@ -1076,7 +1121,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_ring_kernel(DecodeParams p
         const float vi = p.v_inv;
         const u32x2 w = {pack4_e4m3(vf[0] * vi, vf[1] * vi, vf[2] * vi, vf[3] * vi),
                          pack4_e4m3(vf[4] * vi, vf[5] * vi, vf[6] * vi, vf[7] * vi)};
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.v_cache) + off) = w;
+        if (valid) *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.v_cache) + off) = w;
         *reinterpret_cast<u32x4*>(&newv[4 * c]) =
             u32x4{e4m3x2_bf16<false>(w[0]), e4m3x2_bf16<true>(w[0]), e4m3x2_bf16<false>(w[1]),
                   e4m3x2_bf16<true>(w[1])};
@@ -1091,8 +1136,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_ring_kernel(DecodeParams p
 #pragma unroll
     for (int st = 0; st < 8; ++st)
       qa[st] = l32 < G ? *reinterpret_cast<const bf16x8*>(&qhs[l32][32 * hi + 4 * st]) : zero8;
+    zero_past(kraw, wave, n);
     stage_rows(kraw, wtile);
-    put_new_row(newk, wtile);
+    put_new_row(newk, wtile, slot);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are in LDS
     f32x16 sacc = f32x16{};
 #pragma unroll
@@ -1156,8 +1202,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_ring_kernel(DecodeParams p
         const int row = 8 * x + tr_row;
         tr_off[x][db] = row * kMfRow + 16 * ((4 * db + tr_dch) ^ mf_swz(row)) + 8 * (lane & 1);
       }
+    zero_past(vraw, wave, n);
     stage_rows(vraw, wtile);
-    put_new_row(newv, wtile);
+    put_new_row(newv, wtile, slot);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int st2 = 0; st2 < 2; ++st2) {
@@ -1185,18 +1232,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_ring_kernel(DecodeParams p
   __syncthreads();
 
   const float vs = FP8 ? p.v_scale : 1.0f;
-  for (int i = tid; i < G * kHeadDim; i += kDecThreads) {
-    const int h = i / kHeadDim;
-    const int d = i - h * kHeadDim;
-    const float ov = vs * (red[(0 * G + h) * kHeadDim + d] + red[(1 * G + h) * kHeadDim + d] +
-                           red[(2 * G + h) * kHeadDim + d] + red[(3 * G + h) * kHeadDim + d]);
-    const int head = kvh * G + h;
-    float y = ov / ml[h][1];
-    if (p.gated) {
-      const float g = bf16lo(p.gate[((int64_t)b * p.Hq + head) * kHeadDim + d]);
-      y *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+  {
+    const int h = (2 * tid) / kHeadDim;
+    const int d = 2 * tid - h * kHeadDim;
+    float y[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float ov = vs * (red[(0 * G + h) * kHeadDim + d + e] + red[(1 * G + h) * kHeadDim + d + e] +
+                             red[(2 * G + h) * kHeadDim + d + e] + red[(3 * G + h) * kHeadDim + d + e]);
+      y[e] = ov / ml[h][1];
+      if (p.gated) {
+        const float g = e ? bf16hi(graw) : bf16lo(graw);
+        y[e] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+      }
     }
-    p.out[((int64_t)b * p.Hq + head) * kHeadDim + d] = (uint16_t)(pack_bf16(y, 0.f) & 0xffffu);
+    if (valid) *reinterpret_cast<uint32_t*>(p.out + out_base) = pack_bf16(y[0], y[1]);
   }
 }
 
