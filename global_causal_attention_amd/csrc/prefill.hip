@@ -395,9 +395,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int qbase = r0 + 32 * qb;
   const int k_begin = item_k_begin(r0);
   const int n_tiles = item_n_tiles(r0);
-  // the next item's q rows are brought in during iteration 1 (the register RoPE of 42 dims keeps
-  // the staging rows free of scratch)
-  const bool prefetch_q = p.persist && has_next && n_tiles >= 3 && p.rope.half == 21;
+  // the next item's q rows come into the staging rows as soon as this item's prologue has read
+  // them (the register RoPE of 42 dims keeps the staging rows free of scratch)
+  const bool prefetch_q = p.persist && has_next && p.rope.half == 21;
 
   // ---- tile streaming: waves 0-3 bring K rows, waves 4-7 V rows, straight into chunk-swizzled
   // LDS rows (buffer_load ... lds, 4 rows = 1 KB per instruction, 4 per wave per tile). The
@@ -595,7 +595,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   auto iter = [&](int j, auto par_c, f32x16 (&sc)[2], f32x16 (&sn)[2], u32x4 (&pk_prev)[4],
                   u32x4 (&pk_cur)[4]) {
     constexpr int PAR = decltype(par_c)::value;
-    const bool pf = prefetch_q && j == 1;  // n_tiles >= 3: iteration 2 waits for these rows
     mask_tile(j, sc);
     float e[32];
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -647,11 +646,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         // iteration
         if (v_loader) dma_tile(j, true);
         else if (j + 2 < n_tiles) dma_tile(j + 2, false);
-        if (pf) {
-          int qt_n, b_n, kvh_n;
-          item_coords(vb_next, qt_n, b_n, kvh_n);
-          dma_q_rows(b_n, kvh_n * G + hg, qt_n * MQ + 32 * qb);
-        }
       }
       // vector work on tile j's scores, from slot 2 on (S_j is complete after slots 0-1)
       if (i >= 2 && i < 32) soft(i - 2);
@@ -662,14 +656,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     float rs = (part[0] + part[1]) + (part[2] + part[3]);
     if (__builtin_amdgcn_ballot_w64(!m_valid || !(rs <= 0x1p64f))) slow_path(sc, sn, pk_cur, rs);
     l_run += rs;
-    // this iteration's tiles have landed (the q rows issued after them may still be in flight)
-    if (pf) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else vm_wait();
+    vm_wait();  // this iteration's tiles have landed
     __syncthreads();
   };
 
+  // the next item's raw q rows (the prologue above has read this item's out of the staging rows);
+  // they are the last 8 loads issued, so the preamble waits for everything before them
+  if (prefetch_q) {
+    int qt_n, b_n, kvh_n;
+    item_coords(vb_next, qt_n, b_n, kvh_n);
+    dma_q_rows(b_n, kvh_n * G + hg, qt_n * MQ + 32 * qb);
+  }
+
   // ---- preamble: K_0 and K_1 in LDS, S_0 computed
-  vm_wait();
+  if (prefetch_q) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else vm_wait();
   __syncthreads();
   f32x16 sA[2], sB[2];
   u32x4 pA[4], pB[4];
@@ -727,8 +728,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     item_coords(vb_next, qt_n, b_n, kvh_n);
     const __amdgpu_buffer_rsrc_t rs_n = kv_rsrc(b_n, kvh_n);
     const int kb_n = item_k_begin(qt_n * MQ);
-    dma_tile_at(rs_n, kb_n, 0, false);
-    if (item_n_tiles(qt_n * MQ) > 1) dma_tile_at(rs_n, kb_n, 1, false);
+    // lane offsets recomputed here rather than kept in registers through the tile loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint32_t lds_b = lds_k + 16 * wg * kRow;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t == 0 || item_n_tiles(qt_n * MQ) > 1) {
+        const uint32_t row0 = (uint32_t)(kb_n + t * kNk + 16 * wg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * i + (ln >> 4);
+          const uint32_t voff = (uint32_t)((ln >> 4) * row_bytes + 16 * ((ln & 15) ^ swz(row)));
+          lds_dma16(lds_b + t * kTileBytes + 4 * i * kRow, voff, rs_n, (row0 + 4 * i) * (uint32_t)row_bytes);
+        }
+      }
+    }
   }
   // PV of the last tile (its weights are in the set written last)
   {
