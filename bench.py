@@ -370,8 +370,18 @@ def bench_decode(torch, zg, si, dev, stream, reps):
     return res
 
 
+_BUSY = {}
+
+
 def _time(torch, stream, fn, reps, warm=1):
-    """Median of `reps` timed calls (HIP events on the launch stream) after `warm` untimed ones."""
+    """Median of `reps` timed calls (HIP events on the launch stream) after `warm` untimed ones.
+    Before each call the stream is kept busy by a 1 GiB device fill (about 0.2 ms), so the host
+    has enqueued the call's launches before the start event executes: the interval holds the
+    call's GPU work only, not the host's launch latency (which would dominate calls of ~0.1 ms).
+    The fill also leaves the caches cold, as in the decode timings."""
+    busy = _BUSY.get(stream.device)
+    if busy is None:
+        busy = _BUSY[stream.device] = torch.empty(1 << 30, dtype=torch.uint8, device=stream.device)
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
@@ -379,6 +389,7 @@ def _time(torch, stream, fn, reps, warm=1):
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        busy.fill_(1)
         e0.record(stream)
         fn()
         e1.record(stream)

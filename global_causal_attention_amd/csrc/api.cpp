@@ -268,6 +268,12 @@ zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, co
     kp.out_rows = T;
     kp.eps = cfg->rms_eps;
     kp.rope = rt;
+    // the same kernel choice as a plain prefill: local layers of 4 heads per KV head run the banded
+    // streaming kernel on folded keys, everything else the general tiled kernel
+    const int window = cfg->window >= T ? 0 : cfg->window;  // a window covering T is causal
+    const bool swa = zg::prefill_uses_swa(window, 4, rt.half);
+    kp.fold = swa ? 1 : 0;
+    kp.fold_scale = scale_log2(cfg);
     st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
     if (st != ZG_OK) return st;
     zg::PrefillParams pp{};
@@ -284,7 +290,7 @@ zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, co
     pp.T = T;
     pp.Hq = (int32_t)Hq;
     pp.Hkv = (int32_t)Hkv;
-    pp.window = cfg->window >= T ? 0 : cfg->window;
+    pp.window = window;
     pp.n_qtiles = (T + 63) / 64;
     pp.kv_rows = T;
     pp.n_keys = T;
@@ -292,7 +298,8 @@ zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, co
     pp.eps = cfg->rms_eps;
     pp.scale_log2 = scale_log2(cfg);
     pp.rope = rt;
-    return hip_status(zg::launch_prefill_general(pp, 4, cfg->gated != 0, hs), "prefill launch");
+    if (swa) pp.seg_steps = swa_seg_steps(B, T, Hkv);
+    return hip_status(zg::launch_prefill(pp, 4, cfg->gated != 0, hs), "prefill launch");
   } catch (...) {
     return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_forward_train");
   }

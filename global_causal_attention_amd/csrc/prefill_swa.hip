@@ -396,6 +396,11 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillParams p) 
       // (a gate of 0 then gives exactly half the ungated output: rcp(2 l) = rcp(l) / 2)
       const float rcp_l = __builtin_amdgcn_rcpf(l_tot);
       const bool store = my_q < T;
+      // the row's natural-log log-sum-exp for the backward pass: the weights are exp2 of
+      // inv_q * (s - mu), so log2 of the row's sum of exp2(inv_q * s) is inv_q * mu + log2(l)
+      if (p.lse && hi == 0 && store)
+        p.lse[((int64_t)b * T + my_q) * p.Hq + head] =
+            (inv_q * mu + __log2f(l_tot)) * 0.6931471805599453f;
       uint16_t* dst = p.out + ((int64_t)b * T + min(my_q, T - 1)) * p.so + (int64_t)head * kHeadDim;
       if (GATED) {
         // chunks -> output layout: dims 8c + 4 hi .. + 3 of chunk c in half (c & 1) of gch[c / 2]

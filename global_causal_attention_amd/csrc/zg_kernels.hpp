@@ -55,8 +55,8 @@ struct PrefillParams {
   // Plain prefill: kv_rows = n_keys = T, qoff = 0.
   int64_t kv_rows;
   int32_t n_keys, qoff;
-  // optional [B, T, Hq] fp32: natural-log log-sum-exp of each query row's scaled scores (general
-  // kernel only; the backward pass recomputes the softmax from it)
+  // optional [B, T, Hq] fp32: natural-log log-sum-exp of each query row's scaled scores (plain
+  // prefill with qoff = 0; the backward pass recomputes the softmax from it)
   float* lse;
   float eps;
   float scale_log2;  // softmax scale * log2(e)
