@@ -448,41 +448,70 @@ def bench_stack(torch, zg, si, dev, stream, n_layers=32, Ts=65536, hidden=4096):
     ws = torch.empty(max(zg.zg_attn_layer_workspace_bytes(c, 1, Ts) for c in cfgs.values()),
                      dtype=torch.uint8, device=dev)
 
-    def one_pass(evs=None):
-        for i, (g, wqkvg, wo) in enumerate(layers):
-            zg.zg_attn_layer(cfgs[g], x, wqkvg, wo, workspace=ws)
-            if evs is not None:
-                evs[i + 1].record(stream)
+    def timed(run_layer):
+        """One untimed pass, then five timed ones: (fastest total, its per-layer ms, median)."""
+        def one_pass(evs=None):
+            for i, lay in enumerate(layers):
+                run_layer(lay)
+                if evs is not None:
+                    evs[i + 1].record(stream)
 
-    one_pass()
-    torch.cuda.synchronize()
-    runs = []
-    for _ in range(5):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
-        evs[0].record(stream)
-        one_pass(evs)
+        one_pass()
         torch.cuda.synchronize()
-        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n_layers)]
-        runs.append((sum(per), per))
-    runs.sort(key=lambda r: r[0])
-    total, per = runs[0]
-    median_ms = runs[len(runs) // 2][0]
+        runs = []
+        for _ in range(5):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
+            evs[0].record(stream)
+            one_pass(evs)
+            torch.cuda.synchronize()
+            per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n_layers)]
+            runs.append((sum(per), per))
+        runs.sort(key=lambda r: r[0])
+        return runs[0][0], runs[0][1], runs[len(runs) // 2][0]
+
+    total, per, median_ms = timed(lambda lay: zg.zg_attn_layer(cfgs[lay[0]], x, lay[1], lay[2],
+                                                               workspace=ws))
     n_glob = sum(1 for g, _, _ in layers if g)
     t_glob = sum(p for p, (g, _, _) in zip(per, layers) if g)
     t_loc = total - t_glob
     # useful FLOP: projections (2 per weight per token) + attention (4*D per (head, key) pair)
     proj = sum(2 * Ts * (wqkvg.numel() + wo.numel()) for _, wqkvg, wo in layers)
     att = sum(HQ * n_pairs(Ts, 0 if g else W) * 4 * D for g, _, _ in layers)
-    del layers, ws, x
-    return {"workload": f"B=1, T={Ts}, hidden {hidden}, {n_layers} layers ({n_glob} global), "
-                        f"N(0, 0.02) bf16 weights, fp32 residual, base 1e7",
-            "ms": round(total, 2), "ms_median_of_5": round(median_ms, 2),
-            "tokens_per_s": round(Ts / (total * 1e-3), 1),
-            "useful_flop": proj + att,
-            "TFLOPs_useful": round((proj + att) / (total * 1e-3) / 1e12, 1),
-            "mfma_frac": round((proj + att) / (total * 1e-3) / MFMA_BF16_PEAK, 4),
-            "local_layer_ms": round(t_loc / (n_layers - n_glob), 3),
-            "global_layer_ms": round(t_glob / n_glob, 3)}
+    res = {"workload": f"B=1, T={Ts}, hidden {hidden}, {n_layers} layers ({n_glob} global), "
+                       f"N(0, 0.02) bf16 weights, fp32 residual, base 1e7",
+           "ms": round(total, 2), "ms_median_of_5": round(median_ms, 2),
+           "tokens_per_s": round(Ts / (total * 1e-3), 1),
+           "useful_flop": proj + att,
+           "TFLOPs_useful": round((proj + att) / (total * 1e-3) / 1e12, 1),
+           "mfma_frac": round((proj + att) / (total * 1e-3) / MFMA_BF16_PEAK, 4),
+           "local_layer_ms": round(t_loc / (n_layers - n_glob), 3),
+           "global_layer_ms": round(t_glob / n_glob, 3)}
+
+    # the same layers with E4M3 projections: weights quantized per output row once (untimed);
+    # inside each layer the hidden state and the attention output are quantized per row
+    log("[bench] stack with E4M3 projections")
+    layers8 = []
+    for g, wqkvg, wo in layers:
+        cq, sq = zg.zg_quant_rows_fp8(wqkvg)
+        co, so = zg.zg_quant_rows_fp8(wo)
+        layers8.append((g, cq, sq, co, so))
+    del ws
+    ws8 = torch.empty(max(zg.zg_attn_layer_fp8_workspace_bytes(c, 1, Ts) for c in cfgs.values()),
+                      dtype=torch.uint8, device=dev)
+    lay8 = {id(l): l8 for l, l8 in zip(layers, layers8)}
+    total8, per8, median8 = timed(lambda lay: zg.zg_attn_layer_fp8(
+        cfgs[lay[0]], x, *lay8[id(lay)][1:], workspace=ws8))
+    t_glob8 = sum(p for p, (g, _, _) in zip(per8, layers) if g)
+    res["e4m3_projections"] = {
+        "ms": round(total8, 2), "ms_median_of_5": round(median8, 2),
+        "tokens_per_s": round(Ts / (total8 * 1e-3), 1),
+        "speedup_vs_bf16": round(total / total8, 3),
+        "local_layer_ms": round((total8 - t_glob8) / (n_layers - n_glob), 3),
+        "global_layer_ms": round(t_glob8 / n_glob, 3),
+        "note": "projections on E4M3 operands (per-row scales, fp32 accumulation), attention bf16"}
+    log(f"[bench] stack: bf16 {total:.1f} ms, E4M3 projections {total8:.1f} ms")
+    del layers, layers8, ws8, x
+    return res
 
 
 def bench_chunked(torch, zg, si, dev, stream, Bc=4, ctx=16384, Tc=2048):

@@ -21,8 +21,10 @@ __all__ = ["AttnConfig", "ZGError", "zg_attn_prefill", "zg_attn_prefill_cached",
            "zg_hbm_read_probe", "zg_attn_decode", "zg_attn_decode_noalloc", "zg_attn_decode_fp8",
            "zg_kv_to_fp8", "zg_kv_bytes",
            "zg_attn_prefill_workspace_bytes", "zg_attn_decode_workspace_bytes", "zg_rmsnorm",
-           "zg_gemm_bf16", "zg_attn_layer", "zg_attn_layer_workspace_bytes", "zg_last_error",
-           "load_library", "LIB_PATH", "EXPORTS"]
+           "zg_gemm_bf16", "zg_attn_layer", "zg_attn_layer_workspace_bytes", "zg_rmsnorm_fp8",
+           "zg_quant_rows_fp8", "zg_gemm_fp8", "zg_attn_layer_fp8",
+           "zg_attn_layer_fp8_workspace_bytes", "zg_last_error", "load_library", "LIB_PATH",
+           "EXPORTS"]
 
 
 class ZGError(RuntimeError):
@@ -549,4 +551,123 @@ def zg_attn_layer(cfg: AttnConfig, x, w_qkvg, w_o, *, q_norm_w=None, k_norm_w=No
     _check(load_library().zg_attn_layer(
         ctypes.byref(c), B, T, _ptr(x), _ptr(w_qkvg), _ptr(w_o), _ptr(q_norm_w), _ptr(k_norm_w),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return x
+
+
+# ---- E4M3 projections: codes as torch.uint8, one fp32 scale per row ----
+
+def zg_rmsnorm_fp8(x, eps=1e-6, w=None, out=None, scale=None, stream=None):
+    """E4M3 rows of RMSNorm(x) * w (x fp32 [..., dim]): returns (codes uint8 [..., dim],
+    scale fp32 [rows]); row r stands for decode(codes[r]) * scale[r]."""
+    import torch
+    dim = x.shape[-1]
+    rows = x.numel() // dim
+    _shape(w, "w", (dim,))
+    _shape(out, "out", x.shape)
+    _shape(scale, "scale", (rows,))
+    _need(x, "x", torch.float32)
+    if not x.is_contiguous() or (w is not None and not w.is_contiguous()):
+        raise ValueError("x and w must be contiguous")
+    if w is not None:
+        _need(w, "w", torch.float32)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.uint8)
+    _need(scale, "scale", torch.float32)
+    _check(load_library().zg_rmsnorm_fp8(rows, dim, _ptr(x), _ptr(w), float(eps), _ptr(out),
+                                         _ptr(scale), _stream(stream)))
+    return out, scale
+
+
+def zg_quant_rows_fp8(x, out=None, scale=None, stream=None):
+    """E4M3 rows of the bf16 matrix x [rows, dim] (rows may be strided, elements dense): returns
+    (codes uint8 [rows, dim], scale fp32 [rows])."""
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError(f"x must be a 2-D [rows, dim] view with dense rows, got shape {tuple(x.shape)}")
+    rows, dim = x.shape
+    _shape(out, "out", (rows, dim))
+    _shape(scale, "scale", (rows,))
+    _need(x, "x", torch.bfloat16)
+    if out is None:
+        out = torch.empty((rows, dim), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.uint8)
+    _need(scale, "scale", torch.float32)
+    _check(load_library().zg_quant_rows_fp8(rows, dim, _ptr(x), x.stride(0), _ptr(out), _ptr(scale),
+                                            _stream(stream)))
+    return out, scale
+
+
+def zg_gemm_fp8(x, x_scale, w, w_scale, residual=None, y=None, want_y=True, stream=None):
+    """Y = diag(x_scale) X W^T diag(w_scale) for E4M3 codes X [M, K], W [N, K] (fp32 accumulate);
+    residual (fp32) += Y if given; y = bf16(Y) if want_y."""
+    import torch
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError(f"x [M, K] and w [N, K] must be 2-D, got {tuple(x.shape)} and {tuple(w.shape)}")
+    M, K = x.shape
+    N = w.shape[0]
+    _shape(w, "w", (N, K))
+    _shape(x_scale, "x_scale", (M,))
+    _shape(w_scale, "w_scale", (N,))
+    _shape(residual, "residual", (M, N))
+    _shape(y, "y", (M, N))
+    _need(x, "x", torch.uint8)
+    _need(w, "w", torch.uint8)
+    _need(x_scale, "x_scale", torch.float32)
+    _need(w_scale, "w_scale", torch.float32)
+    for t, n in ((x, "x"), (w, "w"), (x_scale, "x_scale"), (w_scale, "w_scale"),
+                 (residual, "residual"), (y, "y")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if residual is not None:
+        _need(residual, "residual", torch.float32)
+    if want_y and y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().zg_gemm_fp8(M, N, K, _ptr(x), _ptr(x_scale), _ptr(w), _ptr(w_scale),
+                                      _ptr(residual), _ptr(y if want_y else None), N,
+                                      _stream(stream)))
+    return y if want_y else residual
+
+
+def zg_attn_layer_fp8_workspace_bytes(cfg: AttnConfig, B: int, T: int) -> int:
+    c = cfg.c()
+    return load_library().zg_attn_layer_fp8_workspace_bytes(ctypes.byref(c), B, T)
+
+
+def zg_attn_layer_fp8(cfg: AttnConfig, x, w_qkvg, s_qkvg, w_o, s_o, *, q_norm_w=None,
+                      k_norm_w=None, workspace=None, stream=None):
+    """zg_attn_layer with E4M3 projections (weights as codes + per-row scales, e.g. from
+    zg_quant_rows_fp8 of the bf16 weights); x (fp32 [B, T, hidden]) is updated in place."""
+    import torch
+    if x.dim() != 3:
+        raise ValueError(f"x must be 3-D [B, T, hidden], got shape {tuple(x.shape)}")
+    B, T, hidden = x.shape
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    n_qkvg = (Hq + 2 * Hkv + (Hq if cfg.gated else 0)) * D
+    _shape(x, "x", (B, T, Hq * D))
+    _shape(w_qkvg, "w_qkvg", (n_qkvg, hidden))
+    _shape(s_qkvg, "s_qkvg", (n_qkvg,))
+    _shape(w_o, "w_o", (hidden, Hq * D))
+    _shape(s_o, "s_o", (hidden,))
+    _need(x, "x", torch.float32)
+    _need(w_qkvg, "w_qkvg", torch.uint8)
+    _need(w_o, "w_o", torch.uint8)
+    _need(s_qkvg, "s_qkvg", torch.float32)
+    _need(s_o, "s_o", torch.float32)
+    for t, n in ((x, "x"), (w_qkvg, "w_qkvg"), (w_o, "w_o"), (s_qkvg, "s_qkvg"), (s_o, "s_o")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    _norm_weights(q_norm_w, k_norm_w, D)
+    need = zg_attn_layer_fp8_workspace_bytes(cfg, B, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    c = cfg.c()
+    _check(load_library().zg_attn_layer_fp8(
+        ctypes.byref(c), B, T, _ptr(x), _ptr(w_qkvg), _ptr(s_qkvg), _ptr(w_o), _ptr(s_o),
+        _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return x

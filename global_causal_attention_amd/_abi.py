@@ -56,6 +56,12 @@ EXPORTS = {
     "zg_gemm_bf16": (ctypes.c_int, [_I64, _I32, _I32, _P, _P, _P, _P, _I64, _P]),
     "zg_attn_layer_workspace_bytes": (_SZ, [_CFG, _I32, _I32]),
     "zg_attn_layer": (ctypes.c_int, [_CFG, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "zg_rmsnorm_fp8": (ctypes.c_int, [_I64, _I32, _P, _P, _F32, _P, _P, _P]),
+    "zg_quant_rows_fp8": (ctypes.c_int, [_I64, _I32, _P, _I64, _P, _P, _P]),
+    "zg_gemm_fp8": (ctypes.c_int, [_I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, _P]),
+    "zg_attn_layer_fp8_workspace_bytes": (_SZ, [_CFG, _I32, _I32]),
+    "zg_attn_layer_fp8": (ctypes.c_int, [_CFG, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                         _P]),
 }
 
 _lib = None

@@ -826,4 +826,107 @@ zg_status zg_attn_layer(const zg_attn_cfg* cfg, int32_t B, int32_t T, float* x,
   return zg_gemm_bf16(bt, (int32_t)hidden, (int32_t)hidden, h, w_o, x, nullptr, 0, stream);
 }
 
+
+// ---- E4M3 projections ----
+static zg_status check_rows_fp8(int64_t rows, int32_t dim) {
+  if (rows < 1 || rows >= (int64_t(1) << 31) || dim < 16 || dim > 8192 || dim % 16 != 0)
+    return fail(ZG_ERR_SHAPE, "rows=%lld dim=%d: need rows >= 1, dim %% 16 == 0, 16 <= dim <= 8192",
+                (long long)rows, dim);
+  return ZG_OK;
+}
+
+zg_status zg_rmsnorm_fp8(int64_t rows, int32_t dim, const float* x, const float* w, float eps,
+                         void* y_fp8, float* y_scale, void* stream) {
+  if (!x || !y_fp8 || !y_scale) return fail(ZG_ERR_NULL, "x, y and y_scale must be non-NULL");
+  zg_status st = check_rows_fp8(rows, dim);
+  if (st != ZG_OK) return st;
+  if (!(eps >= 0.f)) return fail(ZG_ERR_SHAPE, "eps must be >= 0");
+  if (!aligned16(x) || !aligned16(y_fp8) || !aligned16(y_scale))
+    return fail(ZG_ERR_SHAPE, "pointers must be 16-byte aligned");
+  zg::RmsNormFp8Params p{x, w, static_cast<uint8_t*>(y_fp8), y_scale, rows, dim, eps};
+  return hip_status(zg::launch_rmsnorm_fp8(p, reinterpret_cast<hipStream_t>(stream)), "rmsnorm_fp8 launch");
+}
+
+zg_status zg_quant_rows_fp8(int64_t rows, int32_t dim, const void* x_bf16, int64_t ldx,
+                            void* y_fp8, float* y_scale, void* stream) {
+  if (!x_bf16 || !y_fp8 || !y_scale) return fail(ZG_ERR_NULL, "x, y and y_scale must be non-NULL");
+  zg_status st = check_rows_fp8(rows, dim);
+  if (st != ZG_OK) return st;
+  if (ldx < dim || ldx % 8 != 0) return fail(ZG_ERR_SHAPE, "ldx=%lld must be >= dim and a multiple of 8", (long long)ldx);
+  if (!aligned16(x_bf16) || !aligned16(y_fp8) || !aligned16(y_scale))
+    return fail(ZG_ERR_SHAPE, "pointers must be 16-byte aligned");
+  zg::QuantRowsParams p{static_cast<const uint16_t*>(x_bf16), ldx, static_cast<uint8_t*>(y_fp8),
+                        y_scale, rows, dim};
+  return hip_status(zg::launch_quant_rows(p, reinterpret_cast<hipStream_t>(stream)), "quant_rows launch");
+}
+
+zg_status zg_gemm_fp8(int64_t M, int32_t N, int32_t K, const void* x_fp8, const float* x_scale,
+                      const void* w_fp8, const float* w_scale, float* residual, void* y_bf16,
+                      int64_t ldy, void* stream) {
+  if (!x_fp8 || !x_scale || !w_fp8 || !w_scale)
+    return fail(ZG_ERR_NULL, "x, x_scale, w and w_scale must be non-NULL");
+  if (!residual && !y_bf16) return fail(ZG_ERR_NULL, "one of residual / y must be non-NULL");
+  if (M < 1 || N < 8 || K < 128 || K % 128 != 0 || N % 8 != 0)
+    return fail(ZG_ERR_SHAPE, "M=%lld N=%d K=%d: need M >= 1, N %% 8 == 0, K %% 128 == 0",
+                (long long)M, N, K);
+  if (y_bf16 && ldy < N) return fail(ZG_ERR_SHAPE, "ldy=%lld < N=%d", (long long)ldy, N);
+  if (K > (1 << 20) || ((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31))
+    return fail(ZG_ERR_SHAPE, "problem too large (K <= 2^20, fewer than 2^31 tiles of 256 x 256)");
+  if (!aligned16(x_fp8) || !aligned16(w_fp8)) return fail(ZG_ERR_SHAPE, "x and w must be 16-byte aligned");
+  zg::GemmFp8Params p{static_cast<const uint8_t*>(x_fp8), x_scale, static_cast<const uint8_t*>(w_fp8),
+                      w_scale, residual, static_cast<uint16_t*>(y_bf16), ldy, M, N, K};
+  return hip_status(zg::launch_gemm_fp8(p, reinterpret_cast<hipStream_t>(stream)), "gemm_fp8 launch");
+}
+
+size_t zg_attn_layer_fp8_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
+  if (!cfg || B < 1 || T < 1 || cfg->n_q_heads < 1 || cfg->n_kv_heads < 1) return 0;
+  const size_t bt = (size_t)B * T;
+  const size_t hidden = (size_t)cfg->n_q_heads * kD;
+  const size_t nqkvg = (size_t)(cfg->n_q_heads + 2 * cfg->n_kv_heads + (cfg->gated ? cfg->n_q_heads : 0)) * kD;
+  return align256(bt * hidden) + align256(bt * 4) + align256(bt * nqkvg * 2) +
+         align256(bt * hidden * 2) + zg_attn_prefill_workspace_bytes(cfg, B, T);
+}
+
+zg_status zg_attn_layer_fp8(const zg_attn_cfg* cfg, int32_t B, int32_t T, float* x,
+                            const void* w_qkvg_fp8, const float* s_qkvg, const void* w_o_fp8,
+                            const float* s_o, const float* q_norm_w, const float* k_norm_w,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  zg_status st = check_cfg(cfg);
+  if (st != ZG_OK) return st;
+  if (!x || !w_qkvg_fp8 || !s_qkvg || !w_o_fp8 || !s_o)
+    return fail(ZG_ERR_NULL, "x, w_qkvg, s_qkvg, w_o and s_o must be non-NULL");
+  if (B < 1 || T < 1) return fail(ZG_ERR_SHAPE, "B=%d T=%d must be >= 1", B, T);
+  const size_t need = zg_attn_layer_fp8_workspace_bytes(cfg, B, T);
+  if (!workspace || workspace_bytes < need)
+    return fail(ZG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, need);
+  const int64_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+  const int64_t hidden = Hq * kD;
+  const int64_t nqkvg = (Hq + 2 * Hkv + (cfg->gated ? Hq : 0)) * kD;
+  const int64_t bt = (int64_t)B * T;
+  char* ws = static_cast<char*>(workspace);
+  void* hq = ws;                                         // E4M3 [bt, hidden]: h, then attn out
+  float* sx = reinterpret_cast<float*>(ws + align256(bt * hidden));  // their row scales
+  char* ws2 = ws + align256(bt * hidden) + align256(bt * 4);
+  void* qkvg = ws2;                                      // bf16 [bt, nqkvg]
+  void* attn = ws2 + align256(bt * nqkvg * 2);           // bf16 [bt, hidden]
+  void* kws = ws2 + align256(bt * nqkvg * 2) + align256(bt * hidden * 2);
+  const size_t kws_bytes = zg_attn_prefill_workspace_bytes(cfg, B, T);
+
+  st = zg_rmsnorm_fp8(bt, (int32_t)hidden, x, nullptr, cfg->rms_eps, hq, sx, stream);
+  if (st != ZG_OK) return st;
+  st = zg_gemm_fp8(bt, (int32_t)nqkvg, (int32_t)hidden, hq, sx, w_qkvg_fp8, s_qkvg, nullptr, qkvg,
+                   nqkvg, stream);
+  if (st != ZG_OK) return st;
+  const uint16_t* base = static_cast<const uint16_t*>(qkvg);
+  zg_token_strides s{nqkvg, nqkvg, nqkvg, nqkvg, hidden};
+  st = zg_attn_prefill(cfg, B, T, 0, base, base + Hq * kD, base + (Hq + Hkv) * kD,
+                       cfg->gated ? base + (Hq + 2 * Hkv) * kD : nullptr, q_norm_w, k_norm_w, &s,
+                       attn, kws, kws_bytes, stream);
+  if (st != ZG_OK) return st;
+  st = zg_quant_rows_fp8(bt, (int32_t)hidden, attn, hidden, hq, sx, stream);
+  if (st != ZG_OK) return st;
+  return zg_gemm_fp8(bt, (int32_t)hidden, (int32_t)hidden, hq, sx, w_o_fp8, s_o, x, nullptr, 0, stream);
+}
+
 }  // extern "C"

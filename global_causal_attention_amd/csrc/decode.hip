@@ -28,15 +28,7 @@ __device__ __forceinline__ int64_t n_valid_rows(int pos, int window) {
   return window > 0 ? (int64_t)min(pos + 1, window) : (int64_t)pos + 1;
 }
 
-// E4M3 (OCP 8-bit float, 4 exponent bits, 3 mantissa bits, largest finite 448): sixteen floats
-// times `inv` rounded to nearest-even E4M3, saturated to +-448 first (the conversion itself turns
-// values beyond the range into NaN), packed in element order.
-__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.f, 448.f),
-                                                     __builtin_amdgcn_fmed3f(b, -448.f, 448.f), 0u, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, -448.f, 448.f),
-                                         __builtin_amdgcn_fmed3f(d, -448.f, 448.f), w, true);
-}
+// Sixteen floats times `inv` as E4M3 codes (pack4_e4m3), packed in element order.
 __device__ __forceinline__ u32x4 pack16_e4m3(const float* x, float inv) {
   u32x4 w;
 #pragma unroll

@@ -182,4 +182,14 @@ __device__ __forceinline__ void norm_rope_row_scalar_w(float* x, int half, const
   }
 }
 
+// E4M3 (OCP 8-bit float: 4 exponent bits, bias 7, 3 mantissa bits, largest finite 448): four
+// floats rounded to nearest-even E4M3 codes, saturated to +-448 first (the conversion itself turns
+// values beyond the range into NaN), packed in element order.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.f, 448.f),
+                                                     __builtin_amdgcn_fmed3f(b, -448.f, 448.f), 0u, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, -448.f, 448.f),
+                                         __builtin_amdgcn_fmed3f(d, -448.f, 448.f), w, true);
+}
+
 }  // namespace zg

@@ -142,6 +142,38 @@ struct GemmParams {
   int32_t N, K;
 };
 
+// E4M3 rows with one fp32 scale per row: row r stands for decode(code[r, :]) * scale[r].
+// Quantization of a row h: scale = amax / 448, codes = E4M3(h * (448 / amax)) (both factors
+// rounded to fp32 once); a row of zeros gets scale 1 and zero codes.
+struct RmsNormFp8Params {   // y = E4M3 rows of RMSNorm(x) * w (x fp32)
+  const float* x;
+  const float* w;
+  uint8_t* y;
+  float* y_scale;
+  int64_t rows;
+  int32_t dim;
+  float eps;
+};
+struct QuantRowsParams {    // y = E4M3 rows of x (bf16, row stride ldx)
+  const uint16_t* x;
+  int64_t ldx;
+  uint8_t* y;
+  float* y_scale;
+  int64_t rows;
+  int32_t dim;
+};
+struct GemmFp8Params {      // Y[m, n] = x_scale[m] w_scale[n] sum_k X[m, k] W[n, k]
+  const uint8_t* x;   // [M, K] E4M3
+  const float* x_scale;
+  const uint8_t* w;   // [N, K] E4M3
+  const float* w_scale;
+  float* residual;    // [M, N] or null: += Y
+  uint16_t* y;        // [M, ldy] or null: bf16(Y)
+  int64_t ldy;
+  int64_t M;
+  int32_t N, K;
+};
+
 // Row copies between token-major [B, rows, Hkv, 128] buffers (caches, staging): row j of
 // sequence b goes from src row src_row0 + j to dst row dst_row0 + j; a side whose ring > 0 takes
 // its row index modulo ring (a ring cache's slot).
@@ -185,5 +217,8 @@ constexpr size_t kDecodeScratchBytes = size_t(96) << 20;
 hipError_t decode_scratch_ptr(void** out);
 hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+hipError_t launch_rmsnorm_fp8(const RmsNormFp8Params& p, hipStream_t s);
+hipError_t launch_quant_rows(const QuantRowsParams& p, hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmFp8Params& p, hipStream_t s);
 
 }  // namespace zg

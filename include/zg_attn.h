@@ -279,6 +279,47 @@ zg_status zg_attn_layer(const zg_attn_cfg* cfg, int32_t B, int32_t T, float* x,
                         const float* k_norm_w, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * E4M3 projections (zh-TW translation, section 3.1: the model's matrix multiplications run in FP8
+ * with the E4M3 format on the forward pass). An E4M3 row matrix [rows, dim] (OCP E4M3: 4 exponent
+ * bits, bias 7, 3 mantissa bits, largest finite 448; one byte per element, row stride dim) comes
+ * with one fp32 scale per row, and row r stands for decode(code[r, :]) * scale[r]. Quantizing a
+ * row h: amax = max |h|; scale = amax / 448 and codes = E4M3(h * (448 / amax)), each factor an
+ * fp32 division rounded once, the codes rounded to nearest-even from the fp32 product and
+ * saturated at +-448; a row of zeros gets scale 1 and zero codes.
+ *
+ * zg_rmsnorm_fp8: E4M3 rows of h = (x[r,:] / sqrt(mean(x[r,:]^2) + eps)) * (w ? w : 1), h in fp32.
+ *   x: fp32 [rows, dim]; w: fp32 [dim] or NULL; y: [rows, dim] E4M3; y_scale: fp32 [rows].
+ * zg_quant_rows_fp8: E4M3 rows of the bf16 rows x (row stride ldx >= dim, ldx % 8 == 0).
+ *   Both: dim % 16 == 0, 16 <= dim <= 8192, rows >= 1; pointers 16-byte aligned. */
+zg_status zg_rmsnorm_fp8(int64_t rows, int32_t dim, const float* x, const float* w, float eps,
+                         void* y_fp8, float* y_scale, void* stream);
+zg_status zg_quant_rows_fp8(int64_t rows, int32_t dim, const void* x_bf16, int64_t ldx,
+                            void* y_fp8, float* y_scale, void* stream);
+
+/* zg_gemm_fp8: Y[m, n] = x_scale[m] * w_scale[n] * sum_k X[m, k] * W[n, k], fp32 accumulation
+ * of the exact E4M3 products.
+ *   X: E4M3 [M, K] with x_scale fp32 [M]; W: E4M3 [N, K] with w_scale fp32 [N].
+ *   If residual != NULL: residual[m, n] += Y[m, n] (fp32 [M, N], row stride N).
+ *   If y != NULL:        y[m, n] = bf16(Y[m, n]) (bf16, row stride ldy >= N).
+ *   At least one of residual / y must be non-NULL. K % 128 == 0, N % 8 == 0, M >= 1. */
+zg_status zg_gemm_fp8(int64_t M, int32_t N, int32_t K, const void* x_fp8, const float* x_scale,
+                      const void* w_fp8, const float* w_scale, float* residual, void* y_bf16,
+                      int64_t ldy, void* stream);
+
+/* zg_attn_layer_fp8: zg_attn_layer with E4M3 projections: h = E4M3 rows of RMSNorm(x);
+ * [q, k, v, gate] = bf16(h W_qkvg^T); the attention as zg_attn_prefill; its bf16 output a as E4M3
+ * rows; x += a W_o^T (fp32).
+ *   w_qkvg: E4M3 [(Hq + 2*Hkv + (gated ? Hq : 0)) * D, hidden] with s_qkvg fp32 [rows];
+ *   w_o: E4M3 [hidden, Hq*D] with s_o fp32 [hidden] (zg_quant_rows_fp8 of the bf16 weights gives
+ *   both). workspace >= zg_attn_layer_fp8_workspace_bytes(cfg, B, T). */
+size_t zg_attn_layer_fp8_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T);
+
+zg_status zg_attn_layer_fp8(const zg_attn_cfg* cfg, int32_t B, int32_t T, float* x,
+                            const void* w_qkvg_fp8, const float* s_qkvg, const void* w_o_fp8,
+                            const float* s_o, const float* q_norm_w, const float* k_norm_w,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

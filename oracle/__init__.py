@@ -16,7 +16,8 @@ for Math and Agentic Search"):
 * English explainer page (paperglide.net): Fig. 3 and Fig. 4 captions, and the toy KV-entry count
   (window 4, 8 tokens, 4 SWA + 1 global layers: 24 vs 40 entries).
 * FP8: the E4M3 format the pages train their forward matrix multiplications in (zh-TW page §3.1,
-  hyper-parameters), used here for the decode KV cache (``fp8.py``).
+  hyper-parameters), used here for the decode KV cache (``fp8.py``) and the layer's projections
+  (``fp8_stack.py``).
 
 Parity status per function is listed in each module's header.
 """
@@ -26,11 +27,14 @@ from .kv import kv_bytes, kv_entries, is_global_layer, global_layers
 from .stack import stack_layer, stack_layer_rows, stack, layer_is_global
 from .fp8 import e4m3_values, round_e4m3, decode_fp8_cache
 from .backward import layer_backward, layer_backward_rows, row_lse
+from .fp8_stack import (e4m3_decode, quant_rows_e4m3, gemm_e4m3, quantize_layer_weights,
+                        stack_layer_fp8, stack_layer_rows_fp8, stack_fp8)
 
 __all__ = [
     "rms_norm", "rope_inv_freq", "partial_rope", "qk_prologue", "key_set", "prefill",
     "prefill_rows", "attention_probs_row", "decode", "kv_bytes", "kv_entries",
     "is_global_layer", "global_layers", "stack_layer", "stack_layer_rows", "stack", "layer_is_global",
     "e4m3_values", "round_e4m3", "decode_fp8_cache", "layer_backward", "layer_backward_rows",
-    "row_lse",
+    "row_lse", "e4m3_decode", "quant_rows_e4m3", "gemm_e4m3", "quantize_layer_weights",
+    "stack_layer_fp8", "stack_layer_rows_fp8", "stack_fp8",
 ]

@@ -109,3 +109,4 @@ def layer(x, w, *, is_global, rope_base=1e7, window=128, eps=1e-6):
         else:
             a = attention_local(q, k, v, g, rope_base, window=window, eps=eps)
     return x + a.reshape(T, 4096) @ w["wo"].T
+

@@ -97,3 +97,25 @@ def test_stack_wrappers_reject_shapes():
                         residual=torch.zeros(8, 15))
     with pytest.raises(ValueError, match="w"):
         zg.zg_rmsnorm(torch.zeros(3, 64), w=torch.ones(32))
+
+
+def test_fp8_stack_wrappers_reject_shapes():
+    u8, f32 = torch.uint8, torch.float32
+    with pytest.raises(ValueError, match="x_scale"):
+        zg.zg_gemm_fp8(torch.zeros(8, 256, dtype=u8), torch.zeros(7, dtype=f32),
+                       torch.zeros(16, 256, dtype=u8), torch.zeros(16, dtype=f32))
+    with pytest.raises(ValueError, match="w has shape"):
+        zg.zg_gemm_fp8(torch.zeros(8, 256, dtype=u8), torch.zeros(8, dtype=f32),
+                       torch.zeros(16, 128, dtype=u8), torch.zeros(16, dtype=f32))
+    with pytest.raises(ValueError, match="scale"):
+        zg.zg_quant_rows_fp8(torch.zeros(4, 64, dtype=bf), scale=torch.zeros(5, dtype=f32))
+    x = torch.zeros(1, 4, 4096)
+    n_qkvg = (32 + 16 + 32) * 128
+    good = dict(w_qkvg=torch.zeros(n_qkvg, 4096, dtype=u8), s_qkvg=torch.zeros(n_qkvg, dtype=f32),
+                w_o=torch.zeros(4096, 4096, dtype=u8), s_o=torch.zeros(4096, dtype=f32))
+    for name, bad in (("w_qkvg", torch.zeros(n_qkvg - 128, 4096, dtype=u8)),
+                      ("s_qkvg", torch.zeros(n_qkvg - 1, dtype=f32)),
+                      ("s_o", torch.zeros(4095, dtype=f32))):
+        args = dict(good, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            zg.zg_attn_layer_fp8(RING, x, args["w_qkvg"], args["s_qkvg"], args["w_o"], args["s_o"])
