@@ -241,29 +241,35 @@ void gemm_fp8_kernel(GemmFp8Params p) {
     if (it + 1 < n_k) dma_stage((it + 1) % kFNBuf, (it + 1) * kFBK);
     const unsigned char* st = smem + (it % kFNBuf) * kFStage;
     i32x8 a[2][4], b[2][4];
-    auto read_ops = [&](int ks) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(st + a_off[ks][0] + 32 * kFBK * i);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + a_off[ks][1] + 32 * kFBK * i);
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(st + b_off[ks][0] + 32 * kFBK * i);
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(st + b_off[ks][1] + 32 * kFBK * i);
-        a[ks & 1][i] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        b[ks & 1][i] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
-                             (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-      }
+    auto rd = [&](const int (&off)[kFSub][2], int ks, int i) -> i32x8 {
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(st + off[ks][0] + 32 * kFBK * i);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(st + off[ks][1] + 32 * kFBK * i);
+      return i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                   (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
     };
-    read_ops(0);
+    // The first MFMAs need only the step's four B operands and one A operand; every further A
+    // operand (and the next step's operands) is read while the MFMAs of the row block before it
+    // run, so little of the stage's read volume stands in front of idle matrix cores.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[0][j] = rd(b_off, 0, j);
+    a[0][0] = rd(a_off, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kFSub; ++ks) {
-      if (ks + 1 < kFSub) read_ops(ks + 1);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        if (i + 1 < 4) {
+          a[ks][i + 1] = rd(a_off, ks, i + 1);
+        } else if (ks + 1 < kFSub) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp8(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < 4; ++j) b[ks + 1][j] = rd(b_off, ks + 1, j);
+          a[ks + 1][0] = rd(a_off, ks + 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp8(a[ks][i], b[ks][j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
