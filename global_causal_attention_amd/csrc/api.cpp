@@ -368,6 +368,8 @@ zg_status zg_attn_backward(const zg_attn_cfg* cfg, int32_t B, int32_t T, const v
     kp.fold_scale = 1.f;
     st = hip_status(zg::launch_kprep(kp, hs), "kprep launch (k)");
     if (st != ZG_OK) return st;
+    // without a gate dO is dy itself
+    if (!cfg->gated) bp.dO = const_cast<uint16_t*>(static_cast<const uint16_t*>(dout));
 
     bp.q = static_cast<const uint16_t*>(q);
     bp.k = static_cast<const uint16_t*>(k);

@@ -10,9 +10,10 @@
 // dP = dO V^T.
 //
 // Kernels (one launch each, in this order):
-//  1. bwd_pre   per (token, query head): dO = dy * sigmoid(g), dg = dy * y * (1 - sigmoid(g)),
-//               D = sum dy * y, and a 16-value bf16 row (-L log2 e and -D, each split exactly into
-//               three bf16 terms) that an extra matrix-core step subtracts from the scores.
+//  1. bwd_pre   per (token, query head): dO = dy * sigmoid(g), dg = dy * y * (1 - sigmoid(g))
+//               (gated layers; without a gate dO is dy and is not copied), D = sum dy * y, and a
+//               16-value bf16 row (-L log2 e and -D, each split exactly into three bf16 terms)
+//               that an extra matrix-core step subtracts from the scores.
 //  2. bwd_q     per (sequence, KV head, 64 queries): streams K_hat/V tiles like the forward,
 //               accumulates dq_hat = scale * dS K_hat and turns it into dq in its epilogue.
 //  3. bwd_kv    per (sequence, KV head, 64 keys): keeps the tile's K_hat as matrix-core operands
@@ -45,6 +46,12 @@ constexpr int kKvVTile = kKvWaves * 2 * kStepBytes;  // 139264: the tile's V row
 constexpr int kKvLds = kKvVTile + kTileBytes;        // 155648
 static_assert(kKvLds <= 160 * 1024, "LDS budget");
 static_assert(kKvWaves * 32 * 64 * 16 <= kKvVTile, "cross-wave reduction fits the stream buffers");
+
+// acc += A B on the matrix cores with acc held in accumulation registers (AGPRs), whatever form
+// the compiler picks for the kernel's other matrix products
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8 a, const bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -180,14 +187,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const int64_t n_rows = (int64_t)p.B * p.T * p.Hq;
   if (row >= n_rows) return;  // whole 16-lane groups exit together
   const int64_t off = row * kHeadDim + 8 * c;
-  float y[8], dy[8], d_o[8];
+  float y[8], dy[8];
   unpack8(*reinterpret_cast<const u32x4*>(p.out + off), y);
   unpack8(*reinterpret_cast<const u32x4*>(p.dout + off), dy);
   float dsum = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) dsum = fmaf(dy[i], y[i], dsum);
   if (p.gated) {
-    float g[8], dg[8];
+    float g[8], dg[8], d_o[8];
     unpack8(*reinterpret_cast<const u32x4*>(p.gate + off), g);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -196,11 +203,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
       dg[i] = dy[i] * y[i] * (1.0f - s);
     }
     *reinterpret_cast<u32x4*>(p.dgate + off) = pack8(dg);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d_o[i] = dy[i];
+    *reinterpret_cast<u32x4*>(p.dO + off) = pack8(d_o);
   }
-  *reinterpret_cast<u32x4*>(p.dO + off) = pack8(d_o);
+  // without a gate dO is dy itself: the host points dO at dout
   dsum += shfl_xor_f(dsum, 1);
   dsum += shfl_xor_f(dsum, 2);
   dsum += shfl_xor_f(dsum, 4);
@@ -627,7 +632,7 @@ void bwd_kv_kernel(BwdParams p) {
       if (k < 8) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          dv[db][kb] = mfma32(a, __builtin_bit_cast(bf16x8, pp[kb][st]), dv[db][kb]);
+          mfma_agpr(dv[db][kb], a, __builtin_bit_cast(bf16x8, pp[kb][st]));
         const int kb = k >> 2, c = k & 3;  // dS of key block kb, registers 4 c .. 4 c + 3
         ps[kb][c >> 1][2 * (c & 1)] =
             pack_bf16(s[kb][4 * c] * dp[kb][4 * c], s[kb][4 * c + 1] * dp[kb][4 * c + 1]);
@@ -636,12 +641,15 @@ void bwd_kv_kernel(BwdParams p) {
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          dk[db][kb] = mfma32(a, __builtin_bit_cast(bf16x8, ps[kb][st]), dk[db][kb]);
+          mfma_agpr(dk[db][kb], a, __builtin_bit_cast(bf16x8, ps[kb][st]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
+  // the last accumulation's results are read below by register moves the compiler cannot see
+  // depend on it: wait out the matrix pipeline first
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   // sum over the 4 heads: each wave stores its partial sums, then reduces a quarter of them
   // (dim block `wave` of both key blocks): dv straight to memory, dk_hat staged as rows
   f32x4* red = reinterpret_cast<f32x4*>(smem);
