@@ -303,6 +303,39 @@ def bench_decode(torch, zg, si, dev, stream, reps):
         res[name] = {"ms_median": round(med, 4), "kv_bytes": kv_bytes, "GBps": round(bw / 1e9, 1),
                      "hbm_frac": round(bw / HBM_PEAK, 4), "tokens_per_s": round(Bd / (med * 1e-3), 1)}
         log(f"[bench] decode {name}: {med:.4f} ms, {bw / 1e9:.1f} GB/s")
+    # The local layers of one decode step (27 of a 32-layer 5:1 stack) run back to back, each over
+    # its own ring cache (27 x 32 MiB, so every layer starts cold): per-layer time of that sequence.
+    # The isolated call above also holds the event and dispatch overhead around one short kernel.
+    n_local = 27
+    rings = [(si.randn_bf16(gen, x["ring_k"].shape, device=dev),
+              si.randn_bf16(gen, x["ring_v"].shape, device=dev)) for _ in range(n_local)]
+    outs = [torch.empty_like(x["q_new"]) for _ in range(n_local)]
+
+    def ring_layers():
+        for (rk, rv), o in zip(rings, outs):
+            zg.zg_attn_decode(cfg_r, x["q_new"], x["k_new"], x["v_new"], x["gate"], rk, rv, seqlens,
+                              max_seqlen=hi, out=o, workspace=ws_r)
+
+    ring_layers()
+    times = []
+    for _ in range(reps):
+        for _ in range(6):
+            flush.fill_(1)  # ~1.2 ms of device work while the host enqueues the 27 calls
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ring_layers()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / n_local)
+    times.sort()
+    med = times[len(times) // 2]
+    kvb = res["ring"]["kv_bytes"]
+    res["ring"]["back_to_back"] = {
+        "layers": n_local, "ms_per_layer_median": round(med, 4),
+        "GBps": round(kvb / (med * 1e-3) / 1e9, 1), "hbm_frac": round(kvb / (med * 1e-3) / HBM_PEAK, 4)}
+    log(f"[bench] decode ring, {n_local} layers back to back: {med * 1e3:.2f} us per layer")
+    del rings, outs
     # streaming-read reference: the probe reads the 8 GiB linear K cache (cold MALL) with the same
     # non-temporal 16-byte loads the decode kernels use
     sink = torch.empty(4 * 2048, dtype=torch.int32, device=dev)
