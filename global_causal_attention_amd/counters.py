@@ -47,6 +47,13 @@ KERNEL_SOURCES = {
     "bwd_q_kernel": ["backward.hip"] + _COMMON,
     "bwd_kv_kernel": ["backward.hip"] + _COMMON,
     "decode_combine_kernel": ["decode.hip"] + _COMMON,
+    "decode_ring_kernel": ["decode.hip"] + _COMMON,
+    "row_copy_kernel": ["prefill.hip"] + _COMMON,
+    "rmsnorm_kernel": ["stack.hip"] + _COMMON,
+    "gemm_kernel": ["stack.hip"] + _COMMON,
+    "rmsnorm_fp8_kernel": ["stack_fp8.hip"] + _COMMON,
+    "quant_rows_kernel": ["stack_fp8.hip"] + _COMMON,
+    "gemm_fp8_kernel": ["stack_fp8.hip"] + _COMMON,
 }
 
 
