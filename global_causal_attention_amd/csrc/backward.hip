@@ -172,9 +172,11 @@ __device__ __forceinline__ void dx_from_staged(float* srow, const u32x4 (&xr)[8]
   for (int i = 0; i < 8; ++i) reinterpret_cast<u32x4*>(drow + 64 * half)[i] = pack8(dx + 8 * i);
 }
 
-constexpr int kQStageLds = kWaves * 32 * kStageRow * 4;  // bwd_q epilogue: 32 rows per wave
-constexpr int kQLdsTotal = kQStageLds > kQLds ? kQStageLds : kQLds;
-static_assert(kQLdsTotal <= 160 * 1024, "LDS budget");
+constexpr int kQStageWave = 32 * kStageRow * 4;  // bwd_q epilogue: 32 rows per wave
+// LDS of a bwd_q workgroup of 4 QB waves: the tile buffers, or the epilogue's staged rows
+constexpr int q_lds_total(int qb) { return 4 * qb * kQStageWave > kQLds ? 4 * qb * kQStageWave : kQLds; }
+static_assert(q_lds_total(2) <= 160 * 1024, "LDS budget");
+static_assert(2 * q_lds_total(1) <= 160 * 1024, "two 4-wave workgroups per CU");
 static_assert(64 * kStageRow * 4 <= kKvVTile, "bwd_kv epilogue staging fits");
 
 }  // namespace
@@ -224,7 +226,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // dS^T pack straight into the B operand of dQ^T = K_hat^T dS^T. Keys stream in tiles of 64
 // through two K_hat and two V buffers (waves 0-3 load K_hat rows, 4-7 V rows), one barrier per
 // tile; q_hat, dO and the -L/-D row are B operands held in registers.
-__global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
+template <int QB>
+__global__ __launch_bounds__(QB * 256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_q_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
   const int qtile = (p.window == 0) ? (p.n_qtiles - 1 - t_idx) : t_idx;  // heavy tiles first
   const int b = bh / p.Hkv;
   const int kvh = bh - b * p.Hkv;
-  constexpr int MQ = 64;
+  constexpr int MQ = 32 * QB;
   const int r0 = qtile * MQ;
   const int T = p.T;
   const int W = p.window;
@@ -277,25 +281,33 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdParams p) {
   if (W > 0) k_begin = max(0, r0 - W + 1) & ~(kNk - 1);
   const int n_tiles = (q_last + 1 - k_begin + kNk - 1) / kNk;
 
-  // tile streaming: 16 rows per wave, 4 LDS-direct loads of 4 rows
-  const bool v_loader = wave >= 4;
+  // tile streaming: wave w brings rows 16 (w % 4) .. + 15 of the tile, 4 LDS-direct loads of 4
+  // rows each: of K_hat (waves 0-3) or V (waves 4-7) with 8 waves, of both with 4
   const int wg = wave & 3;
   const int row_bytes = p.Hkv * kHeadDim * 2;
-  const uint16_t* slab = (v_loader ? p.v : p.khat) + ((int64_t)b * T * p.Hkv + kvh) * kHeadDim;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (v_loader ? 2 * kTileBytes : 0);
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * i + (lane >> 4);
     voff[i] = (uint32_t)(row * row_bytes + 16 * ((lane & 15) ^ swz(row)));
   }
-  auto dma_tile = [&](int t) {  // tile t into buffer t & 1
+  auto dma_part = [&](int t, bool is_v) {  // tile t of K_hat or V into buffer t & 1
+    const uint16_t* slab = (is_v ? p.v : p.khat) + ((int64_t)b * T * p.Hkv + kvh) * kHeadDim;
     const int row0 = k_begin + t * kNk + 16 * wg;
     const __amdgpu_buffer_rsrc_t r =
         rsrc_of(slab + (int64_t)row0 * p.Hkv * kHeadDim, (int64_t)min(16, T - row0) * row_bytes);
-    const uint32_t base = lds0 + (t & 1) * kTileBytes + 16 * wg * kRow;
+    const uint32_t base = (uint32_t)(uintptr_t)smem + (is_v ? 2 * kTileBytes : 0) +
+                          (t & 1) * kTileBytes + 16 * wg * kRow;
 #pragma unroll
     for (int i = 0; i < 4; ++i) lds_dma(base + 4 * i * kRow, voff[i], r);
+  };
+  auto dma_tile = [&](int t) {
+    if (QB == 2) {
+      dma_part(t, wave >= 4);
+    } else {
+      dma_part(t, false);
+      dma_part(t, true);
+    }
   };
 
   int k_off[8];  // A operand of K step st: tile row l32 (+32 per key block), dims 16 st + 8 hi
@@ -713,11 +725,26 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kQLdsTotal);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_q_kernel, dim3((unsigned)((int64_t)p.n_qtiles * p.B * p.Hkv)),
-                     dim3(kThreads), kQLdsTotal, s, p);
+  // banded layers: 32 queries per workgroup of 4 waves, two workgroups per CU, so one's load and
+  // epilogue latencies overlap the other's tiles (a banded workgroup walks only 2-3 key tiles);
+  // full causal layers: 64 queries per workgroup of 8 waves, every K/V tile shared by twice the
+  // queries
+  BwdParams pq = p;
+  if (p.window > 0) {
+    pq.n_qtiles = (p.T + 31) / 32;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel<1>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, q_lds_total(1));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_q_kernel<1>, dim3((unsigned)((int64_t)pq.n_qtiles * p.B * p.Hkv)),
+                       dim3(256), q_lds_total(1), s, pq);
+  } else {
+    pq.n_qtiles = (p.T + 63) / 64;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel<2>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, q_lds_total(2));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_q_kernel<2>, dim3((unsigned)((int64_t)pq.n_qtiles * p.B * p.Hkv)),
+                       dim3(512), q_lds_total(2), s, pq);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
