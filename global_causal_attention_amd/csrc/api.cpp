@@ -388,7 +388,7 @@ zg_status zg_attn_backward(const zg_attn_cfg* cfg, int32_t B, int32_t T, const v
     bp.Hkv = (int32_t)Hkv;
     bp.window = cfg->window >= T ? 0 : cfg->window;
     bp.gated = cfg->gated;
-    bp.n_qtiles = (T + 63) / 64;
+    bp.n_qtiles = (T + 31) / 32;  // bwd_q: 32 queries per workgroup
     bp.pos0 = 0;
     bp.eps = cfg->rms_eps;
     bp.scale = (float)(cfg->softmax_scale > 0.f ? (double)cfg->softmax_scale : 1.0 / std::sqrt((double)kD));

@@ -14,7 +14,7 @@
 //               (gated layers; without a gate dO is dy and is not copied), D = sum dy * y, and a
 //               16-value bf16 row (-L log2 e and -D, each split exactly into three bf16 terms)
 //               that an extra matrix-core step subtracts from the scores.
-//  2. bwd_q     per (sequence, KV head, 64 queries): streams K_hat/V tiles like the forward,
+//  2. bwd_q     per (sequence, KV head, 32 queries): streams K_hat/V tiles like the forward,
 //               accumulates dq_hat = scale * dS K_hat and turns it into dq in its epilogue.
 //  3. bwd_kv    per (sequence, KV head, 64 keys): keeps the tile's K_hat as matrix-core operands
 //               in registers and its V rows in LDS, one wave per query head streams that head's
@@ -172,11 +172,10 @@ __device__ __forceinline__ void dx_from_staged(float* srow, const u32x4 (&xr)[8]
   for (int i = 0; i < 8; ++i) reinterpret_cast<u32x4*>(drow + 64 * half)[i] = pack8(dx + 8 * i);
 }
 
-constexpr int kQStageWave = 32 * kStageRow * 4;  // bwd_q epilogue: 32 rows per wave
-// LDS of a bwd_q workgroup of 4 QB waves: the tile buffers, or the epilogue's staged rows
-constexpr int q_lds_total(int qb) { return 4 * qb * kQStageWave > kQLds ? 4 * qb * kQStageWave : kQLds; }
-static_assert(q_lds_total(2) <= 160 * 1024, "LDS budget");
-static_assert(2 * q_lds_total(1) <= 160 * 1024, "two 4-wave workgroups per CU");
+constexpr int kQStageLds = 4 * 32 * kStageRow * 4;  // bwd_q epilogue: 32 rows per wave
+// LDS of a bwd_q workgroup: the tile buffers, or the epilogue's staged rows
+constexpr int kQLdsTotal = kQStageLds > kQLds ? kQStageLds : kQLds;
+static_assert(2 * kQLdsTotal <= 160 * 1024, "two bwd_q workgroups per CU");
 static_assert(64 * kStageRow * 4 <= kKvVTile, "bwd_kv epilogue staging fits");
 
 }  // namespace
@@ -220,14 +219,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2. dq_hat. Workgroup = 8 waves = (sequence, KV head, 64 queries); wave w owns query head w % 4
-// and queries 32 (w / 4) .. +31 of the tile. Scores are transposed as in the forward,
-// S^T = K_hat Q^T (one query per lane), and dP^T = V dO^T in the same layout, so the weights
-// dS^T pack straight into the B operand of dQ^T = K_hat^T dS^T. Keys stream in tiles of 64
-// through two K_hat and two V buffers (waves 0-3 load K_hat rows, 4-7 V rows), one barrier per
-// tile; q_hat, dO and the -L/-D row are B operands held in registers.
-template <int QB>
-__global__ __launch_bounds__(QB * 256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// 2. dq_hat. Workgroup = 4 waves = (sequence, KV head, 32 queries); wave w owns query head w of the
+// group. Scores are transposed as in the forward, S^T = K_hat Q^T (one query per lane), and
+// dP^T = V dO^T in the same layout, so the weights dS^T pack straight into the B operand of
+// dQ^T = K_hat^T dS^T. Keys stream in tiles of 64 through two K_hat and two V buffers (each wave
+// loads 16 rows of both), one barrier per tile; q_hat, dO and the -L/-D row are B operands held in
+// registers. At 256 VGPRs and 68 KB of LDS two workgroups share a CU, so the load and epilogue
+// latencies of one overlap the other's tiles (a banded workgroup walks only 2-3 of them).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_q_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -241,7 +240,7 @@ void bwd_q_kernel(BwdParams p) {
   const int qtile = (p.window == 0) ? (p.n_qtiles - 1 - t_idx) : t_idx;  // heavy tiles first
   const int b = bh / p.Hkv;
   const int kvh = bh - b * p.Hkv;
-  constexpr int MQ = 32 * QB;
+  constexpr int MQ = 32;
   const int r0 = qtile * MQ;
   const int T = p.T;
   const int W = p.window;
@@ -281,9 +280,9 @@ void bwd_q_kernel(BwdParams p) {
   if (W > 0) k_begin = max(0, r0 - W + 1) & ~(kNk - 1);
   const int n_tiles = (q_last + 1 - k_begin + kNk - 1) / kNk;
 
-  // tile streaming: wave w brings rows 16 (w % 4) .. + 15 of the tile, 4 LDS-direct loads of 4
-  // rows each: of K_hat (waves 0-3) or V (waves 4-7) with 8 waves, of both with 4
-  const int wg = wave & 3;
+  // tile streaming: wave w brings rows 16 w .. 16 w + 15 of the K_hat and of the V tile, 4
+  // LDS-direct loads of 4 rows each
+  const int wg = wave;
   const int row_bytes = p.Hkv * kHeadDim * 2;
   uint32_t voff[4];
 #pragma unroll
@@ -302,12 +301,8 @@ void bwd_q_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i) lds_dma(base + 4 * i * kRow, voff[i], r);
   };
   auto dma_tile = [&](int t) {
-    if (QB == 2) {
-      dma_part(t, wave >= 4);
-    } else {
-      dma_part(t, false);
-      dma_part(t, true);
-    }
+    dma_part(t, false);
+    dma_part(t, true);
   };
 
   int k_off[8];  // A operand of K step st: tile row l32 (+32 per key block), dims 16 st + 8 hi
@@ -725,26 +720,11 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // banded layers: 32 queries per workgroup of 4 waves, two workgroups per CU, so one's load and
-  // epilogue latencies overlap the other's tiles (a banded workgroup walks only 2-3 key tiles);
-  // full causal layers: 64 queries per workgroup of 8 waves, every K/V tile shared by twice the
-  // queries
-  BwdParams pq = p;
-  if (p.window > 0) {
-    pq.n_qtiles = (p.T + 31) / 32;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel<1>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, q_lds_total(1));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_q_kernel<1>, dim3((unsigned)((int64_t)pq.n_qtiles * p.B * p.Hkv)),
-                       dim3(256), q_lds_total(1), s, pq);
-  } else {
-    pq.n_qtiles = (p.T + 63) / 64;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel<2>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, q_lds_total(2));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_q_kernel<2>, dim3((unsigned)((int64_t)pq.n_qtiles * p.B * p.Hkv)),
-                       dim3(512), q_lds_total(2), s, pq);
-  }
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kQLdsTotal);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_q_kernel, dim3((unsigned)((int64_t)p.n_qtiles * p.B * p.Hkv)), dim3(256),
+                     kQLdsTotal, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
