@@ -51,9 +51,11 @@ hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t s) {
 
 // ---------------------------------------------------------------------------------------------
 // GEMM: Y[m, n] = sum_k X[m, k] W[n, k]. Both operands are K-contiguous, so each MFMA operand lane
-// reads 16 contiguous bytes of a staged row. One workgroup of 4 waves (one per SIMD) computes a
-// 256 x 256 tile; each wave owns a 128 x 128 quadrant of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks, so
-// every operand read from LDS feeds four MFMAs. K advances 64 per stage: the stage's 256-row X and
+// reads 16 contiguous bytes of a staged row. One workgroup of 8 waves (two per SIMD) computes a
+// 256 x 256 tile; each wave owns a 128 x 64 block of 4 x 2 v_mfma_f32_32x32x16_bf16 blocks, so an X
+// operand read from LDS feeds two MFMAs and a W operand four. Two waves per SIMD let one wave's
+// stage loads and barrier waits overlap the other's MFMAs (with one wave per SIMD and 128 x 128
+// blocks the operand reads halve but the matrix cores idle whenever that wave waits: ~10% slower). K advances 64 per stage: the stage's 256-row X and
 // W slabs (128 bytes per row) stream into LDS by buffer_load ... lds, double-buffered, one barrier
 // per stage; within a stage the operands of the next 16-deep step are read while the 16 MFMAs of
 // the current one run. A staged row keeps its eight 16-byte chunks XOR-swizzled by (row / 2 mod 8): two
@@ -67,11 +69,11 @@ constexpr int kGBM = 256;                   // tile M
 constexpr int kGBN = 256;                   // tile N
 constexpr int kGBK = 64;                    // K per stage (32 or 64)
 constexpr int kGNBuf = 2;                   // stages resident in LDS
-constexpr int kGThreads = 256;              // 4 waves
+constexpr int kGThreads = 512;              // 8 waves
 constexpr int kGRowB = 2 * kGBK;            // bytes per staged row
 constexpr int kGChunks = kGRowB / 16;       // 16-byte chunks per staged row
 constexpr int kGRowsPerDma = 1024 / kGRowB; // rows filled by one DMA instruction (1 KB)
-constexpr int kGDmaPerSlab = kGBM / kGRowsPerDma / 4;  // DMA instructions per wave per slab
+constexpr int kGDmaPerSlab = kGBM / kGRowsPerDma / 8;  // DMA instructions per wave per slab
 constexpr int kGTileA = kGBM * kGRowB;
 constexpr int kGStage = kGTileA + kGBN * kGRowB;
 constexpr int kGLds = kGNBuf * kGStage;
@@ -90,7 +92,7 @@ __device__ __forceinline__ f32x16 mfma32g(const bf16x8 a, const bf16x8 b, const 
 }
 }  // namespace
 
-__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -139,8 +141,8 @@ void gemm_kernel(GemmParams p) {
   };
 
   // ---- operand reads: row (quadrant + 32 i + l32), logical chunk 2 ks + hi
-  const int wm = (wave >> 1) * 128;
-  const int wn = (wave & 1) * 128;
+  const int wm = (wave >> 2) * 128;
+  const int wn = (wave & 3) * 64;
   constexpr int kSub = kGBK / 16;
   int a_off[kSub], b_off[kSub];
 #pragma unroll
@@ -150,11 +152,11 @@ void gemm_kernel(GemmParams p) {
     b_off[ks] = kGTileA + (wn + l32) * kGRowB + c;
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int n_k = p.K / kGBK;
   for (int s = 0; s < kGNBuf - 1 && s < n_k; ++s) dma_stage(s, s * kGBK);
@@ -170,13 +172,12 @@ void gemm_kernel(GemmParams p) {
     if (it + kGNBuf - 1 < n_k) dma_stage((it + kGNBuf - 1) % kGNBuf, (it + kGNBuf - 1) * kGBK);
     const unsigned char* st = smem + (it % kGNBuf) * kGStage;
     // operands of step ks + 1 are read while the 16 MFMAs of step ks run
-    bf16x8 a[2][4], b[2][4];
+    bf16x8 a[2][4], b[2][2];
     auto read_ops = [&](int ks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[ks & 1][i] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + 32 * kGRowB * i);
-        b[ks & 1][i] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + 32 * kGRowB * i);
-      }
+      for (int i = 0; i < 4; ++i) a[ks & 1][i] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + 32 * kGRowB * i);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[ks & 1][j] = *reinterpret_cast<const bf16x8*>(st + b_off[ks] + 32 * kGRowB * j);
     };
     read_ops(0);
 #pragma unroll
@@ -186,7 +187,7 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32g(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32g(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -197,7 +198,7 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn + 32 * j + l32;
       const int64_t mb = m0 + wm + 32 * i + 4 * hi;
       if (full) {
