@@ -130,10 +130,11 @@ hipError_t launch_quant_rows(const QuantRowsParams& p, hipStream_t s) {
 
 // ---------------------------------------------------------------------------------------------
 // E4M3 GEMM: Y[m, n] = sx[m] sw[n] sum_k X[m, k] W[n, k], both operands K-contiguous bytes. The
-// tile scheme of the bf16 GEMM, one byte per element: one workgroup of 4 waves (one per SIMD)
-// computes a 256 x 256 tile, each wave a 128 x 128 quadrant of 4 x 4 blocks of
-// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, unit block scales), accumulators in AGPRs, so
-// every operand read from LDS feeds four MFMAs. K advances 128 per stage: 256 rows of 128 bytes of
+// tile scheme of the bf16 GEMM, one byte per element: one workgroup of 8 waves (two per SIMD)
+// computes a 256 x 256 tile, each wave a 128 x 64 block of 4 x 2 blocks of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, unit block scales), so an X operand read from
+// LDS feeds two MFMAs and a W operand four, and one wave's stage loads and barrier waits overlap
+// the other's MFMAs. K advances 128 per stage: 256 rows of 128 bytes of
 // X and of W stream into LDS by buffer_load ... lds, double-buffered, one barrier per stage; a
 // stage is two 64-deep MFMA steps. A lane's 32 operand bytes of a step are two 16-byte chunks of
 // its row, the same k positions for both operands (the MFMA sums over whatever k each element
@@ -144,9 +145,9 @@ constexpr int kFBM = 256;                    // tile M
 constexpr int kFBN = 256;                    // tile N
 constexpr int kFBK = 128;                    // K per stage = bytes per staged row
 constexpr int kFNBuf = 2;                    // stages resident in LDS
-constexpr int kFThreads = 256;               // 4 waves
+constexpr int kFThreads = 512;               // 8 waves
 constexpr int kFRowsPerDma = 1024 / kFBK;    // rows filled by one DMA instruction (1 KB)
-constexpr int kFDmaPerSlab = kFBM / kFRowsPerDma / 4;  // DMA instructions per wave per slab
+constexpr int kFDmaPerSlab = kFBM / kFRowsPerDma / 8;  // DMA instructions per wave per slab
 constexpr int kFTileA = kFBM * kFBK;
 constexpr int kFStage = kFTileA + kFBN * kFBK;
 constexpr int kFLds = kFNBuf * kFStage;
@@ -164,7 +165,7 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8 a, const i32x8 b, const f
 }
 }  // namespace
 
-__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_kernel(GemmFp8Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -212,9 +213,9 @@ void gemm_fp8_kernel(GemmFp8Params p) {
     }
   };
 
-  // ---- operand reads: row (quadrant + 32 i + l32), logical chunks 4 ks + 2 hi and 4 ks + 2 hi + 1
-  const int wm = (wave >> 1) * 128;
-  const int wn = (wave & 1) * 128;
+  // ---- operand reads: row (block + 32 i + l32), logical chunks 4 ks + 2 hi and 4 ks + 2 hi + 1
+  const int wm = (wave >> 2) * 128;
+  const int wn = (wave & 3) * 64;
   int a_off[kFSub][2], b_off[kFSub][2];
 #pragma unroll
   for (int ks = 0; ks < kFSub; ++ks)
@@ -225,11 +226,11 @@ void gemm_fp8_kernel(GemmFp8Params p) {
       b_off[ks][h2] = kFTileA + (wn + l32) * kFBK + c;
     }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int n_k = p.K / kFBK;
   dma_stage(0, 0);
@@ -240,7 +241,7 @@ void gemm_fp8_kernel(GemmFp8Params p) {
     __syncthreads();
     if (it + 1 < n_k) dma_stage((it + 1) % kFNBuf, (it + 1) * kFBK);
     const unsigned char* st = smem + (it % kFNBuf) * kFStage;
-    i32x8 a[2][4], b[2][4];
+    i32x8 a[2][4], b[2][2];
     auto rd = [&](const int (&off)[kFSub][2], int ks, int i) -> i32x8 {
       const u32x4 v0 = *reinterpret_cast<const u32x4*>(st + off[ks][0] + 32 * kFBK * i);
       const u32x4 v1 = *reinterpret_cast<const u32x4*>(st + off[ks][1] + 32 * kFBK * i);
@@ -251,7 +252,7 @@ void gemm_fp8_kernel(GemmFp8Params p) {
     // operand (and the next step's operands) is read while the MFMAs of the row block before it
     // run, so little of the stage's read volume stands in front of idle matrix cores.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[0][j] = rd(b_off, 0, j);
+    for (int j = 0; j < 2; ++j) b[0][j] = rd(b_off, 0, j);
     a[0][0] = rd(a_off, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -262,26 +263,28 @@ void gemm_fp8_kernel(GemmFp8Params p) {
           a[ks][i + 1] = rd(a_off, ks, i + 1);
         } else if (ks + 1 < kFSub) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) b[ks + 1][j] = rd(b_off, ks + 1, j);
+          for (int j = 0; j < 2; ++j) b[ks + 1][j] = rd(b_off, ks + 1, j);
           a[ks + 1][0] = rd(a_off, ks + 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp8(a[ks][i], b[ks][j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_fp8(a[ks][i], b[ks][j], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
   // ---- epilogue: lane holds column n = l32 of each 32x32 block, rows 8*(r/4) + 4*hi + r%4.
-  // First every accumulator takes its row's and column's scale (no branches, so the block loops
-  // unroll and the accumulators stay in registers), then the store as in the bf16 GEMM.
-  float ws[4];
+  // Row block by row block: the block's accumulators take their rows' and columns' scales (no
+  // branches, so the loops unroll and the accumulators stay in registers), then the store as in the
+  // bf16 GEMM; one block's row scales at a time keeps the epilogue within 256 registers.
+  float ws[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn + 32 * j + l32;
     ws[j] = p.w_scale[min(n, p.N - 1)];
   }
+  const bool full = m0 + kFBM <= p.M && n0 + kFBN <= p.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t mb = m0 + wm + 32 * i + 4 * hi;
@@ -289,17 +292,12 @@ void gemm_fp8_kernel(GemmFp8Params p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) xs[r] = p.x_scale[min(mb + 8 * (r >> 2) + (r & 3), p.M - 1)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] *= xs[r] * ws[j];
-  }
-  const bool full = m0 + kFBM <= p.M && n0 + kFBN <= p.N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn + 32 * j + l32;
-      const int64_t mb = m0 + wm + 32 * i + 4 * hi;
       if (full) {
         if (p.residual) {
           float* rp = p.residual + mb * p.N + n;
@@ -327,6 +325,8 @@ void gemm_fp8_kernel(GemmFp8Params p) {
         if (p.y) p.y[m * p.ldy + n] = (uint16_t)(pack_bf16(v, 0.f) & 0xffffu);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 hipError_t launch_gemm_fp8(const GemmFp8Params& p, hipStream_t s) {
