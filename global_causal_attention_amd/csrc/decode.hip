@@ -638,8 +638,11 @@ __device__ __forceinline__ int mf_key(int r) {
 }
 }  // namespace
 
+// At most 256 registers per lane (two workgroups per CU: more loads in flight per CU; the kernel
+// fits in ~156 VGPRs, while left unbounded the compiler took 260 and one workgroup per CU).
 template <bool FP8>
-__global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_mfma_kernel(DecodeParams p) {
   constexpr int G = 4;
   constexpr int kMaxChunk = kDecodeChunkKeys;
   static_assert(kMaxChunk % 32 == 0, "blocks of 32 keys");
