@@ -86,17 +86,26 @@ def test_two_chunks_then_decode(W, gated, B, T1, T2, base):
     assert_parity(out_d, ref_d[:, 0], f"decode after chunks W={W} L={L}")
 
 
-def test_first_chunk_equals_plain_prefill():
-    """pos0 = 0 through the caches computes the same attention as the plain prefill call."""
+@pytest.mark.parametrize("weights", [False, True])
+def test_first_chunk_equals_plain_prefill(weights):
+    """pos0 = 0 through the caches computes the same attention as the plain prefill call; on the
+    banded streaming kernel both calls take the same folded keys from the K prologue kernel, so the
+    same output bit for bit (also with non-unit q and k norm weights)."""
     B, T = 2, 333
-    x = si.prefill_layer(si.generator(2100), B, T, HQ, HKV, D, gated=True)
+    gen = si.generator(2100 + weights)
+    x = si.prefill_layer(gen, B, T, HQ, HKV, D, gated=True)
     q, k, v, g = (x[n].to(DEV) for n in ("q", "k", "v", "gate"))
+    nw = {}
+    if weights:
+        nw = {"q_norm_w": (torch.rand(D, generator=gen) * 1.5 + 0.25).to(DEV),
+              "k_norm_w": (torch.rand(D, generator=gen) * 1.5 + 0.25).to(DEV)}
+    print(f"[case] pos0=0 cached vs plain weights={weights}", flush=True)
     for W in (128, 0):
         cfg = zg.AttnConfig(window=W, gated=W > 0, rope_base=1e6)
         kc = torch.zeros(B, W if W else T, HKV, D, dtype=torch.bfloat16, device=DEV)
         vc = torch.zeros_like(kc)
-        a = zg.zg_attn_prefill_cached(cfg, q, k, v, g if W else None, kc, vc, pos0=0)
-        ref = zg.zg_attn_prefill(cfg, q, k, v, g if W else None)
+        a = zg.zg_attn_prefill_cached(cfg, q, k, v, g if W else None, kc, vc, pos0=0, **nw)
+        ref = zg.zg_attn_prefill(cfg, q, k, v, g if W else None, **nw)
         torch.cuda.synchronize()
         assert_parity(a, f64(ref), f"pos0=0 cached vs plain W={W}", max_abs=2e-2, mean_abs=2e-3)
         if W:  # both run the banded streaming kernel on the same folded keys
