@@ -121,7 +121,8 @@ uint64_t zg_kv_bytes(int32_t n_layers, int32_t global_every, int32_t n_kv_heads,
 
 size_t zg_attn_prefill_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
   if (!cfg || B < 1 || T < 1 || cfg->n_kv_heads < 1) return 0;
-  return align256((size_t)B * T * cfg->n_kv_heads * kD * 2);
+  // k_hat, then the item counters of the tiled kernel's persistent launch
+  return align256((size_t)B * T * cfg->n_kv_heads * kD * 2) + zg::kSchedBytes;
 }
 
 zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t pos0,
@@ -180,6 +181,11 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     kp.fold = swa ? 1 : 0;
     kp.fold_scale = scale_log2(cfg);
     kp.fold_w = q_norm_w;
+    // the item counters after k_hat, zeroed by this launch for the attention launch that follows
+    uint32_t* counters = reinterpret_cast<uint32_t*>(
+        static_cast<unsigned char*>(workspace) + align256((size_t)B * T * Hkv * kD * 2));
+    kp.zero_words = counters;
+    kp.n_zero_words = zg::kSchedWords;
     st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
     if (st != ZG_OK) return st;
 
@@ -211,6 +217,7 @@ zg_status zg_attn_prefill(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t 
     if ((int64_t)pp.n_qtiles * B * Hkv >= (int64_t(1) << 31))
       return fail(ZG_ERR_SHAPE, "grid too large");
     if (swa) pp.seg_steps = swa_seg_steps(B, T, Hkv);
+    pp.counters = counters;
     return hip_status(zg::launch_prefill(pp, G, cfg->gated != 0, hs), "prefill launch");
   } catch (...) {
     return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_prefill");
@@ -236,7 +243,8 @@ static zg_status check_train(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
 
 size_t zg_attn_forward_train_workspace_bytes(const zg_attn_cfg* cfg, int32_t B, int32_t T) {
   if (!cfg || B < 1 || T < 1 || cfg->n_kv_heads < 1) return 0;
-  return align256((size_t)B * T * cfg->n_kv_heads * kD * 2);  // k_hat for the tiled kernel
+  // k_hat for the tiled kernel, then the item counters of its persistent launch
+  return align256((size_t)B * T * cfg->n_kv_heads * kD * 2) + zg::kSchedBytes;
 }
 
 zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, const void* q,
@@ -274,6 +282,10 @@ zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, co
     const bool swa = zg::prefill_uses_swa(window, 4, rt.half);
     kp.fold = swa ? 1 : 0;
     kp.fold_scale = scale_log2(cfg);
+    uint32_t* counters = reinterpret_cast<uint32_t*>(
+        static_cast<unsigned char*>(workspace) + align256((size_t)B * T * Hkv * kD * 2));
+    kp.zero_words = counters;
+    kp.n_zero_words = zg::kSchedWords;
     st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
     if (st != ZG_OK) return st;
     zg::PrefillParams pp{};
@@ -299,6 +311,7 @@ zg_status zg_attn_forward_train(const zg_attn_cfg* cfg, int32_t B, int32_t T, co
     pp.scale_log2 = scale_log2(cfg);
     pp.rope = rt;
     if (swa) pp.seg_steps = swa_seg_steps(B, T, Hkv);
+    pp.counters = counters;
     return hip_status(zg::launch_prefill(pp, 4, cfg->gated != 0, hs), "prefill launch");
   } catch (...) {
     return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_forward_train");

@@ -34,7 +34,8 @@ constexpr int kLdsK0 = 0;                   // two K buffers, then two V buffers
 constexpr int kLdsV0 = 2 * kTileBytes;
 constexpr int kQStage0 = 4 * kTileBytes;    // then per-wave q staging: 32 chunk-swizzled rows
 constexpr int kQWaveBytes = 32 * kRow;
-constexpr int kLdsBytes = kQStage0 + kWaves * kQWaveBytes;  // 128 KB
+constexpr int kLdsSlots = kQStage0 + kWaves * kQWaveBytes;  // 128 KB of tiles and q rows
+constexpr int kLdsBytes = kLdsSlots + 16;  // then the dynamic schedule's three claimed items
 
 // 16-byte chunk c of a staged row r lives at chunk c ^ swz(r). Sixteen consecutive rows read at
 // one logical chunk (the QK^T operand) and the four aligned rows x four adjacent chunks of a
@@ -105,6 +106,8 @@ constexpr int kKpStage = 68;  // floats per staged row (64 used; padded)
 
 __global__ __launch_bounds__(256) void kprep_kernel(KPrepParams p) {
   __shared__ __attribute__((aligned(16))) float stage[4][kKpRowsPerWave][kKpStage];
+  if (blockIdx.x == 0 && p.zero_words)
+    for (int i = (int)threadIdx.x; i < p.n_zero_words; i += 256) p.zero_words[i] = 0u;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
@@ -289,10 +292,37 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // A persistent workgroup brings the next item's q rows into its staging rows during iteration 1
   // of the current item, and the next item's first two K tiles once the current item's last
   // iteration has read its K buffers, so neither waits on memory at the next item's start.
+  // With item counters (p.counters) the schedule is dynamic: XCD x's items, in the same order,
+  // are handed out one at a time from its own counter to whichever of its workgroups asks next,
+  // and a workgroup whose XCD has none left takes the remaining (lightest) items of another XCD,
+  // so XCDs that run slower than others do not hold up the end of the launch. Thread 0 claims
+  // each item two items ahead into a ring of three LDS slots, so every wave reads an item's slot
+  // at least one workgroup barrier after it was written and before it is written again.
   int item_k = 0;
   int vb = p.persist ? -1 : (int)blockIdx.x;   // -1: the schedule's first item, looked up below
   bool q_ready = false;   // this item's raw q rows are already in the staging rows
   bool k_ready = false;   // this item's first K tiles were issued during the previous item
+  int* const slots = reinterpret_cast<int*>(smem + kLdsSlots);
+  auto claim = [](uint32_t* ctr, int n_items_) -> int {
+    const int x = (int)(blockIdx.x & 7);  // workgroup i runs on XCD i mod 8
+#pragma unroll 1
+    for (int sx = 0; sx < 8; ++sx) {
+      const int xs = (x + sx) & 7;
+      const int j = (int)__hip_atomic_fetch_add(ctr + kSchedStride * xs, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      if (j < ((n_items_ - xs + 7) >> 3)) return xs + 8 * j;
+    }
+    return n_items_;
+  };
+  const bool dyn = p.persist && p.counters;
+  if (dyn) {
+    const int n_items0 = p.n_qtiles * p.B * p.Hkv;
+    if (tid == 0) {
+      slots[0] = claim(p.counters, n_items0);
+      slots[1] = claim(p.counters, n_items0);
+    }
+    __syncthreads();
+  }
   while (true) {
   // The kernel arguments are read through a pointer the compiler must treat as new on every item,
   // so it loads them where the item needs them instead of keeping all of them live across the
@@ -384,9 +414,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int qb = wave / G;
   const float c = p.scale_log2;
 
-  if (vb < 0) vb = item_at(0);
+  if (dyn) vb = __builtin_amdgcn_readfirstlane(slots[item_k % 3]);
+  else if (vb < 0) vb = item_at(0);
   if (vb >= n_items) break;
-  const int vb_next = item_at(item_k + 1);
+  const int vb_next =
+      dyn ? __builtin_amdgcn_readfirstlane(slots[(item_k + 1) % 3]) : item_at(item_k + 1);
+  if (dyn && tid == 0) slots[(item_k + 2) % 3] = claim(p.counters, n_items);
   const bool has_next = vb_next < n_items;
   int qtile, b, kvh;
   item_coords(vb, qtile, b, kvh);

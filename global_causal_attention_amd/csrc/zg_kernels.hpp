@@ -34,6 +34,10 @@ struct KPrepParams {
   const float* fold_w;
   // When non-null, the unfolded k_hat rows also go here, packed [B, T, Hkv, 128].
   uint16_t* khat_raw;
+  // When non-null, the first launch block also zeroes these words (the item counters of the
+  // prefill kernel that follows this launch on the stream).
+  uint32_t* zero_words;
+  int32_t n_zero_words;
 };
 
 struct PrefillParams {
@@ -61,7 +65,16 @@ struct PrefillParams {
   float eps;
   float scale_log2;  // softmax scale * log2(e)
   RopeTableH rope;
+  // Tiled kernel, persistent launch: kSchedWords words (zeroed before the launch) holding one item
+  // counter per XCD, kSchedStride words apart; null: the static item schedule.
+  uint32_t* counters;
 };
+
+// Item counters of the persistent tiled kernel's dynamic schedule (one per XCD, one 128-byte line
+// each): the bytes a caller's workspace reserves for them.
+constexpr int kSchedStride = 32;
+constexpr int kSchedWords = 8 * kSchedStride;
+constexpr int kSchedBytes = kSchedWords * 4;
 
 // Split-KV decode: keys per chunk (one workgroup each), and the most chunks one sequence may have.
 constexpr int kDecodeChunkKeys = 1024;
