@@ -292,10 +292,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // A persistent workgroup brings the next item's q rows into its staging rows during iteration 1
   // of the current item, and the next item's first two K tiles once the current item's last
   // iteration has read its K buffers, so neither waits on memory at the next item's start.
-  // With item counters (p.counters) the schedule is dynamic: XCD x's items, in the same order,
-  // are handed out one at a time from its own counter to whichever of its workgroups asks next,
-  // and a workgroup whose XCD has none left takes the remaining (lightest) items of another XCD,
-  // so XCDs that run slower than others do not hold up the end of the launch. Thread 0 claims
+  // With item counters (p.counters) the schedule is dynamic: items are handed out one at a time
+  // to whichever workgroup asks next (see claim below), so XCDs that run slower than others do
+  // not hold up the end of the launch. Thread 0 claims
   // each item two items ahead into a ring of three LDS slots, so every wave reads an item's slot
   // at least one workgroup barrier after it was written and before it is written again.
   int item_k = 0;
@@ -303,23 +302,43 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   bool q_ready = false;   // this item's raw q rows are already in the staging rows
   bool k_ready = false;   // this item's first K tiles were issued during the previous item
   int* const slots = reinterpret_cast<int*>(smem + kLdsSlots);
-  auto claim = [](uint32_t* ctr, int n_items_) -> int {
+  // Item (pair, t) -- t = 0 the pair's heaviest query tile -- is item number
+  // (pair & 7) + 8 ((pair >> 3) n_qt + t) of the static order. XCD x's queue holds the heavy
+  // three quarters (t < n_qt - n_qt / 4) of its pairs' tiles, pair by pair; the light quarter of
+  // every pair's tiles forms one shared pool, handed out heaviest first across all pairs once an
+  // XCD's own queue is empty; after that, workgroups take what is left in other XCDs' queues.
+  auto claim = [](uint32_t* ctr, int n_qt, int n_pairs) -> int {
     const int x = (int)(blockIdx.x & 7);  // workgroup i runs on XCD i mod 8
-#pragma unroll 1
-    for (int sx = 0; sx < 8; ++sx) {
-      const int xs = (x + sx) & 7;
-      const int j = (int)__hip_atomic_fetch_add(ctr + kSchedStride * xs, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      if (j < ((n_items_ - xs + 7) >> 3)) return xs + 8 * j;
+    const int n_light = n_qt >> 2, n_heavy = n_qt - n_light;
+    const int n_own = (n_pairs >> 3) * n_heavy;  // heavy items per XCD queue
+    auto take = [&](int q) {
+      return (int)__hip_atomic_fetch_add(ctr + kSchedStride * q, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto heavy_item = [&](int xq, int j) {
+      const int pl = j / n_heavy;
+      return xq + 8 * (pl * n_qt + (j - pl * n_heavy));
+    };
+    int j = take(x);
+    if (j < n_own) return heavy_item(x, j);
+    const int g = take(8);
+    if (g < n_pairs * n_light) {
+      const int t = n_heavy + g / n_pairs, pair = g % n_pairs;
+      return (pair & 7) + 8 * ((pair >> 3) * n_qt + t);
     }
-    return n_items_;
+#pragma unroll 1
+    for (int sx = 1; sx < 8; ++sx) {
+      const int xs = (x + sx) & 7;
+      j = take(xs);
+      if (j < n_own) return heavy_item(xs, j);
+    }
+    return n_qt * n_pairs;
   };
   const bool dyn = p.persist && p.counters;
   if (dyn) {
-    const int n_items0 = p.n_qtiles * p.B * p.Hkv;
     if (tid == 0) {
-      slots[0] = claim(p.counters, n_items0);
-      slots[1] = claim(p.counters, n_items0);
+      slots[0] = claim(p.counters, p.n_qtiles, p.B * p.Hkv);
+      slots[1] = claim(p.counters, p.n_qtiles, p.B * p.Hkv);
     }
     __syncthreads();
   }
@@ -419,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   if (vb >= n_items) break;
   const int vb_next =
       dyn ? __builtin_amdgcn_readfirstlane(slots[(item_k + 1) % 3]) : item_at(item_k + 1);
-  if (dyn && tid == 0) slots[(item_k + 2) % 3] = claim(p.counters, n_items);
+  if (dyn && tid == 0) slots[(item_k + 2) % 3] = claim(p.counters, p.n_qtiles, p.B * p.Hkv);
   const bool has_next = vb_next < n_items;
   int qtile, b, kvh;
   item_coords(vb, qtile, b, kvh);

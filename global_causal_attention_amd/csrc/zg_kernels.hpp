@@ -65,15 +65,15 @@ struct PrefillParams {
   float eps;
   float scale_log2;  // softmax scale * log2(e)
   RopeTableH rope;
-  // Tiled kernel, persistent launch: kSchedWords words (zeroed before the launch) holding one item
-  // counter per XCD, kSchedStride words apart; null: the static item schedule.
+  // Tiled kernel, persistent launch: kSchedWords words (zeroed before the launch) holding the item
+  // counters of the dynamic schedule, kSchedStride words apart; null: the static item schedule.
   uint32_t* counters;
 };
 
-// Item counters of the persistent tiled kernel's dynamic schedule (one per XCD, one 128-byte line
-// each): the bytes a caller's workspace reserves for them.
+// Item counters of the persistent tiled kernel's dynamic schedule (one per XCD queue and one for
+// the shared pool, a 128-byte line each): the bytes a caller's workspace reserves for them.
 constexpr int kSchedStride = 32;
-constexpr int kSchedWords = 8 * kSchedStride;
+constexpr int kSchedWords = 16 * kSchedStride;
 constexpr int kSchedBytes = kSchedWords * 4;
 
 // Split-KV decode: keys per chunk (one workgroup each), and the most chunks one sequence may have.

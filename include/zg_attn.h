@@ -72,7 +72,7 @@ typedef struct {
  *   q, gate, out: [B, T, Hq, D] bf16;  k, v: [B, T, Hkv, D] bf16  (see zg_token_strides)
  *   q_norm_w, k_norm_w: fp32[D] device pointers, or NULL for weight 1.
  *   workspace: device scratch of at least zg_attn_prefill_workspace_bytes(cfg, B, T) bytes (it holds
- *   the normalised, rotated keys and 1 KB of work counters for the attention launch; contents on
+ *   the normalised, rotated keys and 2 KB of work counters for the attention launch; contents on
  *   entry do not matter); may be NULL when that query returns 0.
  * Numerics: fp32 norm/RoPE/softmax/accumulation; q_hat, k_hat and the softmax weights are rounded to
  * bf16 at the matrix-core inputs; out is rounded to nearest-even bf16.
@@ -127,7 +127,7 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
  * zg_attn_forward_train: out as zg_attn_prefill, plus lse [B, T, Hq] fp32, the natural-log
  * log-sum-exp of each query row's scaled scores over its key set (what the backward recomputes the
  * softmax from). workspace >= zg_attn_forward_train_workspace_bytes(cfg, B, T) (the normalised,
- * rotated keys: B T Hkv 256 bytes, rounded up to 256, then 1 KB of work counters).
+ * rotated keys: B T Hkv 256 bytes, rounded up to 256, then 2 KB of work counters).
  *
  * zg_attn_backward: gradients of L = sum(dout * out) with respect to q, k, v and the gate logits
  * (dgate, written only when cfg->gated), given the forward's inputs, its out and lse:
