@@ -303,14 +303,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   bool k_ready = false;   // this item's first K tiles were issued during the previous item
   int* const slots = reinterpret_cast<int*>(smem + kLdsSlots);
   // Item (pair, t) -- t = 0 the pair's heaviest query tile -- is item number
-  // (pair & 7) + 8 ((pair >> 3) n_qt + t) of the static order. XCD x's queue holds the heavy
-  // three quarters (t < n_qt - n_qt / 4) of its pairs' tiles, pair by pair; the light quarter of
-  // every pair's tiles forms one shared pool, handed out heaviest first across all pairs once an
-  // XCD's own queue is empty; after that, workgroups take what is left in other XCDs' queues.
+  // (pair & 7) + 8 ((pair >> 3) n_qt + t) of the static order. XCD x has two queues (counters x
+  // and 8 + x): the heavy three quarters (t < n_qt - n_qt / 4) of its pairs' tiles, pair by pair,
+  // and the light quarter, heaviest first across its pairs. A workgroup takes from its XCD's heavy
+  // queue, then from its light queue (those pairs' keys were just streamed through the XCD's L2),
+  // then from the light queue whose next item is heaviest, so the launch ends on the lightest
+  // items wherever they are; last from what is left in other XCDs' heavy queues.
   auto claim = [](uint32_t* ctr, int n_qt, int n_pairs) -> int {
     const int x = (int)(blockIdx.x & 7);  // workgroup i runs on XCD i mod 8
     const int n_light = n_qt >> 2, n_heavy = n_qt - n_light;
-    const int n_own = (n_pairs >> 3) * n_heavy;  // heavy items per XCD queue
+    const int ppx = n_pairs >> 3;          // pairs per XCD
+    const int n_own = ppx * n_heavy;       // items per heavy queue
+    const int n_lown = ppx * n_light;      // items per light queue
     auto take = [&](int q) {
       return (int)__hip_atomic_fetch_add(ctr + kSchedStride * q, 1u, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
@@ -319,12 +323,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       const int pl = j / n_heavy;
       return xq + 8 * (pl * n_qt + (j - pl * n_heavy));
     };
+    auto light_item = [&](int xq, int g) {
+      const int tq = g / ppx;
+      return xq + 8 * ((g - tq * ppx) * n_qt + n_heavy + tq);
+    };
     int j = take(x);
     if (j < n_own) return heavy_item(x, j);
-    const int g = take(8);
-    if (g < n_pairs * n_light) {
-      const int t = n_heavy + g / n_pairs, pair = g % n_pairs;
-      return (pair & 7) + 8 * ((pair >> 3) * n_qt + t);
+    int g = take(8 + x);
+    if (g < n_lown) return light_item(x, g);
+    // every light queue runs heaviest first, so the one with the fewest items taken has the
+    // heaviest next item; a take that finds its queue empty leaves that queue out of every later
+    // scan, so the loop ends within eight rounds
+#pragma unroll 1
+    for (int tries = 0; tries < 8; ++tries) {
+      int best = -1, best_n = n_lown;
+#pragma unroll 1
+      for (int xs = 0; xs < 8; ++xs) {
+        const int c = (int)__hip_atomic_load(ctr + kSchedStride * (8 + xs), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        if (c < best_n) {
+          best_n = c;
+          best = xs;
+        }
+      }
+      if (best < 0) break;
+      g = take(8 + best);
+      if (g < n_lown) return light_item(best, g);
     }
 #pragma unroll 1
     for (int sx = 1; sx < 8; ++sx) {

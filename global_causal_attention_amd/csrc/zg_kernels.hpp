@@ -70,8 +70,8 @@ struct PrefillParams {
   uint32_t* counters;
 };
 
-// Item counters of the persistent tiled kernel's dynamic schedule (one per XCD queue and one for
-// the shared pool, a 128-byte line each): the bytes a caller's workspace reserves for them.
+// Item counters of the persistent tiled kernel's dynamic schedule (a heavy and a light queue per
+// XCD, a 128-byte line each): the bytes a caller's workspace reserves for them.
 constexpr int kSchedStride = 32;
 constexpr int kSchedWords = 16 * kSchedStride;
 constexpr int kSchedBytes = kSchedWords * 4;
