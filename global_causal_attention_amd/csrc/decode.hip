@@ -1297,8 +1297,20 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
   if ((d & 63) == 0) red[d >> 6] = lw;
   __syncthreads();
   const float l = red[0] + red[1];
+  // even chunks sum into o0, odd ones into o1, in chunk order; sixteen chunks' loads are issued
+  // together so the loop waits on memory once per sixteen chunks rather than once per two
   float o0 = 0.f, o1 = 0.f;
   int c = 0;
+  for (; c + 15 < nc; c += 16) {
+    float r[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = rec[(int64_t)(c + i) * kPartStride + 4 + d];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      o0 += r[i] * w_s[c + i];
+      o1 += r[i + 1] * w_s[c + i + 1];
+    }
+  }
   for (; c + 1 < nc; c += 2) {
     o0 += rec[(int64_t)c * kPartStride + 4 + d] * w_s[c];
     o1 += rec[(int64_t)(c + 1) * kPartStride + 4 + d] * w_s[c + 1];
