@@ -177,6 +177,14 @@ def bench_block(torch, zg, si, dev, stream, args):
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / K
+    # the global layer again, five launches back to back (reported beside the block timing)
+    e_b2b = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    e_b2b[0].record(stream)
+    for i in range(5):
+        run_glo()
+        e_b2b[i + 1].record(stream)
+    torch.cuda.synchronize()
+    glo_b2b = sorted(e_b2b[i].elapsed_time(e_b2b[i + 1]) for i in range(5))[2]
     swa_ms = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K) for i in range(5)) / (5 * K)
     glo_ms = sum(ev[s][5].elapsed_time(ev[s][6]) for s in range(K)) / K
     tokens = B * T
@@ -217,6 +225,8 @@ def bench_block(torch, zg, si, dev, stream, args):
             "swa_min_bytes": swa_bytes,
             "swa_mfma_TFLOPs_useful": round(swa_flop / (swa_ms * 1e-3) / 1e12, 2),
             "global_TFLOPs": round(glo_achieved / 1e12, 2),
+            "global_back_to_back_ms": round(glo_b2b, 4),
+            "global_back_to_back_mfma_frac": round(glo_flop / (glo_b2b * 1e-3) / MFMA_BF16_PEAK, 4),
             "global_tokens_per_s": round(tokens / (glo_ms * 1e-3), 1),
             "swa_tokens_per_s": round(tokens / (swa_ms * 1e-3), 1),
         },
