@@ -82,6 +82,11 @@ def test_prefill_edges(B, T, Hq, Hkv, W, gated, base, pos0):
     (8, 601, True, 1e6, 0, False),
     (16, 300, False, 1e4, 0, True),
     (4, 1030, True, 1e6, 3, False),
+    # one and two (sequence, KV head) pairs per XCD: each XCD's light queue holds the light
+    # quarter of one or two pairs' tiles, and the launch ends on tiles taken from other XCDs'
+    # light queues
+    (1, 4160, False, 1e6, 0, False),
+    (2, 2100, True, 1e6, 0, False),
 ])
 def test_prefill_persistent_causal(B, T, gated, base, pos0, norm_w):
     out, ref = _run(B, T, 32, 8, 0, gated, base, 17 + T, pos0=pos0, norm_w=norm_w)
