@@ -417,8 +417,8 @@ size_t zg_attn_prefill_cached_workspace_bytes(const zg_attn_cfg* cfg, int32_t B,
   if (cfg->window <= 0) return 0;  // linear caches: keys are read from the cache itself
   const size_t rows = (size_t)cfg->window - 1 + T;  // ring context + the new tokens
   const size_t row_bytes = (size_t)cfg->n_kv_heads * kD * 2;
-  // staged K and V, then the new rows' unfolded k_hat for the ring (streaming-kernel path)
-  return 2 * align256((size_t)B * rows * row_bytes) + align256((size_t)B * T * row_bytes);
+  // staged K and V (the new rows reach the ring straight from the K prologue)
+  return 2 * align256((size_t)B * rows * row_bytes);
 }
 
 zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, int64_t pos0,
@@ -472,20 +472,19 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
     // ring's context followed by the new tokens
     uint16_t* ks = kc;
     uint16_t* vs = vc;
-    uint16_t* k_raw = nullptr;  // unfolded k_hat of the new rows, for the ring write
     int64_t kv_rows = cache_stride, row0 = pos0;
     const zg::RopeTableH rt = rope_table(cfg);
     const int G = (int)(Hq / Hkv);
     const int window = (ring && W < n_keys) ? (int)W : 0;  // a window covering every key is causal
     // Rings whose context offset suits it run on the banded streaming kernel, which takes keys
     // with the softmax scale and the q-norm weights folded in: the context rows are folded as they
-    // are gathered, and the new rows' unfolded k_hat goes to the ring from a separate copy.
+    // are gathered, and the K prologue writes the new rows' k_hat folded to the staging rows and
+    // unfolded to the ring.
     const bool swa = ring && zg::prefill_uses_swa(window, G, rt.half) &&
                      zg::prefill_swa_offset_ok(n_ctx, window);
     if (ring) {
       ks = static_cast<uint16_t*>(workspace);
       vs = ks + align256((size_t)B * (W - 1 + T) * row * 2) / 2;
-      if (swa) k_raw = vs + align256((size_t)B * (W - 1 + T) * row * 2) / 2;
       kv_rows = n_keys;
       row0 = n_ctx;
     }
@@ -514,6 +513,16 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
         }
       }
     }
+    zg::RowCopyParams vcp{};
+    vcp.src = static_cast<const uint16_t*>(v);
+    vcp.dst = vs;
+    vcp.src_bstride = T; vcp.dst_bstride = kv_rows;
+    vcp.src_row0 = 0; vcp.dst_row0 = row0;
+    vcp.src_stride = s.v; vcp.dst_stride = row;
+    vcp.row_elems = (int32_t)row; vcp.rows = T; vcp.B = B;
+    pre[n_pre++] = vcp;
+    st = hip_status(zg::launch_row_copies(pre, n_pre, hs), "ring gather / v copy launch");
+    if (st != ZG_OK) return st;
     zg::KPrepParams kp{};
     kp.k = static_cast<const uint16_t*>(k);
     kp.khat = ks;
@@ -531,19 +540,18 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
       kp.fold = 1;
       kp.fold_scale = scale_log2(cfg);
       kp.fold_w = q_norm_w;
-      kp.khat_raw = k_raw;
+    }
+    if (ring) {
+      // the ring keeps the last W positions; the gather launch above has read its context rows
+      const int64_t first = std::max<int64_t>(pos0, pos0 + T - W);
+      kp.ring_k = kc;
+      kp.ring_v = vc;
+      kp.ring_v_src = static_cast<const uint16_t*>(v);
+      kp.ring_sv = s.v;
+      kp.ring_w = (int32_t)W;
+      kp.ring_t0 = (int32_t)(first - pos0);
     }
     st = hip_status(zg::launch_kprep(kp, hs), "kprep launch");
-    if (st != ZG_OK) return st;
-    zg::RowCopyParams vcp{};
-    vcp.src = static_cast<const uint16_t*>(v);
-    vcp.dst = vs;
-    vcp.src_bstride = T; vcp.dst_bstride = kv_rows;
-    vcp.src_row0 = 0; vcp.dst_row0 = row0;
-    vcp.src_stride = s.v; vcp.dst_stride = row;
-    vcp.row_elems = (int32_t)row; vcp.rows = T; vcp.B = B;
-    pre[n_pre++] = vcp;
-    st = hip_status(zg::launch_row_copies(pre, n_pre, hs), "ring gather / v copy launch");
     if (st != ZG_OK) return st;
 
     const int mq = 256 / G;
@@ -580,25 +588,6 @@ zg_status zg_attn_prefill_cached(const zg_attn_cfg* cfg, int32_t B, int32_t T, i
       st = hip_status(zg::launch_prefill_general(pp, G, cfg->gated != 0, hs), "prefill launch");
     }
     if (st != ZG_OK) return st;
-    if (ring) {
-      // the ring keeps the last W positions; written after the attention has read the context
-      const int64_t first = std::max<int64_t>(pos0, pos0 + T - W);
-      zg::RowCopyParams wr[2];
-      for (int which = 0; which < 2; ++which) {
-        zg::RowCopyParams& w = wr[which];
-        w = zg::RowCopyParams{};
-        const bool raw = swa && which == 0;  // K: the unfolded rows
-        w.src = which ? vs : (raw ? k_raw : ks);
-        w.dst = which ? vc : kc;
-        w.src_bstride = raw ? T : kv_rows; w.dst_bstride = W;
-        w.src_row0 = (raw ? 0 : n_ctx) + (first - pos0); w.dst_row0 = first;
-        w.src_stride = row; w.dst_stride = row;
-        w.src_ring = 0; w.dst_ring = W;
-        w.row_elems = (int32_t)row; w.rows = (int32_t)(pos0 + T - first); w.B = B;
-      }
-      st = hip_status(zg::launch_row_copies(wr, 2, hs), "ring write launch");
-      if (st != ZG_OK) return st;
-    }
     return ZG_OK;
   } catch (...) {
     return fail(ZG_ERR_HIP, "unexpected exception in zg_attn_prefill_cached");

@@ -256,8 +256,16 @@ __global__ __launch_bounds__(256) void kprep_kernel(KPrepParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if (p.khat_raw && cur[i].valid)
-        *reinterpret_cast<u32x4*>(p.khat_raw + (base + grp + 4 * i) * kHeadDim + 8 * c) = pack8(x[i]);
+      if (p.ring_k && cur[i].valid && cur[i].pos - p.pos0 >= p.ring_t0) {
+        // (b, t, h) of the row from its output row and position
+        const int64_t tt = cur[i].pos - p.pos0;
+        const int64_t hh = cur[i].orow % Hkv;
+        const int64_t bb = (cur[i].orow / Hkv - p.out_row0 - tt) / p.out_rows;
+        const int64_t rr = (bb * p.ring_w + cur[i].pos % p.ring_w) * Hkv + hh;
+        *reinterpret_cast<u32x4*>(p.ring_k + rr * kHeadDim + 8 * c) = pack8(x[i]);
+        *reinterpret_cast<u32x4*>(p.ring_v + rr * kHeadDim + 8 * c) = *reinterpret_cast<const u32x4*>(
+            p.ring_v_src + (bb * T + tt) * p.ring_sv + hh * kHeadDim + 8 * c);
+      }
       if (p.fold) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[i][j] *= fv[j];

@@ -32,8 +32,15 @@ struct KPrepParams {
   int32_t fold;
   float fold_scale;
   const float* fold_w;
-  // When non-null, the unfolded k_hat rows also go here, packed [B, T, Hkv, 128].
-  uint16_t* khat_raw;
+  // Ring write of a chunked prefill: when ring_k is non-null, rows t >= ring_t0 (the last
+  // ring_w positions) also go to slot (pos0 + t) % ring_w of their sequence in the rings
+  // [B, ring_w, Hkv, 128]: the unfolded k_hat to ring_k, and row t of ring_v_src (token stride
+  // ring_sv) unchanged to ring_v.
+  uint16_t* ring_k;
+  uint16_t* ring_v;
+  const uint16_t* ring_v_src;
+  int64_t ring_sv;
+  int32_t ring_w, ring_t0;
   // When non-null, the first launch block also zeroes these words (the item counters of the
   // prefill kernel that follows this launch on the stream).
   uint32_t* zero_words;
